@@ -1,0 +1,194 @@
+/*
+ * lags.h - C ABI of the LAGS-SGD data-parallel hot path on one MI355X (gfx950).
+ *
+ * What is computed (the review "Layer-wise Adaptive Gradient Sparsification
+ * for Distributed Deep Learning with Convergence Guarantees", Shi et al. 2019):
+ *   abstract - every worker picks a small set of "significant" gradients from
+ *     each layer independently, with a per-layer size, and the workers run
+ *     synchronous SGD over what was picked;
+ *   proposed method, bullet 1 - per layer, the top-k gradients by magnitude;
+ *   proposed method, bullet 2 - the ratio is adaptive per layer (here: an
+ *     input table of exact ratios);
+ *   proposed method, bullet 4 - error compensation keeps the unsent part.
+ *
+ * One step of worker 0, over a flat fp32 gradient buffer cut into L layers by
+ * an offset table (layer l = entries [off[l], off[l+1])):
+ *   lags_sparsify_layers:  acc = grad + residual (fp32);  per layer, the k_l
+ *     entries of largest |acc| (ties: lower index first) are sent as
+ *     (uint32 global index, fp32 acc) in ascending index order;  residual
+ *     becomes +0.0 at sent entries and acc elsewhere;
+ *   lags_aggregate_apply:  u = sum of the P workers' messages, in worker order
+ *     0..P-1 starting from +0.0;  every touched weight becomes
+ *     w - (s * u) with s = lr / P (fp32, product rounded before the subtract).
+ * Results are bit-identical to a plain sequential fp32 evaluation of these
+ * definitions (round to nearest even, no flush to zero, no FMA contraction).
+ *
+ * Conventions for every entry point:
+ *   - pointers named grad/residual/weights/msg_* are DEVICE pointers on the
+ *     device that was current when the layout was first used; tables passed
+ *     to lags_layout_create are HOST pointers and are copied;
+ *   - device buffers are owned by the caller; the library keeps no pointer
+ *     to them after a call returns;
+ *   - calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream): no host synchronisation, no device-to-host copy, except where
+ *     a function says it synchronises;
+ *   - arguments are validated on the host before anything is launched; on a
+ *     negative status nothing has been launched and nothing written;
+ *   - device faults surface at the caller's next synchronisation (HIP rules);
+ *   - one workspace must not be used by two calls that may overlap in time.
+ */
+#ifndef LAGS_H
+#define LAGS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (negative = error). */
+#define LAGS_OK 0
+#define LAGS_EINVAL (-1)     /* invalid argument: null/misaligned pointer, bad table, overlap */
+#define LAGS_ERANGE (-2)     /* size outside the supported range (n or K >= 2^32, P, L) */
+#define LAGS_EWORKSPACE (-3) /* workspace null, misaligned or smaller than required */
+#define LAGS_EHIP (-4)       /* a HIP runtime call failed (no device, launch error, ...) */
+#define LAGS_EDEVICE (-5)    /* current device differs from the layout's device */
+#define LAGS_ENOMEM (-6)     /* host or device allocation failed */
+
+/* Limits. */
+#define LAGS_MAX_LAYERS 65536
+#define LAGS_MAX_WORKERS 1024
+
+/* Flags for lags_sparsify_layers. */
+#define LAGS_SPARSIFY_EXACT 1u /* skip the sampled threshold estimate: every layer
+                                  above the small-layer size takes the exact
+                                  multi-pass selection (same results, slower) */
+
+typedef struct lags_layout lags_layout; /* opaque; host object; see below */
+
+/* Short English description of a status code (static string). */
+const char *lags_strerror(int status);
+
+/*
+ * Entry count of a layer of n entries at ratio rho = num/den (proposed
+ * method, bullet 2: the ratio is a per-layer quantity):
+ *   k = ceil(n * num / den), in exact integer arithmetic.
+ * Returns k >= 1 for n >= 1, 0 for n == 0, or LAGS_EINVAL for n < 0,
+ * num < 1, den < 1 or num > den.
+ */
+int64_t lags_k_for_ratio(int64_t n, int64_t num, int64_t den);
+
+/*
+ * Build a layout: L layers over a flat buffer of n = layer_off[L] entries, and
+ * the per-layer count k[l] of entries each worker sends (abstract: the set's
+ * size is chosen per layer).
+ *   layer_off: host int64[L+1], layer_off[0] == 0, strictly increasing,
+ *              layer_off[L] < 2^32;
+ *   k:         host int64[L], 1 <= k[l] <= layer_off[l+1] - layer_off[l],
+ *              sum(k) < 2^32;
+ *   out:       receives the new layout (destroy with lags_layout_destroy).
+ * Pure host work: no HIP call is made here.  Device copies of the tables are
+ * made on first use, on the device current at that time.  The layout is
+ * immutable after creation and may be shared by concurrent calls (its lazily
+ * built device tables are guarded by a lock).
+ * Returns LAGS_OK, LAGS_EINVAL (bad table / null pointer), LAGS_ERANGE
+ * (L < 1 or L > LAGS_MAX_LAYERS, n or sum(k) >= 2^32), LAGS_ENOMEM.
+ */
+int lags_layout_create(int32_t L, const int64_t *layer_off, const int64_t *k,
+                       lags_layout **out);
+
+/* Free the layout and its device tables.  NULL is accepted.  The caller must
+ * make sure no call using it is still running on the device. */
+void lags_layout_destroy(lags_layout *layout);
+
+/* n (entries), K = sum(k) (message length per worker), L. -1 on NULL. */
+int64_t lags_layout_num_elems(const lags_layout *layout);
+int64_t lags_layout_total_k(const lags_layout *layout);
+int32_t lags_layout_num_layers(const lags_layout *layout);
+
+/* Message offset of layer l: sum_{j<l} k[j] (l = L gives K); -1 if out of range. */
+int64_t lags_layout_msg_offset(const lags_layout *layout, int32_t l);
+
+/*
+ * Bytes of device workspace that lags_sparsify_layers and
+ * lags_aggregate_apply (with up to P workers) need.  The workspace is scratch
+ * space only: its contents on entry are never read before being written, so
+ * results do not depend on them.  Returns 0 for a NULL layout or P outside
+ * [1, LAGS_MAX_WORKERS].
+ */
+size_t lags_workspace_bytes(const lags_layout *layout, int32_t P);
+
+/*
+ * Sparsify worker 0's gradient (abstract; proposed method, bullets 1 and 4).
+ *   grad:     device fp32[n], read only;
+ *   residual: device fp32[n], in/out: error-compensation memory;
+ *   msg_idx:  device uint32[K], out: global indices, layer by layer in table
+ *             order, ascending inside each layer (layer l at
+ *             lags_layout_msg_offset(l));
+ *   msg_val:  device fp32[K], out: the matching acc values, bit for bit;
+ *   ws:       device workspace of ws_bytes >= lags_workspace_bytes(layout, 1);
+ *   flags:    0 or LAGS_SPARSIFY_EXACT;
+ *   stream:   hipStream_t.
+ * The message buffers are exactly row 0 of the [P][K] layout that
+ * lags_aggregate_apply reads.  grad, residual, msg_idx, msg_val and ws must
+ * be 16-byte aligned and must not overlap.
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_EWORKSPACE, LAGS_EDEVICE, LAGS_EHIP,
+ * LAGS_ENOMEM (first use: device tables).
+ */
+int lags_sparsify_layers(const lags_layout *layout, const float *grad,
+                         float *residual, uint32_t *msg_idx, float *msg_val,
+                         void *ws, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * Aggregate P workers' messages and apply the SGD step (abstract: synchronous
+ * SGD over the workers' sparse gradients).
+ *   weights: device fp32[n], in/out; only touched entries are written;
+ *   msg_idx: device uint32[P][K], worker-major (row p = worker p's message in
+ *            the layout produced by lags_sparsify_layers: per layer k[l]
+ *            distinct indices of that layer, ascending);
+ *   msg_val: device fp32[P][K];
+ *   P:       1..LAGS_MAX_WORKERS;  lr: learning rate (s = lr / P in fp32);
+ *   ws:      device workspace of ws_bytes >= lags_workspace_bytes(layout, P).
+ * A message entry that breaks the layout (index outside its layer, or not
+ * ascending) is skipped and counted in lags_report.bad_entries; it can never
+ * cause an out-of-bounds access.
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_ERANGE (P), LAGS_EWORKSPACE,
+ * LAGS_EDEVICE, LAGS_EHIP, LAGS_ENOMEM (first use with this P: device tables).
+ */
+int lags_aggregate_apply(const lags_layout *layout, float *weights,
+                         const uint32_t *msg_idx, const float *msg_val,
+                         int32_t P, float lr, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* What the last calls that used a workspace did. */
+typedef struct lags_report {
+    int32_t layers_sampled; /* layers on the sampled-threshold path in the last sparsify */
+    int32_t layers_exact;   /* of those, layers that fell back to the exact path */
+    uint32_t bad_entries;   /* message entries the last aggregate skipped as invalid */
+    uint32_t slow_chunks;   /* aggregate chunks above the fast-path capacity */
+} lags_report;
+
+/* Synchronise `stream` and read the report kept in the workspace.  Only
+ * meaningful after a sparsify / aggregate call with this workspace. */
+int lags_workspace_report(const lags_layout *layout, const void *ws,
+                          size_t ws_bytes, void *stream, lags_report *out);
+
+/*
+ * Kernel tracing.  While enabled on a layout, every kernel the library
+ * launches for that layout is bracketed by HIP events on the launch stream.
+ * lags_trace_read synchronises on the recorded events and returns, per
+ * kernel id, the summed device time in milliseconds and the launch count
+ * accumulated since tracing was enabled or last read (then resets them).
+ */
+int lags_trace_enable(lags_layout *layout, int on);
+int lags_trace_read(lags_layout *layout, double *ms, int64_t *launches,
+                    int32_t nkernels);
+int32_t lags_num_kernels(void);
+const char *lags_kernel_name(int32_t id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAGS_H */

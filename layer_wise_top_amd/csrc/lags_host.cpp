@@ -1,0 +1,553 @@
+// Host side of the LAGS-SGD library: argument validation, per-layer planning,
+// workspace sizing, device tables, kernel launches and kernel tracing.
+// The entry points are declared in include/lags.h.
+#include "lags.h"
+#include "lags_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <vector>
+
+using namespace lags;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct AggTables {
+    uint32_t NC = 0;
+    void *dev = nullptr;
+    uint32_t *cbase = nullptr;   // [L+1]
+    uint32_t *csh = nullptr;     // [L]
+    uint32_t *chunk_layer = nullptr;  // [NC]
+};
+
+struct TraceRec {
+    int32_t kid;
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct lags_layout {
+    int32_t L = 0;
+    uint64_t n = 0, K = 0;
+    std::vector<uint32_t> off, k, moff;
+    std::vector<LayerInfo> linfo;
+    std::vector<SampledInfo> sinfo;
+    std::vector<uint2> main_work, fin_work;
+    uint32_t nseg_total = 0;
+    uint64_t slots_total = 0;
+    // workspace plan (byte offsets)
+    size_t ws_report = 0, ws_state = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
+           ws_agg = 0;
+    // device tables, built on first use
+    std::mutex mu;
+    int device = -1;
+    void *dev = nullptr;
+    LayerInfo *d_linfo = nullptr;
+    SampledInfo *d_sinfo = nullptr;
+    uint2 *d_main = nullptr, *d_fin = nullptr;
+    uint32_t *d_moff = nullptr;
+    std::map<int32_t, AggTables> agg;
+    // tracing
+    bool trace = false;
+    std::vector<TraceRec> recs;
+    double tr_ms[kNumKernels] = {};
+    int64_t tr_n[kNumKernels] = {};
+};
+
+namespace {
+
+// Chunk widths of the aggregate for P workers: per layer, a power of two such
+// that a chunk holds about kAggTargetEntries message entries over all workers.
+void plan_agg(const lags_layout *lo, int32_t P, std::vector<uint32_t> &cbase,
+              std::vector<uint32_t> &csh, uint32_t &NC)
+{
+    cbase.assign(lo->L + 1, 0);
+    csh.assign(lo->L, 0);
+    uint64_t total = 0;
+    for (int32_t l = 0; l < lo->L; ++l) {
+        const double nl = lo->linfo[l].n, kl = lo->linfo[l].k;
+        const double width = (double)kAggTargetEntries * nl / ((double)P * kl);
+        int s = 0;
+        while (s < 31 && std::ldexp(1.0, s + 1) <= width) ++s;
+        csh[l] = (uint32_t)s;
+        cbase[l] = (uint32_t)total;
+        total += ((uint64_t)lo->linfo[l].n + (1ull << s) - 1) >> s;
+    }
+    cbase[lo->L] = (uint32_t)total;
+    NC = (uint32_t)total;
+}
+
+// Threshold-guess plan for a sampled layer of n entries sending k: sample s
+// keys and take the j-th largest, with j = m * k * s / n and the margin m the
+// smallest that keeps (1 - 1/m) * sqrt(j) >= 6 (six standard deviations of the
+// sample count above the guess).  Returns false if the ratio is too large for
+// a guess to pay off.
+bool plan_guess(uint32_t n, uint32_t k, uint32_t s, uint32_t &j, double &m)
+{
+    const double lam = (double)k * (double)s / (double)n;
+    m = 1.05;
+    while (m < 1e6 && (1.0 - 1.0 / m) * std::sqrt(m * lam) < 6.0) m *= 1.05;
+    const double jj = std::ceil(m * lam);
+    if (jj > s / 4.0) return false;
+    j = (uint32_t)std::max(1.0, jj);
+    return true;
+}
+
+int build_plan(lags_layout *lo)
+{
+    const int32_t L = lo->L;
+    lo->linfo.resize(L);
+    uint32_t seg_base = 0;
+    uint64_t slot_base = 0;
+    std::vector<uint2> small_work, stream_work;
+    for (int32_t l = 0; l < L; ++l) {
+        LayerInfo &li = lo->linfo[l];
+        li = LayerInfo{};
+        li.off = lo->off[l];
+        li.n = lo->off[l + 1] - lo->off[l];
+        li.k = lo->k[l];
+        li.moff = lo->moff[l];
+        li.sid = 0xffffffffu;
+        if (li.n <= kSmallMax) {
+            li.cls = kClsSmall;
+            li.ntiles = 1;
+            small_work.push_back(make_uint2((uint32_t)l, 0));
+        } else if (li.k == li.n) {
+            li.cls = kClsDense;
+            li.ntiles = (li.n + kDenseTile - 1) / kDenseTile;
+            for (uint32_t t = 0; t < li.ntiles; ++t) stream_work.push_back(make_uint2((uint32_t)l, t));
+        } else {
+            li.cls = kClsSampled;
+            li.sid = (uint32_t)lo->sinfo.size();
+            SampledInfo si{};
+            si.layer = (uint32_t)l;
+            si.a4 = (li.off + 3u) & ~3u;
+            si.b4 = (li.off + li.n) & ~3u;
+            si.nseg = (si.b4 - si.a4 + kSeg - 1) / kSeg;
+            si.seg_base = seg_base;
+            double m = 1.0;
+            if (li.n <= kSampleMax) {
+                si.full_sample = 1;
+                si.j = li.k;
+                si.cap = kSeg;
+            } else {
+                si.nchunk = kSampleMax / kSampleChunk;
+                uint32_t j = 0;
+                if (plan_guess(li.n, li.k, si.nchunk * kSampleChunk, j, m)) {
+                    si.j = j;
+                    const double mu = m * (double)li.k * kSeg / (double)li.n;
+                    size_t cap = (size_t)std::ceil(mu + 8.0 * std::sqrt(mu) + 32.0);
+                    cap = align_up(cap, 32);
+                    si.cap = (uint32_t)std::min<size_t>(cap, kSeg);
+                } else {
+                    si.force_exact = 1;
+                    si.cap = 1;
+                    si.j = 1;
+                }
+            }
+            si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
+            si.slot_hi = (uint32_t)(slot_base >> 32);
+            si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
+            li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
+            for (uint32_t t = 0; t < li.ntiles; ++t) stream_work.push_back(make_uint2((uint32_t)l, t));
+            for (uint32_t b = 0; b < si.fin_nblocks; ++b)
+                lo->fin_work.push_back(make_uint2(li.sid, b * kFinSegs));
+            seg_base += si.nseg;
+            slot_base += (uint64_t)si.nseg * si.cap;
+            lo->sinfo.push_back(si);
+        }
+    }
+    // small layers first: they start while the streaming tiles fill the chip
+    lo->main_work = small_work;
+    lo->main_work.insert(lo->main_work.end(), stream_work.begin(), stream_work.end());
+    lo->nseg_total = seg_base;
+    lo->slots_total = slot_base;
+
+    const size_t ns = lo->sinfo.size();
+    size_t at = 0;
+    lo->ws_report = at;
+    at = align_up(at + kRepWords * 4, kAlign);
+    lo->ws_state = at;
+    at = align_up(at + ns * sizeof(SampledState), kAlign);
+    lo->ws_segcount = at;
+    at = align_up(at + (size_t)lo->nseg_total * 4, kAlign);
+    lo->ws_segsel = at;
+    at = align_up(at + (size_t)lo->nseg_total * 4, kAlign);
+    lo->ws_slots = at;
+    at = align_up(at + (size_t)lo->slots_total * 8, kAlign);
+    lo->ws_tbin = at;
+    at = align_up(at + ns * (size_t)kTbinCap * 8, kAlign);
+    lo->ws_agg = at;
+    return LAGS_OK;
+}
+
+size_t agg_bytes(const lags_layout *lo, int32_t P)
+{
+    std::vector<uint32_t> cb, cs;
+    uint32_t NC;
+    plan_agg(lo, P, cb, cs, NC);
+    return align_up((size_t)P * ((size_t)NC + 1) * 4, kAlign);
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device tables for the layout on the current device (caller holds lo->mu).
+int ensure_device(lags_layout *lo)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LAGS_EHIP;
+    if (lo->dev) return dev == lo->device ? LAGS_OK : LAGS_EDEVICE;
+    const size_t b_l = align_up(lo->linfo.size() * sizeof(LayerInfo), kAlign);
+    const size_t b_s = align_up(std::max<size_t>(1, lo->sinfo.size()) * sizeof(SampledInfo), kAlign);
+    const size_t b_m = align_up(std::max<size_t>(1, lo->main_work.size()) * sizeof(uint2), kAlign);
+    const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(uint2), kAlign);
+    const size_t b_o = align_up(lo->moff.size() * 4, kAlign);
+    const size_t total = b_l + b_s + b_m + b_f + b_o;
+    std::vector<unsigned char> host(total, 0);
+    std::memcpy(host.data(), lo->linfo.data(), lo->linfo.size() * sizeof(LayerInfo));
+    if (!lo->sinfo.empty())
+        std::memcpy(host.data() + b_l, lo->sinfo.data(), lo->sinfo.size() * sizeof(SampledInfo));
+    std::memcpy(host.data() + b_l + b_s, lo->main_work.data(), lo->main_work.size() * sizeof(uint2));
+    if (!lo->fin_work.empty())
+        std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(uint2));
+    std::memcpy(host.data() + b_l + b_s + b_m + b_f, lo->moff.data(), lo->moff.size() * 4);
+    void *d = nullptr;
+    if (hipMalloc(&d, total) != hipSuccess) return LAGS_ENOMEM;
+    if (hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(d);
+        return LAGS_EHIP;
+    }
+    unsigned char *p = (unsigned char *)d;
+    lo->dev = d;
+    lo->device = dev;
+    lo->d_linfo = (LayerInfo *)p;
+    lo->d_sinfo = (SampledInfo *)(p + b_l);
+    lo->d_main = (uint2 *)(p + b_l + b_s);
+    lo->d_fin = (uint2 *)(p + b_l + b_s + b_m);
+    lo->d_moff = (uint32_t *)(p + b_l + b_s + b_m + b_f);
+    return LAGS_OK;
+}
+
+int ensure_agg(lags_layout *lo, int32_t P, AggTables **out)
+{
+    auto it = lo->agg.find(P);
+    if (it != lo->agg.end()) {
+        *out = &it->second;
+        return LAGS_OK;
+    }
+    std::vector<uint32_t> cb, cs;
+    uint32_t NC;
+    plan_agg(lo, P, cb, cs, NC);
+    std::vector<uint32_t> cl(std::max<uint32_t>(NC, 1), 0);
+    for (int32_t l = 0; l < lo->L; ++l)
+        for (uint32_t c = cb[l]; c < cb[l + 1]; ++c) cl[c] = (uint32_t)l;
+    const size_t b0 = align_up(cb.size() * 4, kAlign), b1 = align_up(cs.size() * 4, kAlign),
+                 b2 = align_up(cl.size() * 4, kAlign);
+    std::vector<unsigned char> host(b0 + b1 + b2, 0);
+    std::memcpy(host.data(), cb.data(), cb.size() * 4);
+    std::memcpy(host.data() + b0, cs.data(), cs.size() * 4);
+    std::memcpy(host.data() + b0 + b1, cl.data(), cl.size() * 4);
+    void *d = nullptr;
+    if (hipMalloc(&d, host.size()) != hipSuccess) return LAGS_ENOMEM;
+    if (hipMemcpy(d, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(d);
+        return LAGS_EHIP;
+    }
+    AggTables t;
+    t.NC = NC;
+    t.dev = d;
+    t.cbase = (uint32_t *)d;
+    t.csh = (uint32_t *)((unsigned char *)d + b0);
+    t.chunk_layer = (uint32_t *)((unsigned char *)d + b0 + b1);
+    auto res = lo->agg.emplace(P, t);
+    *out = &res.first->second;
+    return LAGS_OK;
+}
+
+// Launch with optional tracing events around it.
+template <class F>
+int traced(lags_layout *lo, int32_t kid, hipStream_t s, F &&launch)
+{
+    hipEvent_t a = nullptr, b = nullptr;
+    if (lo->trace) {
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return LAGS_EHIP;
+        if (hipEventRecord(a, s) != hipSuccess) return LAGS_EHIP;
+    }
+    if (launch() != hipSuccess) return LAGS_EHIP;
+    if (lo->trace) {
+        if (hipEventRecord(b, s) != hipSuccess) return LAGS_EHIP;
+        lo->recs.push_back(TraceRec{kid, a, b});
+    }
+    return LAGS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lags_strerror(int status)
+{
+    switch (status) {
+    case LAGS_OK: return "ok";
+    case LAGS_EINVAL: return "invalid argument";
+    case LAGS_ERANGE: return "size out of the supported range";
+    case LAGS_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case LAGS_EHIP: return "HIP runtime error";
+    case LAGS_EDEVICE: return "current device differs from the layout's device";
+    case LAGS_ENOMEM: return "out of memory";
+    default: return "unknown status";
+    }
+}
+
+int64_t lags_k_for_ratio(int64_t n, int64_t num, int64_t den)
+{
+    if (n < 0 || num < 1 || den < 1 || num > den) return LAGS_EINVAL;
+    const __int128 p = (__int128)n * num;
+    return (int64_t)((p + den - 1) / den);
+}
+
+int lags_layout_create(int32_t L, const int64_t *layer_off, const int64_t *k, lags_layout **out)
+{
+    if (!out) return LAGS_EINVAL;
+    *out = nullptr;
+    if (!layer_off || !k) return LAGS_EINVAL;
+    if (L < 1 || L > LAGS_MAX_LAYERS) return LAGS_ERANGE;
+    if (layer_off[0] != 0) return LAGS_EINVAL;
+    uint64_t K = 0;
+    for (int32_t l = 0; l < L; ++l) {
+        if (layer_off[l + 1] <= layer_off[l]) return LAGS_EINVAL;
+        const int64_t nl = layer_off[l + 1] - layer_off[l];
+        if (k[l] < 1 || k[l] > nl) return LAGS_EINVAL;
+        K += (uint64_t)k[l];
+    }
+    if (layer_off[L] >= (int64_t)0xffffffffLL || K >= 0xffffffffull) return LAGS_ERANGE;
+    lags_layout *lo = new (std::nothrow) lags_layout();
+    if (!lo) return LAGS_ENOMEM;
+    lo->L = L;
+    lo->n = (uint64_t)layer_off[L];
+    lo->K = K;
+    lo->off.resize(L + 1);
+    lo->k.resize(L);
+    lo->moff.resize(L + 1);
+    uint64_t m = 0;
+    for (int32_t l = 0; l <= L; ++l) {
+        lo->off[l] = (uint32_t)layer_off[l];
+        lo->moff[l] = (uint32_t)m;
+        if (l < L) {
+            lo->k[l] = (uint32_t)k[l];
+            m += (uint64_t)k[l];
+        }
+    }
+    try {
+        build_plan(lo);
+    } catch (...) {
+        delete lo;
+        return LAGS_ENOMEM;
+    }
+    *out = lo;
+    return LAGS_OK;
+}
+
+void lags_layout_destroy(lags_layout *lo)
+{
+    if (!lo) return;
+    for (auto &r : lo->recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (auto &kv : lo->agg) (void)hipFree(kv.second.dev);
+    if (lo->dev) (void)hipFree(lo->dev);
+    delete lo;
+}
+
+int64_t lags_layout_num_elems(const lags_layout *lo) { return lo ? (int64_t)lo->n : -1; }
+int64_t lags_layout_total_k(const lags_layout *lo) { return lo ? (int64_t)lo->K : -1; }
+int32_t lags_layout_num_layers(const lags_layout *lo) { return lo ? lo->L : -1; }
+
+int64_t lags_layout_msg_offset(const lags_layout *lo, int32_t l)
+{
+    if (!lo || l < 0 || l > lo->L) return -1;
+    return (int64_t)lo->moff[l];
+}
+
+size_t lags_workspace_bytes(const lags_layout *lo, int32_t P)
+{
+    if (!lo || P < 1 || P > LAGS_MAX_WORKERS) return 0;
+    return lo->ws_agg + agg_bytes(lo, P);
+}
+
+int lags_sparsify_layers(const lags_layout *clo, const float *grad, float *residual,
+                         uint32_t *msg_idx, float *msg_val, void *ws, size_t ws_bytes,
+                         uint32_t flags, void *stream)
+{
+    lags_layout *lo = const_cast<lags_layout *>(clo);
+    if (!lo || !grad || !residual || !msg_idx || !msg_val) return LAGS_EINVAL;
+    if (flags & ~LAGS_SPARSIFY_EXACT) return LAGS_EINVAL;
+    if (!aligned16(grad) || !aligned16(residual) || !aligned16(msg_idx) || !aligned16(msg_val))
+        return LAGS_EINVAL;
+    if (!ws || !aligned16(ws) || ws_bytes < lo->ws_agg) return LAGS_EWORKSPACE;
+    const size_t nb = lo->n * 4, kb = lo->K * 4;
+    const void *bufs[5] = {grad, residual, msg_idx, msg_val, ws};
+    const size_t lens[5] = {nb, nb, kb, kb, lo->ws_agg};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
+
+    std::lock_guard<std::mutex> g(lo->mu);
+    int rc = ensure_device(lo);
+    if (rc != LAGS_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char *w = (unsigned char *)ws;
+    SparsifyArgs a{};
+    a.grad = grad;
+    a.res = residual;
+    a.msg_idx = msg_idx;
+    a.msg_val = msg_val;
+    a.linfo = lo->d_linfo;
+    a.sinfo = lo->d_sinfo;
+    a.main_work = lo->d_main;
+    a.fin_work = lo->d_fin;
+    a.report = (uint32_t *)(w + lo->ws_report);
+    a.state = (SampledState *)(w + lo->ws_state);
+    a.seg_count = (uint32_t *)(w + lo->ws_segcount);
+    a.seg_sel = (uint32_t *)(w + lo->ws_segsel);
+    a.slots = (uint2 *)(w + lo->ws_slots);
+    a.tbin = (uint2 *)(w + lo->ws_tbin);
+    a.nsampled = (uint32_t)lo->sinfo.size();
+    a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
+    const uint32_t ns = a.nsampled;
+    rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
+    if (rc != LAGS_OK) return rc;
+    rc = traced(lo, kKMain, s, [&] { return launch_main(a, (uint32_t)lo->main_work.size(), s); });
+    if (rc != LAGS_OK) return rc;
+    if (ns) {
+        rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, (uint32_t)lo->fin_work.size(), s); });
+        if (rc != LAGS_OK) return rc;
+        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, (uint32_t)lo->fin_work.size(), s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    return LAGS_OK;
+}
+
+int lags_aggregate_apply(const lags_layout *clo, float *weights, const uint32_t *msg_idx,
+                         const float *msg_val, int32_t P, float lr, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    lags_layout *lo = const_cast<lags_layout *>(clo);
+    if (!lo || !weights || !msg_idx || !msg_val) return LAGS_EINVAL;
+    if (P < 1 || P > LAGS_MAX_WORKERS) return LAGS_ERANGE;
+    if ((uint64_t)P * lo->K >= (1ull << 40)) return LAGS_ERANGE;
+    if (!aligned16(weights) || !aligned16(msg_idx) || !aligned16(msg_val)) return LAGS_EINVAL;
+    const size_t need = lo->ws_agg + agg_bytes(lo, P);
+    if (!ws || !aligned16(ws) || ws_bytes < need) return LAGS_EWORKSPACE;
+    const size_t nb = lo->n * 4, mb = (size_t)P * lo->K * 4;
+    const void *bufs[4] = {weights, msg_idx, msg_val, ws};
+    const size_t lens[4] = {nb, mb, mb, need};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
+
+    std::lock_guard<std::mutex> g(lo->mu);
+    int rc = ensure_device(lo);
+    if (rc != LAGS_OK) return rc;
+    AggTables *t = nullptr;
+    rc = ensure_agg(lo, P, &t);
+    if (rc != LAGS_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char *w = (unsigned char *)ws;
+    AggArgs a{};
+    a.w = weights;
+    a.msg_idx = msg_idx;
+    a.msg_val = msg_val;
+    a.linfo = lo->d_linfo;
+    a.moff = lo->d_moff;
+    a.cbase = t->cbase;
+    a.csh = t->csh;
+    a.chunk_layer = t->chunk_layer;
+    a.start = (uint32_t *)(w + lo->ws_agg);
+    a.report = (uint32_t *)(w + lo->ws_report);
+    a.L = (uint32_t)lo->L;
+    a.P = (uint32_t)P;
+    a.K = (uint32_t)lo->K;
+    a.NC = t->NC;
+    a.s = lr / (float)P;
+    rc = traced(lo, kKAggStarts, s, [&] { return launch_agg_starts(a, s); });
+    if (rc != LAGS_OK) return rc;
+    return traced(lo, kKAgg, s, [&] { return launch_agg(a, s); });
+}
+
+int lags_workspace_report(const lags_layout *lo, const void *ws, size_t ws_bytes, void *stream,
+                          lags_report *out)
+{
+    if (!lo || !ws || !out) return LAGS_EINVAL;
+    if (ws_bytes < lo->ws_report + 16) return LAGS_EWORKSPACE;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LAGS_EHIP;
+    uint32_t h[4];
+    if (hipMemcpy(h, (const unsigned char *)ws + lo->ws_report, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
+        return LAGS_EHIP;
+    out->layers_sampled = (int32_t)h[kRepSampled];
+    out->layers_exact = (int32_t)h[kRepExact];
+    out->bad_entries = h[kRepBad];
+    out->slow_chunks = h[kRepSlow];
+    return LAGS_OK;
+}
+
+int lags_trace_enable(lags_layout *lo, int on)
+{
+    if (!lo) return LAGS_EINVAL;
+    std::lock_guard<std::mutex> g(lo->mu);
+    lo->trace = on != 0;
+    return LAGS_OK;
+}
+
+int lags_trace_read(lags_layout *lo, double *ms, int64_t *launches, int32_t nkernels)
+{
+    if (!lo || !ms || !launches || nkernels < 0) return LAGS_EINVAL;
+    std::lock_guard<std::mutex> g(lo->mu);
+    int rc = LAGS_OK;
+    for (auto &r : lo->recs) {
+        float t = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+            rc = LAGS_EHIP;
+        lo->tr_ms[r.kid] += t;
+        lo->tr_n[r.kid] += 1;
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    lo->recs.clear();
+    for (int32_t i = 0; i < nkernels; ++i) {
+        ms[i] = i < kNumKernels ? lo->tr_ms[i] : 0.0;
+        launches[i] = i < kNumKernels ? lo->tr_n[i] : 0;
+    }
+    for (int i = 0; i < kNumKernels; ++i) {
+        lo->tr_ms[i] = 0.0;
+        lo->tr_n[i] = 0;
+    }
+    return rc;
+}
+
+int32_t lags_num_kernels(void) { return kNumKernels; }
+
+const char *lags_kernel_name(int32_t id)
+{
+    static const char *names[kNumKernels] = {"k_sample", "k_main", "k_fin_select",
+                                             "k_fin_emit", "k_agg_starts", "k_agg"};
+    return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// Internal tables and constants shared by the host planner (lags_host.cpp)
+// and the gfx950 kernels (lags_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace lags {
+
+// ---- launch geometry ------------------------------------------------------
+constexpr int kBlock = 256;              // threads per workgroup (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr uint32_t kSeg = 4096;          // entries per segment (one wave's stripe)
+constexpr uint32_t kTileSegs = 4;        // segments per streaming workgroup
+constexpr uint32_t kSmallMax = 4096;     // layers up to this size: one workgroup, exact
+constexpr uint32_t kDenseTile = 16384;   // entries per workgroup for k == n layers
+constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident)
+constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
+constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
+constexpr uint32_t kTbinCap = 4096;      // entries of the threshold bin kept per layer
+constexpr uint32_t kFinSegs = 16;        // segments per finishing workgroup
+// aggregate
+constexpr uint32_t kAggTargetEntries = 1024;  // expected entries per chunk
+constexpr uint32_t kAggCap = 2048;            // fast-path capacity (entries per chunk)
+constexpr uint32_t kAggTable = 4096;          // LDS hash slots (power of two, >= 2 * kAggCap)
+constexpr uint32_t kAggWindow = 4096;         // slow-path dense window
+
+// ---- layer classes --------------------------------------------------------
+enum : uint32_t {
+    kClsSmall = 0,    // n <= kSmallMax: one workgroup does everything (LDS)
+    kClsDense = 1,    // k == n: every entry is sent
+    kClsSampled = 2,  // sampled threshold guess + candidate compaction
+};
+
+// ---- per-call status of a sampled layer -----------------------------------
+enum : uint32_t {
+    kStPending = 0,
+    kStOk = 1,        // candidates hold the top k; threshold bin resolved
+    kStExact = 2,     // the exact multi-pass path handled the layer
+};
+
+struct LayerInfo {        // one per layer, device table
+    uint32_t off;         // first entry
+    uint32_t n;           // entries
+    uint32_t k;           // entries sent
+    uint32_t moff;        // message offset
+    uint32_t cls;
+    uint32_t sid;         // sampled-layer id or 0xffffffff
+    uint32_t ntiles;      // streaming workgroups of this layer in the main kernel
+    uint32_t pad;
+};
+
+struct SampledInfo {      // one per sampled layer, device table
+    uint32_t layer;
+    uint32_t a4, b4;      // 4-aligned interior [a4, b4) of the layer
+    uint32_t nseg;        // segments (kSeg entries of the interior each)
+    uint32_t seg_base;    // first global segment id
+    uint32_t cap;         // candidate slots per segment
+    uint32_t slot_lo, slot_hi;   // first slot (64-bit, in 8-byte slots)
+    uint32_t full_sample; // 1: the sample is the whole layer (guess = exact k-th key)
+    uint32_t nchunk;      // sample chunks (when not full)
+    uint32_t j;           // rank of the guess inside the sample (1-based, from the top)
+    uint32_t force_exact; // ratio too large for a guess: exact path
+    uint32_t fin_nblocks; // finishing workgroups of this layer
+    uint32_t pad[3];
+};
+
+struct SampledState {     // per sampled layer, per call, in the workspace
+    uint32_t G;           // guess: candidates have key >= G
+    uint32_t SH;          // histogram bin width 2^SH above G
+    uint32_t status;
+    uint32_t overflow;    // a segment had more candidates than slots
+    uint32_t bstar;       // histogram bin holding the k-th largest candidate
+    uint32_t c_above;     // candidates in bins above bstar
+    uint32_t done_main;   // streaming workgroups finished
+    uint32_t done_fin;    // finishing workgroups finished
+    uint32_t tbin_n;      // entries of bin bstar collected
+    uint32_t T;           // k-th largest key of the layer
+    uint32_t idx_cut;     // largest global index taken among keys == T
+    uint32_t pad[5];
+    uint32_t hist[kNBins];
+};
+
+// report counters at the head of the workspace
+enum : uint32_t { kRepSampled = 0, kRepExact = 1, kRepBad = 2, kRepSlow = 3, kRepWords = 64 };
+
+struct SparsifyArgs {
+    const float *grad;
+    float *res;
+    uint32_t *msg_idx;
+    float *msg_val;
+    const LayerInfo *linfo;
+    const SampledInfo *sinfo;
+    const uint2 *main_work;   // (layer, tile) per main workgroup
+    const uint2 *fin_work;    // (sid, first segment) per finishing workgroup
+    uint32_t *report;
+    SampledState *state;
+    uint32_t *seg_count;
+    uint32_t *seg_sel;
+    uint2 *slots;
+    uint2 *tbin;
+    uint32_t nsampled;
+    uint32_t force_exact;
+};
+
+struct AggArgs {
+    float *w;
+    const uint32_t *msg_idx;
+    const float *msg_val;
+    const LayerInfo *linfo;
+    const uint32_t *moff;       // [L+1]
+    const uint32_t *cbase;      // [L+1] first chunk of each layer
+    const uint32_t *csh;        // [L] log2 chunk width
+    const uint32_t *chunk_layer;// [NC]
+    uint32_t *start;            // [P][NC+1]
+    uint32_t *report;
+    uint32_t L;
+    uint32_t P;
+    uint32_t K;
+    uint32_t NC;
+    float s;                    // lr / P, rounded to fp32 on the host
+};
+
+// kernel ids for tracing
+enum : int32_t {
+    kKSample = 0, kKMain = 1, kKFinSelect = 2, kKFinEmit = 3,
+    kKAggStarts = 4, kKAgg = 5, kNumKernels = 6
+};
+
+// launchers (lags_kernels.hip)
+hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
+hipError_t launch_agg(const AggArgs &a, hipStream_t s);
+
+}  // namespace lags

@@ -1,0 +1,914 @@
+// gfx950 kernels of the LAGS-SGD data-parallel hot path.
+//
+// What is computed follows the review "Layer-wise Adaptive Gradient
+// Sparsification for Distributed Deep Learning with Convergence Guarantees"
+// (abstract; proposed method, bullets 1, 2 and 4): per layer, error-
+// compensated top-k by magnitude, index-ordered (index, value) messages, the
+// residual of what was not sent, and the S-SGD average of P workers'
+// messages applied to the weights.
+//
+// How it is computed here (the pages give no GPU design):
+//   k_sample      one workgroup per sampled layer: reads a stratified sample
+//                 of acc = grad + residual, takes a rank from the top of the
+//                 sample as a threshold guess G that at least k entries of the
+//                 layer exceed with overwhelming probability; also clears the
+//                 layer's per-call state.
+//   k_main        the streaming pass: acc = grad + residual is written back
+//                 to the residual buffer; entries with |acc| key >= G are
+//                 compacted, in index order, into per-segment candidate slots
+//                 and counted in a per-layer histogram of bins above G.  The
+//                 last workgroup of a layer finds the bin holding the k-th
+//                 largest candidate.  Small layers (<= 4096 entries) are done
+//                 start to finish by one workgroup (exact radix select in
+//                 LDS); k == n layers are sent whole.
+//   k_fin_select  counts, per segment, candidates above the threshold bin and
+//                 gathers the threshold bin's candidates; the last workgroup of
+//                 a layer resolves the exact threshold key T and the tie cut
+//                 (lowest indices first) and scans segment counts into message
+//                 offsets.  A layer whose guess failed (too few candidates or
+//                 a full segment) is done here by the exact multi-pass path.
+//   k_fin_emit    writes the selected candidates of each segment, in index
+//                 order, to the message and zeroes their residual.
+//   k_agg_starts  for every worker, where each index chunk starts in its
+//                 message (messages ascend per layer).
+//   k_agg         one workgroup per index chunk: worker-ordered sums in an LDS
+//                 hash table, then w -= (lr/P) * u at each touched index.
+//
+// Keys: key(x) = bits(x) & 0x7fffffff orders fp32 magnitudes (-0 ties +0).
+// All fp32 arithmetic is IEEE round to nearest even; the product and the
+// subtraction of the update are separate roundings.
+#include "lags_internal.h"
+
+namespace lags {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t key_of(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint32_t ld_acquire(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix over the wave of small counts c in [0, 7].
+__device__ __forceinline__ uint32_t wave_prefix3(uint32_t c, uint32_t &tot)
+{
+    const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+    tot = (uint32_t)__popcll(b0) + 2u * (uint32_t)__popcll(b1) + 4u * (uint32_t)__popcll(b2);
+    return mbcnt(b0) + 2u * mbcnt(b1) + 4u * mbcnt(b2);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    const uint32_t l = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (l >= (uint32_t)d) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x = max(x, (uint32_t)__shfl_xor(x, d, 64));
+    return x;
+}
+
+// Block-wide exclusive scan (all kBlock threads must call).
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t *tmp, uint32_t &total)
+{
+    const uint32_t w = threadIdx.x >> 6;
+    const uint32_t inc = wave_incl_scan(v);
+    if (lane_id() == 63) tmp[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const uint32_t t = tmp[i];
+        before += (i < (int)w) ? t : 0u;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + inc - v;
+}
+
+// Block-wide exclusive scan of counts in [0, 7].
+__device__ uint32_t block_excl_small(uint32_t c, uint32_t *tmp, uint32_t &total)
+{
+    const uint32_t w = threadIdx.x >> 6;
+    uint32_t wt;
+    const uint32_t pre = wave_prefix3(c, wt);
+    if (lane_id() == 0) tmp[w] = wt;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const uint32_t t = tmp[i];
+        before += (i < (int)w) ? t : 0u;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return before + pre;
+}
+
+__device__ uint32_t block_max(uint32_t v, uint32_t *tmp)
+{
+    const uint32_t m = wave_max(v);
+    if (lane_id() == 0) tmp[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) r = max(r, tmp[i]);
+    __syncthreads();
+    return r;
+}
+
+// Find, in an LDS histogram of nbins bins (nbins a multiple of kBlock), the bin
+// holding the rank-th largest item (rank >= 1, counting from the top bin).
+// res[0] = bin, res[1] = items in higher bins.  The caller guarantees rank <=
+// total.  All threads call; res is valid after return.
+__device__ void block_find_rank(const uint32_t *hist, uint32_t nbins, uint32_t rank,
+                                uint32_t *res, uint32_t *tmp)
+{
+    const uint32_t per = nbins / kBlock;
+    uint32_t s = 0;
+    for (uint32_t q = 0; q < per; ++q) s += hist[nbins - 1 - (threadIdx.x * per + q)];
+    uint32_t tot;
+    uint32_t above = block_excl_scan(s, tmp, tot);
+    for (uint32_t q = 0; q < per; ++q) {
+        const uint32_t b = nbins - 1 - (threadIdx.x * per + q);
+        const uint32_t h = hist[b];
+        if (above < rank && rank <= above + h) {
+            res[0] = b;
+            res[1] = above;
+        }
+        above += h;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Exact selection by one workgroup: MSD radix select of the rank-th largest
+// 32-bit value among the items with match(i) true, digits of 11/11/10 bits.
+// Returns the value and, in *eq_take, how many items equal to it are needed to
+// reach rank (the items strictly above it number rank - eq_take).
+template <class Val, class Match>
+__device__ uint32_t block_radix_select(const Val &val, const Match &match, uint32_t n, uint32_t rank,
+                                       uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t *eq_take)
+{
+    uint32_t prefix = 0;
+    const uint32_t shifts[3] = {21u, 10u, 0u};
+    const uint32_t widths[3] = {11u, 11u, 10u};
+    for (int lev = 0; lev < 3; ++lev) {
+        const uint32_t sh = shifts[lev];
+        const uint32_t nb = 1u << widths[lev];
+        const uint32_t top = sh + widths[lev];   // bits above this digit: [top, 32)
+        for (uint32_t b = threadIdx.x; b < nb; b += kBlock) hist[b] = 0;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
+            if (!match(i)) continue;
+            const uint32_t v = val(i);
+            const bool same = (top >= 32u) ? true : ((v >> top) == (prefix >> top));
+            if (same) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        block_find_rank(hist, nb < (uint32_t)kBlock ? (uint32_t)kBlock : nb, rank, res, tmp);
+        prefix |= res[0] << sh;
+        rank -= res[1];
+        __syncthreads();
+    }
+    *eq_take = rank;
+    return prefix;
+}
+
+// Emit the selection of one layer from a value source, in index order: entries
+// with key > T, then among key == T the first e (lowest index).  Writes the
+// message at msg_idx/msg_val[moff ...], residual +0.0 at sent entries, and
+// (WRITE_ALL) acc at the others.
+template <bool WRITE_ALL, class Src>
+__device__ void exact_emit(const Src &src, uint32_t n, uint32_t k, uint32_t off, uint32_t moff, uint32_t T,
+                           uint32_t e, float *res_layer, uint32_t *msg_idx, float *msg_val, uint32_t *tmp)
+{
+    uint32_t run_eq = 0, run_sel = 0;
+    for (uint32_t base = 0; base < n; base += 4u * kBlock) {
+        float a[4];
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t i = base + 4u * threadIdx.x + j;
+            a[j] = 0.0f;
+            if (i < n) {
+                a[j] = src(i);
+                const uint32_t key = key_of(a[j]);
+                if (key > T) gt |= 1u << j;
+                else if (key == T) eq |= 1u << j;
+            }
+        }
+        uint32_t teq;
+        const uint32_t eq_before = block_excl_small((uint32_t)__popc(eq), tmp, teq);
+        uint32_t sel = gt;
+        uint32_t r = run_eq + eq_before;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (eq & (1u << j)) {
+                if (r < e) sel |= 1u << j;
+                ++r;
+            }
+        }
+        uint32_t tsel;
+        uint32_t pos = run_sel + block_excl_small((uint32_t)__popc(sel), tmp, tsel);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t i = base + 4u * threadIdx.x + j;
+            if (i < n) {
+                if (sel & (1u << j)) {
+                    if (pos < k) {           // the selection holds exactly k entries
+                        msg_idx[moff + pos] = off + i;
+                        msg_val[moff + pos] = a[j];
+                    }
+                    res_layer[i] = 0.0f;
+                    ++pos;
+                } else if (WRITE_ALL) {
+                    res_layer[i] = a[j];
+                }
+            }
+        }
+        run_eq += teq;
+        run_sel += tsel;
+    }
+}
+
+// Whole-layer exact path: select the k-th largest key of n values, then emit.
+template <bool WRITE_ALL, class Src>
+__device__ void exact_layer(const Src &src, uint32_t n, uint32_t k, uint32_t off, uint32_t moff,
+                            float *res_layer, uint32_t *msg_idx, float *msg_val,
+                            uint32_t *hist, uint32_t *tmp, uint32_t *res)
+{
+    uint32_t e;
+    const uint32_t T = block_radix_select([&](uint32_t i) { return key_of(src(i)); },
+                                          [](uint32_t) { return true; }, n, k, hist, tmp, res, &e);
+    exact_emit<WRITE_ALL>(src, n, k, off, moff, T, e, res_layer, msg_idx, msg_val, tmp);
+}
+
+// ---------------------------------------------------------------------------
+// k_sample
+__global__ __launch_bounds__(kBlock) void k_sample(SparsifyArgs a)
+{
+    __shared__ uint32_t keys[kSampleMax];
+    __shared__ uint32_t hist[kBlock];
+    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t res[2];
+
+    if (blockIdx.x == 0 && threadIdx.x < 2) a.report[kRepSampled + threadIdx.x] = 0;
+    if (blockIdx.x >= a.nsampled) return;
+    const SampledInfo S = a.sinfo[blockIdx.x];
+    const LayerInfo L = a.linfo[S.layer];
+    SampledState *st = a.state + blockIdx.x;
+    uint32_t *stw = reinterpret_cast<uint32_t *>(st);
+    for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += kBlock) stw[t] = 0;
+    __syncthreads();
+    if (S.force_exact || a.force_exact) {
+        if (threadIdx.x == 0) {
+            st->G = 0xffffffffu;   // no key reaches it: the layer takes the exact path
+            st->SH = 0;
+        }
+        return;
+    }
+    uint32_t cnt, rank;
+    if (S.full_sample) {
+        cnt = L.n;
+        rank = L.k;
+        for (uint32_t i = threadIdx.x; i < cnt; i += kBlock)
+            keys[i] = key_of(a.grad[L.off + i] + a.res[L.off + i]);
+    } else {
+        cnt = S.nchunk * kSampleChunk;
+        rank = S.j;
+        const uint64_t span = S.b4 - S.a4 - kSampleChunk;
+        for (uint32_t e = threadIdx.x; e < cnt; e += kBlock) {
+            const uint32_t c = e / kSampleChunk, l = e % kSampleChunk;
+            const uint32_t pos = S.a4 + (uint32_t)((uint64_t)c * span / (S.nchunk - 1)) + l;
+            keys[e] = key_of(a.grad[pos] + a.res[pos]);
+        }
+    }
+    __syncthreads();
+    // rank-th largest key of the sample: four 8-bit digits, most significant first
+    uint32_t prefix = 0;
+    for (int sh = 24; sh >= 0; sh -= 8) {
+        hist[threadIdx.x] = 0;
+        __syncthreads();
+        for (uint32_t e = threadIdx.x; e < cnt; e += kBlock) {
+            const uint32_t key = keys[e];
+            const bool same = (sh == 24) ? true : ((key >> (sh + 8)) == (prefix >> (sh + 8)));
+            if (same) atomicAdd(&hist[(key >> sh) & 255u], 1u);
+        }
+        __syncthreads();
+        block_find_rank(hist, kBlock, rank, res, tmp);
+        prefix |= res[0] << sh;
+        rank -= res[1];
+        __syncthreads();
+    }
+    uint32_t m = 0;
+    for (uint32_t e = threadIdx.x; e < cnt; e += kBlock) m = max(m, keys[e]);
+    const uint32_t M = block_max(m, tmp);
+    if (threadIdx.x == 0) {
+        const uint32_t G = prefix;
+        uint32_t sh = 0;
+        while (sh < 31u && (uint64_t)(M - G) >= ((uint64_t)kNBins << sh)) ++sh;
+        st->G = G;
+        st->SH = sh;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_main
+
+__device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t SH)
+{
+    return min((key - G) >> SH, kNBins - 1u);
+}
+
+// Append the flagged entries of a lane group (up to 4 per lane, index order
+// lane-major, then j) to the segment's slots and the LDS histogram.
+__device__ __forceinline__ void append_candidates(uint32_t cmask, const uint32_t *idx, const float *v,
+                                                  uint32_t &run, uint2 *slots, uint32_t cap,
+                                                  uint32_t G, uint32_t SH, uint32_t *hist)
+{
+    uint32_t tot;
+    const uint32_t pre = wave_prefix3((uint32_t)__popc(cmask), tot);
+    if (tot == 0) return;
+    uint32_t pos = run + pre;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (cmask & (1u << j)) {
+            if (pos < cap) slots[pos] = make_uint2(idx[j], __float_as_uint(v[j]));
+            atomicAdd(&hist[cand_bin(key_of(v[j]), G, SH)], 1u);
+            ++pos;
+        }
+    }
+    run += tot;
+}
+
+__device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const SampledInfo &S,
+                                SampledState *st, uint32_t seg, uint32_t G, uint32_t SH, uint32_t *hist)
+{
+    constexpr int U = 4;
+    const uint32_t ln = lane_id();
+    const uint32_t e0 = S.a4 + seg * kSeg;
+    const uint32_t e1 = min(e0 + kSeg, S.b4);
+    const uint64_t slot0 = (((uint64_t)S.slot_hi << 32) | S.slot_lo) + (uint64_t)seg * S.cap;
+    uint2 *slots = a.slots + slot0;
+    const uint32_t cap = S.cap;
+    uint32_t run = 0;
+    uint32_t idx[4];
+    float v[4];
+
+    if (seg == 0 && L.off < S.a4) {          // unaligned head of the layer
+        const uint32_t i = L.off + ln;
+        uint32_t cm = 0;
+        v[0] = v[1] = v[2] = v[3] = 0.0f;
+        idx[0] = i;
+        if (i < S.a4) {
+            v[0] = a.grad[i] + a.res[i];
+            a.res[i] = v[0];
+            if (key_of(v[0]) >= G) cm = 1;
+        }
+        append_candidates(cm, idx, v, run, slots, cap, G, SH, hist);
+    }
+
+    const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
+    v4f *r4 = reinterpret_cast<v4f *>(a.res);
+    const uint32_t q1 = e1 / 4u;
+    for (uint32_t q0 = e0 / 4u; q0 < q1; q0 += 64u * U) {
+        v4f gv[U], rv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t q = q0 + u * 64u + ln;
+            if (q < q1) {
+                gv[u] = __builtin_nontemporal_load(g4 + q);
+                rv[u] = __builtin_nontemporal_load(r4 + q);
+            } else {
+                gv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                rv[u] = gv[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t q = q0 + u * 64u + ln;
+            const v4f acc = gv[u] + rv[u];
+            uint32_t cm = 0;
+            if (q < q1) {
+                __builtin_nontemporal_store(acc, r4 + q);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (key_of(acc[j]) >= G) cm |= 1u << j;
+            }
+            if (__ballot(cm != 0)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    idx[j] = 4u * q + j;
+                    v[j] = acc[j];
+                }
+                append_candidates(cm, idx, v, run, slots, cap, G, SH, hist);
+            }
+        }
+    }
+
+    const uint32_t end = L.off + L.n;
+    if (seg == S.nseg - 1 && S.b4 < end) {   // unaligned tail of the layer
+        const uint32_t i = S.b4 + ln;
+        uint32_t cm = 0;
+        v[0] = v[1] = v[2] = v[3] = 0.0f;
+        idx[0] = i;
+        if (i < end) {
+            v[0] = a.grad[i] + a.res[i];
+            a.res[i] = v[0];
+            if (key_of(v[0]) >= G) cm = 1;
+        }
+        append_candidates(cm, idx, v, run, slots, cap, G, SH, hist);
+    }
+    if (ln == 0) {
+        a.seg_count[S.seg_base + seg] = run;
+        if (run > cap) atomicOr(&st->overflow, 1u);
+    }
+}
+
+// Last streaming workgroup of a sampled layer: locate the candidate bin that
+// holds the k-th largest, or mark the layer for the exact path.
+__device__ void finalize_main(const SparsifyArgs &a, const LayerInfo &L, SampledState *st,
+                              uint32_t *hist, uint32_t *tmp, uint32_t *res)
+{
+    uint32_t part = 0;
+    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
+        hist[b] = ld_acquire(&st->hist[b]);
+        part += hist[b];
+    }
+    uint32_t C;
+    block_excl_scan(part, tmp, C);    // also orders the LDS writes above
+    const uint32_t overflow = ld_acquire(&st->overflow);
+    if (C < L.k || overflow) {
+        if (threadIdx.x == 0) {
+            st->status = kStExact;
+            atomicAdd(&a.report[kRepSampled], 1u);
+            atomicAdd(&a.report[kRepExact], 1u);
+        }
+        return;
+    }
+    block_find_rank(hist, kNBins, L.k, res, tmp);
+    if (threadIdx.x == 0) {
+        st->bstar = res[0];
+        st->c_above = res[1];
+        st->status = kStOk;
+        atomicAdd(&a.report[kRepSampled], 1u);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
+{
+    __shared__ uint32_t hist[kNBins];
+    __shared__ float acc_s[kSmallMax];
+    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t last;
+
+    const uint2 w = a.main_work[blockIdx.x];
+    const LayerInfo L = a.linfo[w.x];
+
+    if (L.cls == kClsSmall) {
+        for (uint32_t i = threadIdx.x; i < L.n; i += kBlock)
+            acc_s[i] = a.grad[L.off + i] + a.res[L.off + i];
+        __syncthreads();
+        if (L.k == L.n) {
+            for (uint32_t i = threadIdx.x; i < L.n; i += kBlock) {
+                a.msg_idx[L.moff + i] = L.off + i;
+                a.msg_val[L.moff + i] = acc_s[i];
+                a.res[L.off + i] = 0.0f;
+            }
+            return;
+        }
+        exact_layer<true>([&](uint32_t i) { return acc_s[i]; }, L.n, L.k, L.off, L.moff,
+                          a.res + L.off, a.msg_idx, a.msg_val, hist, tmp, res);
+        return;
+    }
+
+    if (L.cls == kClsDense) {
+        const uint32_t lo = L.off + w.y * kDenseTile;
+        const uint32_t hi = min(lo + kDenseTile, L.off + L.n);
+        for (uint32_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+            const float x = a.grad[i] + a.res[i];
+            a.res[i] = 0.0f;
+            a.msg_idx[L.moff + (i - L.off)] = i;
+            a.msg_val[L.moff + (i - L.off)] = x;
+        }
+        return;
+    }
+
+    // sampled layer, streaming tile w.y
+    const SampledInfo S = a.sinfo[L.sid];
+    SampledState *st = a.state + L.sid;
+    const uint32_t G = st->G, SH = st->SH;
+    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) hist[b] = 0;
+    __syncthreads();
+    const uint32_t seg = w.y * kTileSegs + (threadIdx.x >> 6);
+    if (seg < S.nseg) sampled_segment(a, L, S, st, seg, G, SH, hist);
+    __syncthreads();
+    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
+        const uint32_t v = hist[b];
+        if (v) atomicAdd(&st->hist[b], v);
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last = (atomicAdd(&st->done_main, 1u) == L.ntiles - 1u) ? 1u : 0u;
+    __syncthreads();
+    if (last) {
+        __threadfence();
+        finalize_main(a, L, st, hist, tmp, res);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_fin_select
+
+__device__ __forceinline__ uint32_t seg_of(const SampledInfo &S, uint32_t i)
+{
+    if (i < S.a4) return 0;
+    return min((i - S.a4) / kSeg, S.nseg - 1u);
+}
+
+__global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
+{
+    __shared__ uint32_t hist[kNBins];
+    __shared__ uint32_t tk[kTbinCap];
+    __shared__ uint32_t ti[kTbinCap];
+    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t last;
+
+    const uint2 w = a.fin_work[blockIdx.x];
+    const uint32_t sid = w.x;
+    const SampledInfo S = a.sinfo[sid];
+    const LayerInfo L = a.linfo[S.layer];
+    SampledState *st = a.state + sid;
+    const uint32_t status = st->status;
+    const uint32_t ln = lane_id();
+
+    if (status == kStOk) {
+        const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
+        const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
+        const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
+        for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
+            const uint32_t cnt = min(a.seg_count[S.seg_base + s], S.cap);
+            const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
+            uint32_t D = 0;
+            for (uint32_t p = ln; p < cnt; p += 64) {
+                const uint2 c = slots[p];
+                const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
+                if (bin > bstar) {
+                    ++D;
+                } else if (bin == bstar) {
+                    const uint32_t t = atomicAdd(&st->tbin_n, 1u);
+                    if (t < kTbinCap) a.tbin[(uint64_t)sid * kTbinCap + t] = c;
+                }
+            }
+            D = wave_sum(D);
+            if (ln == 0) a.seg_sel[S.seg_base + s] = D;
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last = (atomicAdd(&st->done_fin, 1u) == S.fin_nblocks - 1u) ? 1u : 0u;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+
+    const uint32_t h = ld_acquire(&st->tbin_n);
+    if (status != kStOk || h > kTbinCap) {
+        // exact multi-pass path over the accumulated values (the residual
+        // buffer holds acc for every entry of the layer after k_main)
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            if (status == kStOk) atomicAdd(&a.report[kRepExact], 1u);
+            st->status = kStExact;
+        }
+        const float *accp = a.res + L.off;
+        exact_layer<false>([&](uint32_t i) { return accp[i]; }, L.n, L.k, L.off, L.moff,
+                           a.res + L.off, a.msg_idx, a.msg_val, hist, tmp, res);
+        return;
+    }
+
+    // resolve the threshold inside bin bstar
+    const uint32_t need = L.k - st->c_above;
+    for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
+        const uint2 c = a.tbin[(uint64_t)sid * kTbinCap + p];
+        tk[p] = c.y & 0x7fffffffu;
+        ti[p] = c.x;
+    }
+    __syncthreads();
+    uint32_t e;
+    const uint32_t T = block_radix_select([&](uint32_t p) { return tk[p]; }, [](uint32_t) { return true; },
+                                          h, need, hist, tmp, res, &e);
+    // e-th smallest index among keys == T  ==  e-th largest of ~index
+    uint32_t e2;
+    const uint32_t ncut = block_radix_select([&](uint32_t p) { return ~ti[p]; },
+                                             [&](uint32_t p) { return tk[p] == T; }, h, e, hist, tmp, res, &e2);
+    const uint32_t idx_cut = ~ncut;
+    for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
+        if (tk[p] > T || (tk[p] == T && ti[p] <= idx_cut))
+            atomicAdd(&a.seg_sel[S.seg_base + seg_of(S, ti[p])], 1u);
+    }
+    __threadfence();
+    __syncthreads();
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < S.nseg; base += kBlock) {
+        const uint32_t s = base + threadIdx.x;
+        const uint32_t v = (s < S.nseg) ? ld_acquire(&a.seg_sel[S.seg_base + s]) : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(v, tmp, tot);
+        if (s < S.nseg) a.seg_sel[S.seg_base + s] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) {
+        st->T = T;
+        st->idx_cut = idx_cut;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_fin_emit
+__global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
+{
+    const uint2 w = a.fin_work[blockIdx.x];
+    const uint32_t sid = w.x;
+    const SampledState *st = a.state + sid;
+    if (st->status != kStOk) return;
+    const SampledInfo S = a.sinfo[sid];
+    const LayerInfo L = a.linfo[S.layer];
+    const uint32_t T = st->T, cut = st->idx_cut;
+    const uint32_t mend = L.moff + L.k;
+    const uint32_t ln = lane_id();
+    const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
+    const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
+    for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
+        const uint32_t cnt = min(a.seg_count[S.seg_base + s], S.cap);
+        const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
+        const uint32_t base = L.moff + a.seg_sel[S.seg_base + s];
+        uint32_t run = 0;
+        for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
+            const uint32_t p = p0 + ln;
+            bool sel = false;
+            uint2 c = make_uint2(0, 0);
+            if (p < cnt) {
+                c = slots[p];
+                const uint32_t key = c.y & 0x7fffffffu;
+                sel = key > T || (key == T && c.x <= cut);
+            }
+            const uint64_t m = __ballot(sel);
+            if (sel) {
+                const uint32_t pos = base + run + mbcnt(m);
+                if (pos < mend) {            // the layer's selection holds exactly k entries
+                    a.msg_idx[pos] = c.x;
+                    a.msg_val[pos] = __uint_as_float(c.y);
+                }
+                a.res[c.x] = 0.0f;
+            }
+            run += (uint32_t)__popcll(m);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// aggregate
+
+__global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
+{
+    __shared__ uint32_t l0s;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) a.report[kRepBad + threadIdx.x] = 0;
+    const uint32_t p = blockIdx.y;
+    const uint32_t j0 = blockIdx.x * kBlock;
+    if (threadIdx.x == 0) {
+        uint32_t lo = 0, hi = a.L;      // largest l in [0, L) with moff[l] <= j0
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (a.moff[mid] <= j0) lo = mid; else hi = mid;
+        }
+        l0s = lo;
+    }
+    __syncthreads();
+    const uint32_t j = j0 + threadIdx.x;
+    if (j > a.K) return;
+    const uint32_t *row = a.msg_idx + (uint64_t)p * a.K;
+    auto chunk_at = [&](uint32_t jj, uint32_t ll) -> uint32_t {
+        const LayerInfo Li = a.linfo[ll];
+        uint32_t rel = row[jj] - Li.off;
+        if (rel >= Li.n) rel = 0;          // invalid entry: counted by k_agg
+        return a.cbase[ll] + (rel >> a.csh[ll]);
+    };
+    uint32_t l = l0s;
+    while (l + 1 < a.L && a.moff[l + 1] <= j) ++l;
+    const uint32_t c = (j == a.K) ? a.NC : chunk_at(j, l);
+    uint32_t cp = 0xffffffffu;
+    if (j > 0) {
+        uint32_t lp = l;
+        while (lp > 0 && a.moff[lp] > j - 1) --lp;
+        cp = chunk_at(j - 1, lp);
+    }
+    uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
+    for (uint32_t cc = cp + 1u; cc <= c && cc <= a.NC; ++cc) srow[cc] = j;
+}
+
+__global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
+{
+    __shared__ uint32_t keys[kAggTable];
+    __shared__ float vals[kAggTable];
+    __shared__ uint32_t ws0[1024];
+    __shared__ uint32_t pre[1025];
+    __shared__ uint32_t tmp[kWaves];
+
+    const uint32_t c = blockIdx.x;
+    const uint32_t l = a.chunk_layer[c];
+    const LayerInfo L = a.linfo[l];
+    const uint32_t sh = a.csh[l];
+    const uint64_t lo64 = (uint64_t)L.off + ((uint64_t)(c - a.cbase[l]) << sh);
+    const uint64_t hi64 = min(lo64 + (1ull << sh), (uint64_t)L.off + L.n);
+    const uint32_t lo = (uint32_t)lo64, hi = (uint32_t)hi64;
+    const uint32_t m0 = a.moff[l], m1 = a.moff[l + 1];
+    const uint32_t P = a.P;
+
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < P; base += kBlock) {
+        const uint32_t p = base + threadIdx.x;
+        uint32_t m = 0;
+        if (p < P) {
+            const uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
+            uint32_t s0 = srow[c], s1 = srow[c + 1];
+            s0 = min(max(s0, m0), m1);
+            s1 = min(max(s1, s0), m1);
+            ws0[p] = s0;
+            m = s1 - s0;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(m, tmp, tot);
+        if (p < P) pre[p] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) pre[P] = carry;
+    __syncthreads();
+    const uint32_t E = carry;
+    const float s = a.s;
+    uint32_t bad = 0;
+
+    if (E <= kAggCap) {
+        for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
+            keys[t] = 0xffffffffu;
+            vals[t] = 0.0f;
+        }
+        __syncthreads();
+        constexpr int EPT = kAggCap / kBlock;
+        int slot[EPT];
+        uint32_t wk[EPT];
+        float v[EPT];
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            slot[q] = -1;
+            wk[q] = 0;
+            v[q] = 0.0f;
+            const uint32_t e = threadIdx.x + q * kBlock;
+            if (e < E) {
+                uint32_t plo = 0, phi = P;   // pre[plo] <= e < pre[phi]
+                while (phi - plo > 1) {
+                    const uint32_t mid = (plo + phi) / 2;
+                    if (pre[mid] <= e) plo = mid; else phi = mid;
+                }
+                const uint32_t j = ws0[plo] + (e - pre[plo]);
+                const uint64_t at = (uint64_t)plo * a.K + j;
+                const uint32_t x = a.msg_idx[at];
+                if (x < lo || x >= hi) {
+                    ++bad;
+                } else {
+                    const uint32_t key = x - lo;
+                    uint32_t hsh = (key * 2654435761u) >> 20;   // 12-bit hash
+                    while (true) {
+                        const uint32_t old = atomicCAS(&keys[hsh], 0xffffffffu, key);
+                        if (old == 0xffffffffu || old == key) break;
+                        hsh = (hsh + 1u) & (kAggTable - 1u);
+                    }
+                    slot[q] = (int)hsh;
+                    wk[q] = plo;
+                    v[q] = a.msg_val[at];
+                }
+            }
+        }
+        __syncthreads();
+        for (uint32_t p = 0; p < P; ++p) {
+            if (pre[p + 1] == pre[p]) continue;
+#pragma unroll
+            for (int q = 0; q < EPT; ++q)
+                if (slot[q] >= 0 && wk[q] == p) vals[slot[q]] = vals[slot[q]] + v[q];
+            __syncthreads();
+        }
+        for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
+            const uint32_t key = keys[t];
+            if (key != 0xffffffffu) {
+                const uint32_t x = lo + key;
+                a.w[x] = __fsub_rn(a.w[x], __fmul_rn(s, vals[t]));
+            }
+        }
+    } else {
+        // dense windows over the chunk's index range; every entry is visited
+        // once per window, workers in order
+        uint32_t *touched = keys;
+        float *u = vals;
+        const uint32_t nwin = (hi - lo + kAggWindow - 1) / kAggWindow;
+        for (uint32_t win = 0; win < nwin; ++win) {
+            const uint32_t wlo = lo + win * kAggWindow;
+            const uint32_t whi = min(wlo + kAggWindow, hi);
+            for (uint32_t t = threadIdx.x; t < kAggWindow; t += kBlock) {
+                touched[t] = 0;
+                u[t] = 0.0f;
+            }
+            __syncthreads();
+            for (uint32_t p = 0; p < P; ++p) {
+                const uint32_t m = pre[p + 1] - pre[p];
+                if (m == 0) continue;
+                for (uint32_t jj = threadIdx.x; jj < m; jj += kBlock) {
+                    const uint64_t at = (uint64_t)p * a.K + ws0[p] + jj;
+                    const uint32_t x = a.msg_idx[at];
+                    if (x >= wlo && x < whi) {
+                        u[x - wlo] = u[x - wlo] + a.msg_val[at];
+                        touched[x - wlo] = 1;
+                    } else if (win == 0 && (x < lo || x >= hi)) {
+                        ++bad;
+                    }
+                }
+                __syncthreads();
+            }
+            for (uint32_t t = threadIdx.x; t < whi - wlo; t += kBlock) {
+                if (touched[t]) {
+                    const uint32_t x = wlo + t;
+                    a.w[x] = __fsub_rn(a.w[x], __fmul_rn(s, u[t]));
+                }
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) atomicAdd(&a.report[kRepSlow], 1u);
+    }
+    bad = wave_sum(bad);
+    if (lane_id() == 0 && bad) atomicAdd(&a.report[kRepBad], bad);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_sample, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_main, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fin_select, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fin_emit, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
+{
+    const uint32_t nx = (a.K + 1u + kBlock - 1u) / kBlock;
+    hipLaunchKernelGGL(k_agg_starts, dim3(nx, a.P), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_agg(const AggArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_agg, dim3(a.NC), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace lags
