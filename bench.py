@@ -1,0 +1,254 @@
+"""Benchmark of the LAGS-SGD hot path on one MI355X.
+
+A step is one pass of the whole path for worker 0: lags_sparsify_layers
+(error-compensated per-layer top-k, messages, residual) followed by
+lags_aggregate_apply (P workers' messages summed in worker order and applied
+to the weights).  The other P-1 workers' messages are seeded inputs, resident
+in HBM with everything else before the timed region starts.
+
+Prints one JSON line (rank 0).  Default workload: the 1.3B-parameter
+transformer gradient (1,311,178,752 fp32 entries in 193 tensors, rho = 1/1000,
+P = 16), the largest layout that fits one GPU.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
+                  [--no-cpu-baseline] [--flush]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Gelem/s layer-wise EC top-k sparsify+aggregate; % of HBM peak BW"
+HBM_PEAK_GBS = 8000.0
+DOMINANT = "k_main"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n, K, P, U):
+    """What the method must move per step: read grad and residual, write the
+    residual (12 B/entry); write the own message (8 B per sent entry); read
+    all P messages (8 B per entry); read-modify-write the touched weights."""
+    return 12 * n + 8 * K + 8 * P * K + 8 * U
+
+
+def main_kernel_bytes(wl, k):
+    """Algorithmic bytes of one k_main launch: every entry's grad and residual
+    read and residual written, plus the message of layers it sends whole
+    (small layers and k == n layers)."""
+    n = np.diff(wl.offsets())
+    whole = (n <= 4096) | (k == n)
+    return int(12 * wl.n + 8 * int(k[whole].sum()))
+
+
+def cpu_baseline(wl, k, budget_s=20.0):
+    """The oracle (single thread, as it stands) on a bounded sample of the
+    same workload: the first layers of the table up to ~budget of CPU time
+    (estimated from a small calibration run), sparsify + aggregate with P."""
+    import oracle as O
+    from layer_wise_top_amd import workloads as W
+    orc = O.default()
+    off = wl.offsets()
+    n_l = np.diff(off)
+    # calibrate on the smallest prefix with at least ~2M entries
+    def run_prefix(nl):
+        sub_off = off[: nl + 1]
+        sub_k = k[:nl]
+        n = int(sub_off[-1])
+        g = np.concatenate([W.gen_grad_layer(wl, 0, 0, l) for l in range(nl)])
+        r = np.zeros(n, np.float32)
+        w = np.concatenate([W.gen_weights_layer(wl, l) for l in range(nl)])
+        P = wl.P
+        Ks = int(sub_k.sum())
+        oi = np.empty((P - 1, Ks), np.uint32)
+        ov = np.empty((P - 1, Ks), np.float32)
+        moff = np.concatenate([[0], np.cumsum(sub_k)])
+        for p in range(1, P):
+            for l in range(nl):
+                i, v = W.gen_message_layer(wl, 0, p, l, int(sub_k[l]))
+                oi[p - 1, moff[l]:moff[l + 1]] = i
+                ov[p - 1, moff[l]:moff[l + 1]] = v
+        t0 = time.perf_counter()
+        orc.step(sub_off, sub_k, g, r, oi, ov, w, wl.lr)
+        return n, time.perf_counter() - t0
+    nl = 1
+    while nl < wl.L and off[nl] < 2_000_000:
+        nl += 1
+    n1, t1 = run_prefix(nl)
+    rate = n1 / max(t1, 1e-9)
+    target = rate * budget_s
+    nl2 = nl
+    while nl2 < wl.L and off[nl2 + 1] <= max(target, n1):
+        nl2 += 1
+    if nl2 > nl:
+        n2, t2 = run_prefix(nl2)
+    else:
+        n2, t2 = n1, t1
+    return {
+        "value": round(n2 / t2 / 1e9, 6),
+        "unit": "Gelem/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{wl.name}: first {nl2} of {wl.L} tensors ({n2:,} entries), one "
+                  f"sparsify + aggregate step with P={wl.P}, {t2:.1f} s single-threaded",
+    }
+
+
+def run_config(name, steps, warmup, do_cpu, flush):
+    import torch
+    from layer_wise_top_amd import lags, workloads as W
+
+    wl = W.get(name)
+    off = wl.offsets()
+    num, den = wl.ratios()
+    k = lags.k_table(off, num, den)
+    lay = lags.Layout(off, k)
+    P = wl.P
+    dev = torch.device("cuda", 0)
+    log(f"{name}: n={wl.n:,} L={wl.L} K={lay.K:,} P={P}: generating inputs")
+    t0 = time.time()
+    g = W.gen_grad(wl, 0)
+    w0 = W.gen_weights(wl)
+    oi, ov = W.gen_messages(wl, 0, k)
+    log(f"inputs generated in {time.time() - t0:.1f} s; moving to HBM")
+    g_d = torch.from_numpy(g).to(dev)
+    del g
+    w_d = torch.from_numpy(w0).to(dev)
+    del w0
+    r_d = torch.zeros(wl.n, dtype=torch.float32, device=dev)
+    mi = torch.empty((P, lay.K), dtype=torch.int32, device=dev)
+    mv = torch.empty((P, lay.K), dtype=torch.float32, device=dev)
+    if P > 1:
+        mi[1:].copy_(torch.from_numpy(oi.view(np.int32)))
+        mv[1:].copy_(torch.from_numpy(ov))
+    del oi, ov
+    ws = lags.workspace(lay, P, device=dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        lags.lags_sparsify_layers(lay, g_d, r_d, mi[0], mv[0], ws, 0, stream)
+        lags.lags_aggregate_apply(lay, w_d, mi, mv, P, wl.lr, ws, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    rep = lags.lags_workspace_report(lay, ws)
+    # distinct touched indices of one step (messages of the last warm step)
+    U = int(torch.unique(mi.view(-1)).numel())
+
+    # timed region: exactly `steps` steps bracketed by synchronisation
+    lags.lags_trace_enable(lay, True)
+    lags.lags_trace_read(lay)
+    times = []
+    if flush:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            scratch.fill_(i & 0xff)
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) for a, b in ev]
+        total_ms = sum(times)
+    else:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        total_ms = e0.elapsed_time(e1)
+    trace = lags.lags_trace_read(lay)
+    lags.lags_trace_enable(lay, False)
+    ms_per_step = total_ms / steps
+    kernels = {kname: round(ms / max(cnt, 1), 5) for kname, (ms, cnt) in trace.items() if cnt}
+    main_ms = kernels[DOMINANT]
+    b_main = main_kernel_bytes(wl, k)
+    achieved = b_main / (main_ms * 1e-3) / 1e9
+    B = algorithmic_bytes(wl.n, lay.K, P, U)
+    gelem = wl.n / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gelem, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy draws of the workload's shapes and distributions)",
+        "config": {
+            "workload": wl.name, "entries": wl.n, "tensors": wl.L, "sent_per_worker": lay.K,
+            "workers": P, "touched": U, "rho": "adaptive" if wl.rho_rule == "adaptive"
+            else f"{wl.rho_uniform[0]}/{wl.rho_uniform[1]}", "flush_infinity_cache": bool(flush),
+        },
+        "hbm_frac_step": round(B / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "alg_bytes_step": B,
+        "roofline": {
+            "kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None, "alg_bytes_per_launch": b_main, "avg_ms": main_ms,
+        },
+        "kernels_avg_ms": kernels,
+        "report": rep,
+    }
+    if times:
+        out["step_ms_min"] = round(min(times), 5)
+    del g_d, w_d, r_d, mi, mv, ws, scratch
+    torch.cuda.empty_cache()
+    if do_cpu:
+        log("timing the oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl, k)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="tfm1p3b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", action="store_true",
+                    help="write 512 MiB between steps (outside the step events) to evict the "
+                         "Infinity Cache; steps are then timed one by one")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on one GPU's share; other workers' messages are inputs)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from layer_wise_top_amd import workloads as W
+    names = list(W.ORDER) if args.config == "all" else [args.config]
+    for name in names:
+        out = run_config(name, args.steps, args.warmup, not args.no_cpu_baseline, args.flush)
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -50,9 +50,28 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint32_t ld_acquire(const uint32_t *p)
+// Cross-workgroup handoff inside one kernel.  The L2 of each XCD is not
+// coherent with the others for plain stores, and an agent-scope fence writes
+// back and invalidates the whole L2, which costs far more than the data
+// involved.  So data that another workgroup reads within the same kernel is
+// written with agent-scope atomics (stores with sc1, or read-modify-writes),
+// read with agent-scope atomic loads, and a writer waits for its own memory
+// operations to complete before it bumps the completion counter.
+__device__ __forceinline__ uint32_t ld_coherent(const uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_coherent(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_mem_done()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Exclusive prefix over the wave of small counts c in [0, 7].
@@ -455,12 +474,12 @@ __device__ void finalize_main(const SparsifyArgs &a, const LayerInfo &L, Sampled
 {
     uint32_t part = 0;
     for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
-        hist[b] = ld_acquire(&st->hist[b]);
+        hist[b] = ld_coherent(&st->hist[b]);
         part += hist[b];
     }
     uint32_t C;
     block_excl_scan(part, tmp, C);    // also orders the LDS writes above
-    const uint32_t overflow = ld_acquire(&st->overflow);
+    const uint32_t overflow = ld_coherent(&st->overflow);
     if (C < L.k || overflow) {
         if (threadIdx.x == 0) {
             st->status = kStExact;
@@ -531,14 +550,11 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
         const uint32_t v = hist[b];
         if (v) atomicAdd(&st->hist[b], v);
     }
-    __threadfence();
+    wait_mem_done();
     __syncthreads();
     if (threadIdx.x == 0) last = (atomicAdd(&st->done_main, 1u) == L.ntiles - 1u) ? 1u : 0u;
     __syncthreads();
-    if (last) {
-        __threadfence();
-        finalize_main(a, L, st, hist, tmp, res);
-    }
+    if (last) finalize_main(a, L, st, hist, tmp, res);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,21 +598,24 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
                     ++D;
                 } else if (bin == bstar) {
                     const uint32_t t = atomicAdd(&st->tbin_n, 1u);
-                    if (t < kTbinCap) a.tbin[(uint64_t)sid * kTbinCap + t] = c;
+                    if (t < kTbinCap) {
+                        uint32_t *e = reinterpret_cast<uint32_t *>(a.tbin + (uint64_t)sid * kTbinCap + t);
+                        st_coherent(e, c.x);
+                        st_coherent(e + 1, c.y);
+                    }
                 }
             }
             D = wave_sum(D);
-            if (ln == 0) a.seg_sel[S.seg_base + s] = D;
+            if (ln == 0) st_coherent(&a.seg_sel[S.seg_base + s], D);
         }
     }
-    __threadfence();
+    wait_mem_done();
     __syncthreads();
     if (threadIdx.x == 0) last = (atomicAdd(&st->done_fin, 1u) == S.fin_nblocks - 1u) ? 1u : 0u;
     __syncthreads();
     if (!last) return;
-    __threadfence();
 
-    const uint32_t h = ld_acquire(&st->tbin_n);
+    const uint32_t h = ld_coherent(&st->tbin_n);
     if (status != kStOk || h > kTbinCap) {
         // exact multi-pass path over the accumulated values (the residual
         // buffer holds acc for every entry of the layer after k_main)
@@ -614,9 +633,9 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     // resolve the threshold inside bin bstar
     const uint32_t need = L.k - st->c_above;
     for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
-        const uint2 c = a.tbin[(uint64_t)sid * kTbinCap + p];
-        tk[p] = c.y & 0x7fffffffu;
-        ti[p] = c.x;
+        const uint32_t *e = reinterpret_cast<const uint32_t *>(a.tbin + (uint64_t)sid * kTbinCap + p);
+        ti[p] = ld_coherent(e);
+        tk[p] = ld_coherent(e + 1) & 0x7fffffffu;
     }
     __syncthreads();
     uint32_t e;
@@ -631,12 +650,12 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
         if (tk[p] > T || (tk[p] == T && ti[p] <= idx_cut))
             atomicAdd(&a.seg_sel[S.seg_base + seg_of(S, ti[p])], 1u);
     }
-    __threadfence();
+    wait_mem_done();
     __syncthreads();
     uint32_t carry = 0;
     for (uint32_t base = 0; base < S.nseg; base += kBlock) {
         const uint32_t s = base + threadIdx.x;
-        const uint32_t v = (s < S.nseg) ? ld_acquire(&a.seg_sel[S.seg_base + s]) : 0u;
+        const uint32_t v = (s < S.nseg) ? ld_coherent(&a.seg_sel[S.seg_base + s]) : 0u;
         uint32_t tot;
         const uint32_t ex = block_excl_scan(v, tmp, tot);
         if (s < S.nseg) a.seg_sel[S.seg_base + s] = carry + ex;
