@@ -149,8 +149,6 @@ def run_config(name, steps, warmup, do_cpu, flush):
     U = int(torch.unique(mi.view(-1)).numel())
 
     # timed region: exactly `steps` steps bracketed by synchronisation
-    lags.lags_trace_enable(lay, True)
-    lags.lags_trace_read(lay)
     times = []
     if flush:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -168,14 +166,21 @@ def run_config(name, steps, warmup, do_cpu, flush):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t_wall = time.perf_counter()
         e0.record(stream)
         for _ in range(steps):
             step()
         e1.record(stream)
         torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
         total_ms = e0.elapsed_time(e1)
+    # per-kernel device time: the same steps again with the library's tracer,
+    # which brackets every launch with HIP events on the launch stream
+    lags.lags_trace_enable(lay, True)
+    lags.lags_trace_read(lay)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        if flush:
+            scratch.fill_(0)
+        step()
     trace = lags.lags_trace_read(lay)
     lags.lags_trace_enable(lay, False)
     ms_per_step = total_ms / steps
@@ -230,6 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="tfm1p3b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer a few times (reference for traffic counters)")
     ap.add_argument("--flush", action="store_true",
                     help="write 512 MiB between steps (outside the step events) to evict the "
                          "Infinity Cache; steps are then timed one by one")
@@ -243,6 +250,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": {"read": 1 << 30, "write": 1 << 30},
+                          "launches": 3}), flush=True)
+        return
     from layer_wise_top_amd import workloads as W
     names = list(W.ORDER) if args.config == "all" else [args.config]
     for name in names:

@@ -42,11 +42,12 @@ struct lags_layout {
     std::vector<LayerInfo> linfo;
     std::vector<SampledInfo> sinfo;
     std::vector<uint2> main_work, fin_work;
+    std::vector<uint32_t> pos_layer;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
     // workspace plan (byte offsets)
     size_t ws_report = 0, ws_state = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
-           ws_agg = 0;
+           ws_fintot = 0, ws_agg = 0;
     // device tables, built on first use
     std::mutex mu;
     int device = -1;
@@ -55,6 +56,7 @@ struct lags_layout {
     SampledInfo *d_sinfo = nullptr;
     uint2 *d_main = nullptr, *d_fin = nullptr;
     uint32_t *d_moff = nullptr;
+    uint32_t *d_poslayer = nullptr;
     std::map<int32_t, AggTables> agg;
     // tracing
     bool trace = false;
@@ -157,6 +159,7 @@ int build_plan(lags_layout *lo)
             si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
             si.slot_hi = (uint32_t)(slot_base >> 32);
             si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
+            si.fin_first = (uint32_t)lo->fin_work.size();
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
             for (uint32_t t = 0; t < li.ntiles; ++t) stream_work.push_back(make_uint2((uint32_t)l, t));
             for (uint32_t b = 0; b < si.fin_nblocks; ++b)
@@ -171,6 +174,14 @@ int build_plan(lags_layout *lo)
     lo->main_work.insert(lo->main_work.end(), stream_work.begin(), stream_work.end());
     lo->nseg_total = seg_base;
     lo->slots_total = slot_base;
+    // layer of every kBlock-th message position (the aggregate's start pass)
+    const uint64_t npb = (lo->K + 1 + kBlock - 1) / kBlock;
+    lo->pos_layer.resize(npb);
+    for (uint64_t b = 0, l = 0; b < npb; ++b) {
+        const uint64_t j = b * kBlock;
+        while (l + 1 < (uint64_t)L && lo->moff[l + 1] <= j) ++l;
+        lo->pos_layer[b] = (uint32_t)l;
+    }
 
     const size_t ns = lo->sinfo.size();
     size_t at = 0;
@@ -186,6 +197,8 @@ int build_plan(lags_layout *lo)
     at = align_up(at + (size_t)lo->slots_total * 8, kAlign);
     lo->ws_tbin = at;
     at = align_up(at + ns * (size_t)kTbinCap * 8, kAlign);
+    lo->ws_fintot = at;
+    at = align_up(at + lo->fin_work.size() * 4, kAlign);
     lo->ws_agg = at;
     return LAGS_OK;
 }
@@ -217,7 +230,8 @@ int ensure_device(lags_layout *lo)
     const size_t b_m = align_up(std::max<size_t>(1, lo->main_work.size()) * sizeof(uint2), kAlign);
     const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(uint2), kAlign);
     const size_t b_o = align_up(lo->moff.size() * 4, kAlign);
-    const size_t total = b_l + b_s + b_m + b_f + b_o;
+    const size_t b_p = align_up(lo->pos_layer.size() * 4, kAlign);
+    const size_t total = b_l + b_s + b_m + b_f + b_o + b_p;
     std::vector<unsigned char> host(total, 0);
     std::memcpy(host.data(), lo->linfo.data(), lo->linfo.size() * sizeof(LayerInfo));
     if (!lo->sinfo.empty())
@@ -226,6 +240,7 @@ int ensure_device(lags_layout *lo)
     if (!lo->fin_work.empty())
         std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(uint2));
     std::memcpy(host.data() + b_l + b_s + b_m + b_f, lo->moff.data(), lo->moff.size() * 4);
+    std::memcpy(host.data() + b_l + b_s + b_m + b_f + b_o, lo->pos_layer.data(), lo->pos_layer.size() * 4);
     void *d = nullptr;
     if (hipMalloc(&d, total) != hipSuccess) return LAGS_ENOMEM;
     if (hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
@@ -240,6 +255,7 @@ int ensure_device(lags_layout *lo)
     lo->d_main = (uint2 *)(p + b_l + b_s);
     lo->d_fin = (uint2 *)(p + b_l + b_s + b_m);
     lo->d_moff = (uint32_t *)(p + b_l + b_s + b_m + b_f);
+    lo->d_poslayer = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o);
     return LAGS_OK;
 }
 
@@ -428,6 +444,7 @@ int lags_sparsify_layers(const lags_layout *clo, const float *grad, float *resid
     a.seg_sel = (uint32_t *)(w + lo->ws_segsel);
     a.slots = (uint2 *)(w + lo->ws_slots);
     a.tbin = (uint2 *)(w + lo->ws_tbin);
+    a.fin_total = (uint32_t *)(w + lo->ws_fintot);
     a.nsampled = (uint32_t)lo->sinfo.size();
     a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
     const uint32_t ns = a.nsampled;
@@ -436,6 +453,8 @@ int lags_sparsify_layers(const lags_layout *clo, const float *grad, float *resid
     rc = traced(lo, kKMain, s, [&] { return launch_main(a, (uint32_t)lo->main_work.size(), s); });
     if (rc != LAGS_OK) return rc;
     if (ns) {
+        rc = traced(lo, kKFinHist, s, [&] { return launch_fin_hist(a, (uint32_t)lo->fin_work.size(), s); });
+        if (rc != LAGS_OK) return rc;
         rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, (uint32_t)lo->fin_work.size(), s); });
         if (rc != LAGS_OK) return rc;
         rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, (uint32_t)lo->fin_work.size(), s); });
@@ -476,6 +495,7 @@ int lags_aggregate_apply(const lags_layout *clo, float *weights, const uint32_t 
     a.msg_val = msg_val;
     a.linfo = lo->d_linfo;
     a.moff = lo->d_moff;
+    a.pos_layer = lo->d_poslayer;
     a.cbase = t->cbase;
     a.csh = t->csh;
     a.chunk_layer = t->chunk_layer;
@@ -545,7 +565,7 @@ int32_t lags_num_kernels(void) { return kNumKernels; }
 
 const char *lags_kernel_name(int32_t id)
 {
-    static const char *names[kNumKernels] = {"k_sample", "k_main", "k_fin_select",
+    static const char *names[kNumKernels] = {"k_sample", "k_main", "k_fin_hist", "k_fin_select",
                                              "k_fin_emit", "k_agg_starts", "k_agg"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }

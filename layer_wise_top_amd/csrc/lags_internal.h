@@ -22,10 +22,11 @@ constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
 constexpr uint32_t kTbinCap = 4096;      // entries of the threshold bin kept per layer
 constexpr uint32_t kFinSegs = 16;        // segments per finishing workgroup
 // aggregate
-constexpr uint32_t kAggTargetEntries = 1024;  // expected entries per chunk
-constexpr uint32_t kAggCap = 2048;            // fast-path capacity (entries per chunk)
-constexpr uint32_t kAggTable = 4096;          // LDS hash slots (power of two, >= 2 * kAggCap)
-constexpr uint32_t kAggWindow = 4096;         // slow-path dense window
+constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
+constexpr uint32_t kAggCap = 1024;            // fast-path capacity (entries per chunk)
+constexpr uint32_t kAggTableLog2 = 11;
+constexpr uint32_t kAggTable = 1u << kAggTableLog2;  // LDS hash slots (>= 2 * kAggCap);
+                                                     // also the slow path's dense window
 
 // ---- layer classes --------------------------------------------------------
 enum : uint32_t {
@@ -64,7 +65,8 @@ struct SampledInfo {      // one per sampled layer, device table
     uint32_t j;           // rank of the guess inside the sample (1-based, from the top)
     uint32_t force_exact; // ratio too large for a guess: exact path
     uint32_t fin_nblocks; // finishing workgroups of this layer
-    uint32_t pad[3];
+    uint32_t fin_first;   // index of the layer's first finishing workgroup
+    uint32_t pad[2];
 };
 
 struct SampledState {     // per sampled layer, per call, in the workspace
@@ -74,7 +76,7 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t overflow;    // a segment had more candidates than slots
     uint32_t bstar;       // histogram bin holding the k-th largest candidate
     uint32_t c_above;     // candidates in bins above bstar
-    uint32_t done_main;   // streaming workgroups finished
+    uint32_t done_hist;   // histogram workgroups finished
     uint32_t done_fin;    // finishing workgroups finished
     uint32_t tbin_n;      // entries of bin bstar collected
     uint32_t T;           // k-th largest key of the layer
@@ -101,6 +103,7 @@ struct SparsifyArgs {
     uint32_t *seg_sel;
     uint2 *slots;
     uint2 *tbin;
+    uint32_t *fin_total;      // per finishing workgroup: count, then message offset
     uint32_t nsampled;
     uint32_t force_exact;
 };
@@ -111,6 +114,7 @@ struct AggArgs {
     const float *msg_val;
     const LayerInfo *linfo;
     const uint32_t *moff;       // [L+1]
+    const uint32_t *pos_layer;  // [ceil((K+1)/kBlock)] layer of message position b*kBlock
     const uint32_t *cbase;      // [L+1] first chunk of each layer
     const uint32_t *csh;        // [L] log2 chunk width
     const uint32_t *chunk_layer;// [NC]
@@ -125,13 +129,14 @@ struct AggArgs {
 
 // kernel ids for tracing
 enum : int32_t {
-    kKSample = 0, kKMain = 1, kKFinSelect = 2, kKFinEmit = 3,
-    kKAggStarts = 4, kKAgg = 5, kNumKernels = 6
+    kKSample = 0, kKMain = 1, kKFinHist = 2, kKFinSelect = 3, kKFinEmit = 4,
+    kKAggStarts = 5, kKAgg = 6, kNumKernels = 7
 };
 
 // launchers (lags_kernels.hip)
 hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_fin_hist(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);

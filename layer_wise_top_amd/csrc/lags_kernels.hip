@@ -15,12 +15,12 @@
 //                 layer's per-call state.
 //   k_main        the streaming pass: acc = grad + residual is written back
 //                 to the residual buffer; entries with |acc| key >= G are
-//                 compacted, in index order, into per-segment candidate slots
-//                 and counted in a per-layer histogram of bins above G.  The
-//                 last workgroup of a layer finds the bin holding the k-th
-//                 largest candidate.  Small layers (<= 4096 entries) are done
-//                 start to finish by one workgroup (exact radix select in
-//                 LDS); k == n layers are sent whole.
+//                 compacted, in index order, into per-segment candidate
+//                 slots.  Small layers (<= 4096 entries) are done start to
+//                 finish by one workgroup (exact radix select in LDS); k == n
+//                 layers are sent whole.
+//   k_fin_hist    histogram of the candidates in bins above G; the last
+//                 workgroup of a layer finds the bin holding the k-th largest.
 //   k_fin_select  counts, per segment, candidates above the threshold bin and
 //                 gathers the threshold bin's candidates; the last workgroup of
 //                 a layer resolves the exact threshold key T and the tie cut
@@ -107,7 +107,8 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x)
     return x;
 }
 
-// Block-wide exclusive scan (all kBlock threads must call).
+// Block-wide exclusive scan (all NT threads must call; tmp holds NT/64 words).
+template <int NT = kBlock>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *tmp, uint32_t &total)
 {
     const uint32_t w = threadIdx.x >> 6;
@@ -116,7 +117,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *tmp, uint32_t &total)
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         const uint32_t t = tmp[i];
         before += (i < (int)w) ? t : 0u;
         tot += t;
@@ -146,6 +147,7 @@ __device__ uint32_t block_excl_small(uint32_t c, uint32_t *tmp, uint32_t &total)
     return before + pre;
 }
 
+template <int NT = kBlock>
 __device__ uint32_t block_max(uint32_t v, uint32_t *tmp)
 {
     const uint32_t m = wave_max(v);
@@ -153,23 +155,24 @@ __device__ uint32_t block_max(uint32_t v, uint32_t *tmp)
     __syncthreads();
     uint32_t r = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) r = max(r, tmp[i]);
+    for (int i = 0; i < NT / 64; ++i) r = max(r, tmp[i]);
     __syncthreads();
     return r;
 }
 
-// Find, in an LDS histogram of nbins bins (nbins a multiple of kBlock), the bin
+// Find, in an LDS histogram of nbins bins (nbins a multiple of NT), the bin
 // holding the rank-th largest item (rank >= 1, counting from the top bin).
 // res[0] = bin, res[1] = items in higher bins.  The caller guarantees rank <=
-// total.  All threads call; res is valid after return.
+// total.  All NT threads call; res is valid after return.
+template <int NT = kBlock>
 __device__ void block_find_rank(const uint32_t *hist, uint32_t nbins, uint32_t rank,
                                 uint32_t *res, uint32_t *tmp)
 {
-    const uint32_t per = nbins / kBlock;
+    const uint32_t per = nbins / NT;
     uint32_t s = 0;
     for (uint32_t q = 0; q < per; ++q) s += hist[nbins - 1 - (threadIdx.x * per + q)];
     uint32_t tot;
-    uint32_t above = block_excl_scan(s, tmp, tot);
+    uint32_t above = block_excl_scan<NT>(s, tmp, tot);
     for (uint32_t q = 0; q < per; ++q) {
         const uint32_t b = nbins - 1 - (threadIdx.x * per + q);
         const uint32_t h = hist[b];
@@ -286,12 +289,21 @@ __device__ void exact_layer(const Src &src, uint32_t n, uint32_t k, uint32_t off
 }
 
 // ---------------------------------------------------------------------------
-// k_sample
-__global__ __launch_bounds__(kBlock) void k_sample(SparsifyArgs a)
+// k_sample: one 1024-thread workgroup per sampled layer.  The whole sample is
+// requested at once (4 float4 of grad and residual per thread), its keys go
+// to LDS, and two 12-bit histogram passes locate the 24-bit key prefix that
+// holds the rank-th largest sample key.  The guess G is that prefix's lower
+// edge, so at least as many entries reach G as reach the exact sample
+// quantile.
+constexpr int kSampleThreads = 1024;
+constexpr uint32_t kSampleBins = 4096;
+
+__global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 {
+    constexpr int NT = kSampleThreads;
     __shared__ uint32_t keys[kSampleMax];
-    __shared__ uint32_t hist[kBlock];
-    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t hist[kSampleBins];
+    __shared__ uint32_t tmp[NT / 64];
     __shared__ uint32_t res[2];
 
     if (blockIdx.x == 0 && threadIdx.x < 2) a.report[kRepSampled + threadIdx.x] = 0;
@@ -300,7 +312,8 @@ __global__ __launch_bounds__(kBlock) void k_sample(SparsifyArgs a)
     const LayerInfo L = a.linfo[S.layer];
     SampledState *st = a.state + blockIdx.x;
     uint32_t *stw = reinterpret_cast<uint32_t *>(st);
-    for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += kBlock) stw[t] = 0;
+    for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += NT) stw[t] = 0;
+    for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
     __syncthreads();
     if (S.force_exact || a.force_exact) {
         if (threadIdx.x == 0) {
@@ -309,44 +322,63 @@ __global__ __launch_bounds__(kBlock) void k_sample(SparsifyArgs a)
         }
         return;
     }
-    uint32_t cnt, rank;
+    uint32_t cnt, rank, m = 0;
     if (S.full_sample) {
         cnt = L.n;
         rank = L.k;
-        for (uint32_t i = threadIdx.x; i < cnt; i += kBlock)
-            keys[i] = key_of(a.grad[L.off + i] + a.res[L.off + i]);
+        for (uint32_t i = threadIdx.x; i < cnt; i += NT) {
+            const uint32_t key = key_of(a.grad[L.off + i] + a.res[L.off + i]);
+            keys[i] = key;
+            m = max(m, key);
+            atomicAdd(&hist[key >> 19], 1u);
+        }
     } else {
         cnt = S.nchunk * kSampleChunk;
         rank = S.j;
+        constexpr int QPT = kSampleMax / 4 / NT;            // float4 per thread
+        constexpr uint32_t QPC = kSampleChunk / 4;          // float4 per chunk
         const uint64_t span = S.b4 - S.a4 - kSampleChunk;
-        for (uint32_t e = threadIdx.x; e < cnt; e += kBlock) {
-            const uint32_t c = e / kSampleChunk, l = e % kSampleChunk;
-            const uint32_t pos = S.a4 + (uint32_t)((uint64_t)c * span / (S.nchunk - 1)) + l;
-            keys[e] = key_of(a.grad[pos] + a.res[pos]);
+        const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
+        const v4f *r4 = reinterpret_cast<const v4f *>(a.res);
+        v4f gv[QPT], rv[QPT];
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const uint32_t qi = threadIdx.x + u * NT;
+            const uint32_t c = qi / QPC, part = qi % QPC;
+            const uint32_t start = S.a4 + ((uint32_t)((uint64_t)c * span / (S.nchunk - 1)) & ~3u);
+            const uint32_t q = start / 4u + part;
+            gv[u] = g4[q];
+            rv[u] = r4[q];
+        }
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const uint32_t qi = threadIdx.x + u * NT;
+            const v4f acc = gv[u] + rv[u];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_of(acc[j]);
+                keys[qi * 4 + j] = key;
+                m = max(m, key);
+                atomicAdd(&hist[key >> 19], 1u);
+            }
         }
     }
     __syncthreads();
-    // rank-th largest key of the sample: four 8-bit digits, most significant first
-    uint32_t prefix = 0;
-    for (int sh = 24; sh >= 0; sh -= 8) {
-        hist[threadIdx.x] = 0;
-        __syncthreads();
-        for (uint32_t e = threadIdx.x; e < cnt; e += kBlock) {
-            const uint32_t key = keys[e];
-            const bool same = (sh == 24) ? true : ((key >> (sh + 8)) == (prefix >> (sh + 8)));
-            if (same) atomicAdd(&hist[(key >> sh) & 255u], 1u);
-        }
-        __syncthreads();
-        block_find_rank(hist, kBlock, rank, res, tmp);
-        prefix |= res[0] << sh;
-        rank -= res[1];
-        __syncthreads();
+    const uint32_t M = block_max<NT>(m, tmp);
+    block_find_rank<NT>(hist, kSampleBins, rank, res, tmp);
+    const uint32_t b1 = res[0];
+    const uint32_t rank2 = rank - res[1];
+    __syncthreads();
+    for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
+    __syncthreads();
+    for (uint32_t e = threadIdx.x; e < cnt; e += NT) {
+        const uint32_t key = keys[e];
+        if ((key >> 19) == b1) atomicAdd(&hist[(key >> 7) & (kSampleBins - 1)], 1u);
     }
-    uint32_t m = 0;
-    for (uint32_t e = threadIdx.x; e < cnt; e += kBlock) m = max(m, keys[e]);
-    const uint32_t M = block_max(m, tmp);
+    __syncthreads();
+    block_find_rank<NT>(hist, kSampleBins, rank2, res, tmp);
     if (threadIdx.x == 0) {
-        const uint32_t G = prefix;
+        const uint32_t G = (b1 << 19) | (res[0] << 7);
         uint32_t sh = 0;
         while (sh < 31u && (uint64_t)(M - G) >= ((uint64_t)kNBins << sh)) ++sh;
         st->G = G;
@@ -355,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(SparsifyArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// k_main
+// k_main: the streaming pass.
 
 __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t SH)
 {
@@ -363,30 +395,30 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
 }
 
 // Append the flagged entries of a lane group (up to 4 per lane, index order
-// lane-major, then j) to the segment's slots and the LDS histogram.
+// lane-major, then j) to the segment's slots.  Wave-uniform call.
 __device__ __forceinline__ void append_candidates(uint32_t cmask, const uint32_t *idx, const float *v,
-                                                  uint32_t &run, uint2 *slots, uint32_t cap,
-                                                  uint32_t G, uint32_t SH, uint32_t *hist)
+                                                  uint32_t &run, uint2 *slots, uint32_t cap)
 {
     uint32_t tot;
     const uint32_t pre = wave_prefix3((uint32_t)__popc(cmask), tot);
-    if (tot == 0) return;
     uint32_t pos = run + pre;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (cmask & (1u << j)) {
             if (pos < cap) slots[pos] = make_uint2(idx[j], __float_as_uint(v[j]));
-            atomicAdd(&hist[cand_bin(key_of(v[j]), G, SH)], 1u);
             ++pos;
         }
     }
     run += tot;
 }
 
+// One wave streams one segment of a sampled layer: acc = grad + residual is
+// written back to the residual buffer, and entries with key >= G are appended
+// in index order to the segment's candidate slots.
 __device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const SampledInfo &S,
-                                SampledState *st, uint32_t seg, uint32_t G, uint32_t SH, uint32_t *hist)
+                                uint32_t seg, uint32_t G)
 {
-    constexpr int U = 4;
+    constexpr int U = 2;
     const uint32_t ln = lane_id();
     const uint32_t e0 = S.a4 + seg * kSeg;
     const uint32_t e1 = min(e0 + kSeg, S.b4);
@@ -401,13 +433,13 @@ __device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const
         const uint32_t i = L.off + ln;
         uint32_t cm = 0;
         v[0] = v[1] = v[2] = v[3] = 0.0f;
-        idx[0] = i;
+        idx[0] = idx[1] = idx[2] = idx[3] = i;
         if (i < S.a4) {
             v[0] = a.grad[i] + a.res[i];
             a.res[i] = v[0];
             if (key_of(v[0]) >= G) cm = 1;
         }
-        append_candidates(cm, idx, v, run, slots, cap, G, SH, hist);
+        append_candidates(cm, idx, v, run, slots, cap);
     }
 
     const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
@@ -443,7 +475,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const
                     idx[j] = 4u * q + j;
                     v[j] = acc[j];
                 }
-                append_candidates(cm, idx, v, run, slots, cap, G, SH, hist);
+                append_candidates(cm, idx, v, run, slots, cap);
             }
         }
     }
@@ -453,48 +485,15 @@ __device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const
         const uint32_t i = S.b4 + ln;
         uint32_t cm = 0;
         v[0] = v[1] = v[2] = v[3] = 0.0f;
-        idx[0] = i;
+        idx[0] = idx[1] = idx[2] = idx[3] = i;
         if (i < end) {
             v[0] = a.grad[i] + a.res[i];
             a.res[i] = v[0];
             if (key_of(v[0]) >= G) cm = 1;
         }
-        append_candidates(cm, idx, v, run, slots, cap, G, SH, hist);
+        append_candidates(cm, idx, v, run, slots, cap);
     }
-    if (ln == 0) {
-        a.seg_count[S.seg_base + seg] = run;
-        if (run > cap) atomicOr(&st->overflow, 1u);
-    }
-}
-
-// Last streaming workgroup of a sampled layer: locate the candidate bin that
-// holds the k-th largest, or mark the layer for the exact path.
-__device__ void finalize_main(const SparsifyArgs &a, const LayerInfo &L, SampledState *st,
-                              uint32_t *hist, uint32_t *tmp, uint32_t *res)
-{
-    uint32_t part = 0;
-    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
-        hist[b] = ld_coherent(&st->hist[b]);
-        part += hist[b];
-    }
-    uint32_t C;
-    block_excl_scan(part, tmp, C);    // also orders the LDS writes above
-    const uint32_t overflow = ld_coherent(&st->overflow);
-    if (C < L.k || overflow) {
-        if (threadIdx.x == 0) {
-            st->status = kStExact;
-            atomicAdd(&a.report[kRepSampled], 1u);
-            atomicAdd(&a.report[kRepExact], 1u);
-        }
-        return;
-    }
-    block_find_rank(hist, kNBins, L.k, res, tmp);
-    if (threadIdx.x == 0) {
-        st->bstar = res[0];
-        st->c_above = res[1];
-        st->status = kStOk;
-        atomicAdd(&a.report[kRepSampled], 1u);
-    }
+    if (ln == 0) a.seg_count[S.seg_base + seg] = run;
 }
 
 __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
@@ -503,7 +502,6 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
     __shared__ float acc_s[kSmallMax];
     __shared__ uint32_t tmp[kWaves];
     __shared__ uint32_t res[2];
-    __shared__ uint32_t last;
 
     const uint2 w = a.main_work[blockIdx.x];
     const LayerInfo L = a.linfo[w.x];
@@ -537,28 +535,16 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
         return;
     }
 
-    // sampled layer, streaming tile w.y
+    // sampled layer, streaming tile w.y: one segment per wave
     const SampledInfo S = a.sinfo[L.sid];
-    SampledState *st = a.state + L.sid;
-    const uint32_t G = st->G, SH = st->SH;
-    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) hist[b] = 0;
-    __syncthreads();
+    const uint32_t G = a.state[L.sid].G;
     const uint32_t seg = w.y * kTileSegs + (threadIdx.x >> 6);
-    if (seg < S.nseg) sampled_segment(a, L, S, st, seg, G, SH, hist);
-    __syncthreads();
-    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
-        const uint32_t v = hist[b];
-        if (v) atomicAdd(&st->hist[b], v);
-    }
-    wait_mem_done();
-    __syncthreads();
-    if (threadIdx.x == 0) last = (atomicAdd(&st->done_main, 1u) == L.ntiles - 1u) ? 1u : 0u;
-    __syncthreads();
-    if (last) finalize_main(a, L, st, hist, tmp, res);
+    if (seg < S.nseg) sampled_segment(a, L, S, seg, G);
 }
 
 // ---------------------------------------------------------------------------
-// k_fin_select
+// Finishing kernels.  fin_work lists, per sampled layer, workgroups of up to
+// kFinSegs consecutive segments; each wave of a workgroup takes every fourth.
 
 __device__ __forceinline__ uint32_t seg_of(const SampledInfo &S, uint32_t i)
 {
@@ -566,12 +552,88 @@ __device__ __forceinline__ uint32_t seg_of(const SampledInfo &S, uint32_t i)
     return min((i - S.a4) / kSeg, S.nseg - 1u);
 }
 
+// Last workgroup of a layer after the histogram pass: locate the candidate
+// bin that holds the k-th largest, or mark the layer for the exact path.
+__device__ void finalize_hist(const SparsifyArgs &a, const LayerInfo &L, SampledState *st,
+                              uint32_t *hist, uint32_t *tmp, uint32_t *res)
+{
+    uint32_t part = 0;
+    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
+        hist[b] = ld_coherent(&st->hist[b]);
+        part += hist[b];
+    }
+    uint32_t C;
+    block_excl_scan(part, tmp, C);    // also orders the LDS writes above
+    const uint32_t overflow = ld_coherent(&st->overflow);
+    if (C < L.k || overflow) {
+        if (threadIdx.x == 0) {
+            st->status = kStExact;
+            atomicAdd(&a.report[kRepSampled], 1u);
+            atomicAdd(&a.report[kRepExact], 1u);
+        }
+        return;
+    }
+    block_find_rank(hist, kNBins, L.k, res, tmp);
+    if (threadIdx.x == 0) {
+        st->bstar = res[0];
+        st->c_above = res[1];
+        st->status = kStOk;
+        atomicAdd(&a.report[kRepSampled], 1u);
+    }
+}
+
+// k_fin_hist: histogram of the candidates' keys in bins of width 2^SH above G.
+__global__ __launch_bounds__(kBlock) void k_fin_hist(SparsifyArgs a)
+{
+    __shared__ uint32_t hist[kNBins];
+    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t last;
+
+    const uint2 w = a.fin_work[blockIdx.x];
+    const uint32_t sid = w.x;
+    const SampledInfo S = a.sinfo[sid];
+    const LayerInfo L = a.linfo[S.layer];
+    SampledState *st = a.state + sid;
+    const uint32_t G = st->G, SH = st->SH;
+    const uint32_t ln = lane_id();
+    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) hist[b] = 0;
+    __syncthreads();
+    const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
+    const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
+    uint32_t ovf = 0;
+    for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
+        const uint32_t c = a.seg_count[S.seg_base + s];
+        if (c > S.cap) ovf = 1;
+        const uint32_t cnt = min(c, S.cap);
+        const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
+        for (uint32_t p = ln; p < cnt; p += 64)
+            atomicAdd(&hist[cand_bin(slots[p].y & 0x7fffffffu, G, SH)], 1u);
+    }
+    __syncthreads();
+    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
+        const uint32_t v = hist[b];
+        if (v) atomicAdd(&st->hist[b], v);
+    }
+    if (ovf && ln == 0) atomicOr(&st->overflow, 1u);
+    wait_mem_done();
+    __syncthreads();
+    if (threadIdx.x == 0) last = (atomicAdd(&st->done_hist, 1u) == S.fin_nblocks - 1u) ? 1u : 0u;
+    __syncthreads();
+    if (last) finalize_hist(a, L, st, hist, tmp, res);
+}
+
+// k_fin_select: count, per segment, candidates above the threshold bin and
+// gather the threshold bin; the last workgroup of a layer resolves the exact
+// threshold key T and the tie cut, and turns per-workgroup counts into
+// message offsets.  A layer whose guess failed is done here exactly.
 __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
 {
     __shared__ uint32_t hist[kNBins];
     __shared__ uint32_t tk[kTbinCap];
     __shared__ uint32_t ti[kTbinCap];
     __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t wtot[kWaves];
     __shared__ uint32_t res[2];
     __shared__ uint32_t last;
 
@@ -582,12 +644,14 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     SampledState *st = a.state + sid;
     const uint32_t status = st->status;
     const uint32_t ln = lane_id();
+    const uint32_t wv = threadIdx.x >> 6;
 
     if (status == kStOk) {
         const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
         const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
         const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
-        for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
+        uint32_t wsum = 0;
+        for (uint32_t s = w.y + wv; s < s_end; s += kWaves) {
             const uint32_t cnt = min(a.seg_count[S.seg_base + s], S.cap);
             const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
             uint32_t D = 0;
@@ -607,6 +671,14 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
             }
             D = wave_sum(D);
             if (ln == 0) st_coherent(&a.seg_sel[S.seg_base + s], D);
+            wsum += D;
+        }
+        if (ln == 0) wtot[wv] = wsum;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t t = 0;
+            for (int i = 0; i < kWaves; ++i) t += wtot[i];
+            st_coherent(&a.fin_total[blockIdx.x], t);
         }
     }
     wait_mem_done();
@@ -619,7 +691,6 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     if (status != kStOk || h > kTbinCap) {
         // exact multi-pass path over the accumulated values (the residual
         // buffer holds acc for every entry of the layer after k_main)
-        __syncthreads();
         if (threadIdx.x == 0) {
             if (status == kStOk) atomicAdd(&a.report[kRepExact], 1u);
             st->status = kStExact;
@@ -646,19 +717,24 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     const uint32_t ncut = block_radix_select([&](uint32_t p) { return ~ti[p]; },
                                              [&](uint32_t p) { return tk[p] == T; }, h, e, hist, tmp, res, &e2);
     const uint32_t idx_cut = ~ncut;
+    const uint32_t fin_first = S.fin_first;
     for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
-        if (tk[p] > T || (tk[p] == T && ti[p] <= idx_cut))
-            atomicAdd(&a.seg_sel[S.seg_base + seg_of(S, ti[p])], 1u);
+        if (tk[p] > T || (tk[p] == T && ti[p] <= idx_cut)) {
+            const uint32_t sg = seg_of(S, ti[p]);
+            atomicAdd(&a.seg_sel[S.seg_base + sg], 1u);
+            atomicAdd(&a.fin_total[fin_first + sg / kFinSegs], 1u);
+        }
     }
     wait_mem_done();
     __syncthreads();
+    // per-workgroup totals -> exclusive message offsets (in place)
     uint32_t carry = 0;
-    for (uint32_t base = 0; base < S.nseg; base += kBlock) {
-        const uint32_t s = base + threadIdx.x;
-        const uint32_t v = (s < S.nseg) ? ld_coherent(&a.seg_sel[S.seg_base + s]) : 0u;
+    for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
+        const uint32_t b = base + threadIdx.x;
+        const uint32_t v = (b < S.fin_nblocks) ? ld_coherent(&a.fin_total[fin_first + b]) : 0u;
         uint32_t tot;
         const uint32_t ex = block_excl_scan(v, tmp, tot);
-        if (s < S.nseg) a.seg_sel[S.seg_base + s] = carry + ex;
+        if (b < S.fin_nblocks) a.fin_total[fin_first + b] = carry + ex;
         carry += tot;
     }
     if (threadIdx.x == 0) {
@@ -667,10 +743,11 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     }
 }
 
-// ---------------------------------------------------------------------------
-// k_fin_emit
+// k_fin_emit: write the selected candidates of each segment, in index order,
+// and zero their residual.
 __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 {
+    __shared__ uint32_t sbase[kFinSegs];
     const uint2 w = a.fin_work[blockIdx.x];
     const uint32_t sid = w.x;
     const SampledState *st = a.state + sid;
@@ -680,12 +757,20 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
     const uint32_t T = st->T, cut = st->idx_cut;
     const uint32_t mend = L.moff + L.k;
     const uint32_t ln = lane_id();
-    const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
     const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
+    if (threadIdx.x == 0) {
+        uint32_t run = L.moff + a.fin_total[blockIdx.x];
+        for (uint32_t s = w.y; s < s_end; ++s) {
+            sbase[s - w.y] = run;
+            run += a.seg_sel[S.seg_base + s];
+        }
+    }
+    __syncthreads();
+    const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
     for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
         const uint32_t cnt = min(a.seg_count[S.seg_base + s], S.cap);
         const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
-        const uint32_t base = L.moff + a.seg_sel[S.seg_base + s];
+        const uint32_t base = sbase[s - w.y];
         uint32_t run = 0;
         for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
             const uint32_t p = p0 + ln;
@@ -694,7 +779,9 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
             if (p < cnt) {
                 c = slots[p];
                 const uint32_t key = c.y & 0x7fffffffu;
-                sel = key > T || (key == T && c.x <= cut);
+                // candidates always lie in their layer; the range test keeps a
+                // damaged workspace from turning into a stray store
+                sel = (c.x - L.off < L.n) && (key > T || (key == T && c.x <= cut));
             }
             const uint64_t m = __ballot(sel);
             if (sel) {
@@ -713,49 +800,69 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 // ---------------------------------------------------------------------------
 // aggregate
 
+// k_agg_starts: for every worker p and message position j in [0, K], the
+// chunk of entry j; chunk starts are written where the chunk id changes.
 __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
 {
-    __shared__ uint32_t l0s;
+    __shared__ uint32_t t_off[kBlock + 2], t_n[kBlock + 2], t_moff[kBlock + 3], t_cb[kBlock + 2],
+        t_sh[kBlock + 2];
+    __shared__ uint32_t lrange[2];
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) a.report[kRepBad + threadIdx.x] = 0;
     const uint32_t p = blockIdx.y;
     const uint32_t j0 = blockIdx.x * kBlock;
+    const uint32_t j = j0 + threadIdx.x;
+    const uint32_t *row = a.msg_idx + (uint64_t)p * a.K;
+    // message entries first: they do not depend on the layer lookup
+    const uint32_t x = (j < a.K) ? row[j] : 0u;
+    const uint32_t xp = (j > 0 && j <= a.K) ? row[j - 1] : 0u;
     if (threadIdx.x == 0) {
-        uint32_t lo = 0, hi = a.L;      // largest l in [0, L) with moff[l] <= j0
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) / 2;
-            if (a.moff[mid] <= j0) lo = mid; else hi = mid;
-        }
-        l0s = lo;
+        const uint32_t l0 = a.pos_layer[blockIdx.x];
+        const uint32_t npb = gridDim.x;
+        const uint32_t l1 = (blockIdx.x + 1 < npb) ? a.pos_layer[blockIdx.x + 1] : a.L - 1;
+        lrange[0] = l0 > 0 ? l0 - 1 : 0;   // the layer of position j0 - 1 may precede l0
+        lrange[1] = l1;
     }
     __syncthreads();
-    const uint32_t j = j0 + threadIdx.x;
+    const uint32_t la = lrange[0], nl = lrange[1] - la + 1;   // nl <= kBlock + 2
+    for (uint32_t t = threadIdx.x; t < nl; t += kBlock) {
+        const LayerInfo Li = a.linfo[la + t];
+        t_off[t] = Li.off;
+        t_n[t] = Li.n;
+        t_moff[t] = Li.moff;
+        t_cb[t] = a.cbase[la + t];
+        t_sh[t] = a.csh[la + t];
+    }
+    if (threadIdx.x == 0) t_moff[nl] = a.moff[la + nl];
+    __syncthreads();
     if (j > a.K) return;
-    const uint32_t *row = a.msg_idx + (uint64_t)p * a.K;
-    auto chunk_at = [&](uint32_t jj, uint32_t ll) -> uint32_t {
-        const LayerInfo Li = a.linfo[ll];
-        uint32_t rel = row[jj] - Li.off;
-        if (rel >= Li.n) rel = 0;          // invalid entry: counted by k_agg
-        return a.cbase[ll] + (rel >> a.csh[ll]);
+    auto chunk_of = [&](uint32_t xx, uint32_t t) -> uint32_t {
+        uint32_t rel = xx - t_off[t];
+        if (rel >= t_n[t]) rel = 0;          // invalid entry: counted by k_agg
+        return t_cb[t] + (rel >> t_sh[t]);
     };
-    uint32_t l = l0s;
-    while (l + 1 < a.L && a.moff[l + 1] <= j) ++l;
-    const uint32_t c = (j == a.K) ? a.NC : chunk_at(j, l);
+    // local layer of position j: largest t with t_moff[t] <= j
+    uint32_t t = 0;
+    while (t + 1 < nl && t_moff[t + 1] <= j) ++t;
+    const uint32_t c = (j == a.K) ? a.NC : chunk_of(x, t);
     uint32_t cp = 0xffffffffu;
     if (j > 0) {
-        uint32_t lp = l;
-        while (lp > 0 && a.moff[lp] > j - 1) --lp;
-        cp = chunk_at(j - 1, lp);
+        uint32_t tp = t;
+        while (tp > 0 && t_moff[tp] > j - 1) --tp;
+        cp = chunk_of(xp, tp);
     }
     uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
     for (uint32_t cc = cp + 1u; cc <= c && cc <= a.NC; ++cc) srow[cc] = j;
 }
 
+// k_agg: one workgroup per index chunk [lo, hi) of one layer.  Dynamic LDS:
+// keys[kAggTable], vals[kAggTable], ws0[P], pre[P+1].
 __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
 {
-    __shared__ uint32_t keys[kAggTable];
-    __shared__ float vals[kAggTable];
-    __shared__ uint32_t ws0[1024];
-    __shared__ uint32_t pre[1025];
+    extern __shared__ uint32_t dyn[];
+    uint32_t *keys = dyn;
+    float *vals = reinterpret_cast<float *>(dyn + kAggTable);
+    uint32_t *ws0 = dyn + 2 * kAggTable;
+    uint32_t *pre = ws0 + a.P;
     __shared__ uint32_t tmp[kWaves];
 
     const uint32_t c = blockIdx.x;
@@ -765,7 +872,7 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     const uint64_t lo64 = (uint64_t)L.off + ((uint64_t)(c - a.cbase[l]) << sh);
     const uint64_t hi64 = min(lo64 + (1ull << sh), (uint64_t)L.off + L.n);
     const uint32_t lo = (uint32_t)lo64, hi = (uint32_t)hi64;
-    const uint32_t m0 = a.moff[l], m1 = a.moff[l + 1];
+    const uint32_t m0 = L.moff, m1 = L.moff + L.k;
     const uint32_t P = a.P;
 
     uint32_t carry = 0;
@@ -801,39 +908,46 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
         int slot[EPT];
         uint32_t wk[EPT];
         float v[EPT];
+        uint32_t xs[EPT];
 #pragma unroll
-        for (int q = 0; q < EPT; ++q) {
+        for (int q = 0; q < EPT; ++q) {       // issue every entry load first
+            const uint32_t e = threadIdx.x + q * kBlock;
             slot[q] = -1;
             wk[q] = 0;
             v[q] = 0.0f;
-            const uint32_t e = threadIdx.x + q * kBlock;
+            xs[q] = 0xffffffffu;
             if (e < E) {
                 uint32_t plo = 0, phi = P;   // pre[plo] <= e < pre[phi]
                 while (phi - plo > 1) {
                     const uint32_t mid = (plo + phi) / 2;
                     if (pre[mid] <= e) plo = mid; else phi = mid;
                 }
-                const uint32_t j = ws0[plo] + (e - pre[plo]);
-                const uint64_t at = (uint64_t)plo * a.K + j;
-                const uint32_t x = a.msg_idx[at];
-                if (x < lo || x >= hi) {
-                    ++bad;
-                } else {
-                    const uint32_t key = x - lo;
-                    uint32_t hsh = (key * 2654435761u) >> 20;   // 12-bit hash
-                    while (true) {
-                        const uint32_t old = atomicCAS(&keys[hsh], 0xffffffffu, key);
-                        if (old == 0xffffffffu || old == key) break;
-                        hsh = (hsh + 1u) & (kAggTable - 1u);
-                    }
-                    slot[q] = (int)hsh;
-                    wk[q] = plo;
-                    v[q] = a.msg_val[at];
-                }
+                const uint64_t at = (uint64_t)plo * a.K + ws0[plo] + (e - pre[plo]);
+                wk[q] = plo;
+                xs[q] = a.msg_idx[at];
+                v[q] = a.msg_val[at];
             }
         }
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const uint32_t e = threadIdx.x + q * kBlock;
+            if (e >= E) continue;
+            const uint32_t x = xs[q];
+            if (x < lo || x >= hi) {
+                ++bad;
+                continue;
+            }
+            const uint32_t key = x - lo;
+            uint32_t hsh = (key * 2654435761u) >> (32 - kAggTableLog2);
+            while (true) {
+                const uint32_t old = atomicCAS(&keys[hsh], 0xffffffffu, key);
+                if (old == 0xffffffffu || old == key) break;
+                hsh = (hsh + 1u) & (kAggTable - 1u);
+            }
+            slot[q] = (int)hsh;
+        }
         __syncthreads();
-        for (uint32_t p = 0; p < P; ++p) {
+        for (uint32_t p = 0; p < P; ++p) {   // worker order, one worker at a time
             if (pre[p + 1] == pre[p]) continue;
 #pragma unroll
             for (int q = 0; q < EPT; ++q)
@@ -852,11 +966,11 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
         // once per window, workers in order
         uint32_t *touched = keys;
         float *u = vals;
-        const uint32_t nwin = (hi - lo + kAggWindow - 1) / kAggWindow;
+        const uint32_t nwin = (hi - lo + kAggTable - 1) / kAggTable;
         for (uint32_t win = 0; win < nwin; ++win) {
-            const uint32_t wlo = lo + win * kAggWindow;
-            const uint32_t whi = min(wlo + kAggWindow, hi);
-            for (uint32_t t = threadIdx.x; t < kAggWindow; t += kBlock) {
+            const uint32_t wlo = lo + win * kAggTable;
+            const uint32_t whi = min(wlo + kAggTable, hi);
+            for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
                 touched[t] = 0;
                 u[t] = 0.0f;
             }
@@ -895,13 +1009,19 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
 
 hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_sample, dim3(nblocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_sample, dim3(nblocks), dim3(kSampleThreads), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     hipLaunchKernelGGL(k_main, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fin_hist(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fin_hist, dim3(nblocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
@@ -926,7 +1046,8 @@ hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
 
 hipError_t launch_agg(const AggArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_agg, dim3(a.NC), dim3(kBlock), 0, s, a);
+    const size_t lds = (2u * kAggTable + 2u * a.P + 1u) * sizeof(uint32_t);
+    hipLaunchKernelGGL(k_agg, dim3(a.NC), dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 

@@ -104,6 +104,8 @@ LAYOUT_CASES = [
     ("int", [300000, 12345], (1, 1000), "int", 8, 3),
     ("rand_k", [3000, 70000, 12000, 4200, 500000], "rand", "normal", 6, 2),
     ("many_layers", [97] * 300 + [5000] * 20 + [33333] * 5, (1, 100), "normal", 3, 2),
+    # one sent entry per layer: a block of 256 message positions spans 258 layers
+    ("tiny_layers", [5] * 700 + [20000], (1, 100), "normal", 4, 2),
 ]
 
 
