@@ -67,8 +67,9 @@ struct lags_layout {
 
 namespace {
 
-// Chunk widths of the aggregate for P workers: per layer, a power of two such
-// that a chunk holds about kAggTargetEntries message entries over all workers.
+// Chunk widths of the aggregate for P workers: per layer, a power of two (at
+// most 2^kAggMaxWidthLog2) such that a chunk holds about kAggTargetEntries
+// message entries over all workers.
 void plan_agg(const lags_layout *lo, int32_t P, std::vector<uint32_t> &cbase,
               std::vector<uint32_t> &csh, uint32_t &NC)
 {
@@ -79,7 +80,7 @@ void plan_agg(const lags_layout *lo, int32_t P, std::vector<uint32_t> &cbase,
         const double nl = lo->linfo[l].n, kl = lo->linfo[l].k;
         const double width = (double)kAggTargetEntries * nl / ((double)P * kl);
         int s = 0;
-        while (s < 31 && std::ldexp(1.0, s + 1) <= width) ++s;
+        while (s < (int)kAggMaxWidthLog2 && std::ldexp(1.0, s + 1) <= width) ++s;
         csh[l] = (uint32_t)s;
         cbase[l] = (uint32_t)total;
         total += ((uint64_t)lo->linfo[l].n + (1ull << s) - 1) >> s;
@@ -174,11 +175,11 @@ int build_plan(lags_layout *lo)
     lo->main_work.insert(lo->main_work.end(), stream_work.begin(), stream_work.end());
     lo->nseg_total = seg_base;
     lo->slots_total = slot_base;
-    // layer of every kBlock-th message position (the aggregate's start pass)
-    const uint64_t npb = (lo->K + 1 + kBlock - 1) / kBlock;
+    // layer of every kStartsBlock-th message position (the aggregate's start pass)
+    const uint64_t npb = (lo->K + 1 + kStartsBlock - 1) / kStartsBlock;
     lo->pos_layer.resize(npb);
     for (uint64_t b = 0, l = 0; b < npb; ++b) {
-        const uint64_t j = b * kBlock;
+        const uint64_t j = b * kStartsBlock;
         while (l + 1 < (uint64_t)L && lo->moff[l + 1] <= j) ++l;
         lo->pos_layer[b] = (uint32_t)l;
     }

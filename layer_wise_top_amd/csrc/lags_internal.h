@@ -20,13 +20,15 @@ constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident
 constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
 constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
 constexpr uint32_t kTbinCap = 4096;      // entries of the threshold bin kept per layer
-constexpr uint32_t kFinSegs = 16;        // segments per finishing workgroup
+constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup
 // aggregate
 constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
 constexpr uint32_t kAggCap = 1024;            // fast-path capacity (entries per chunk)
+constexpr uint32_t kStartsBlock = 1024;       // message positions per start-pass workgroup
 constexpr uint32_t kAggTableLog2 = 11;
 constexpr uint32_t kAggTable = 1u << kAggTableLog2;  // LDS hash slots (>= 2 * kAggCap);
                                                      // also the slow path's dense window
+constexpr uint32_t kAggMaxWidthLog2 = 30;     // chunk width cap (entries)
 
 // ---- layer classes --------------------------------------------------------
 enum : uint32_t {
@@ -114,7 +116,7 @@ struct AggArgs {
     const float *msg_val;
     const LayerInfo *linfo;
     const uint32_t *moff;       // [L+1]
-    const uint32_t *pos_layer;  // [ceil((K+1)/kBlock)] layer of message position b*kBlock
+    const uint32_t *pos_layer;  // [ceil((K+1)/kStartsBlock)] layer of position b*kStartsBlock
     const uint32_t *cbase;      // [L+1] first chunk of each layer
     const uint32_t *csh;        // [L] log2 chunk width
     const uint32_t *chunk_layer;// [NC]

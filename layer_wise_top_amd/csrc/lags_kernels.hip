@@ -582,6 +582,43 @@ __device__ void finalize_hist(const SparsifyArgs &a, const LayerInfo &L, Sampled
     }
 }
 
+// The segments a wave handles in a finishing workgroup (every kWaves-th of the
+// workgroup's kFinSegs), with their candidate counts and first 64 slots loaded
+// up front so that one memory round trip serves all of them.
+constexpr int kSegsPerWave = kFinSegs / kWaves;
+struct WaveSegs {
+    uint32_t s0;                      // first segment of the workgroup
+    uint32_t wave;
+    uint32_t nseg;
+    uint32_t cnt[kSegsPerWave];
+    uint2 first[kSegsPerWave];
+    __device__ uint32_t seg(int i) const { return s0 + wave + (uint32_t)i * kWaves; }
+    __device__ bool valid(int i) const { return seg(i) < nseg; }
+    __device__ const uint2 *slots(const SparsifyArgs &a, const SampledInfo &S, int i) const
+    {
+        return a.slots + (((uint64_t)S.slot_hi << 32) | S.slot_lo) + (uint64_t)seg(i) * S.cap;
+    }
+    // returns 1 if a segment had more candidates than slots
+    __device__ uint32_t load(const SparsifyArgs &a, const SampledInfo &S, uint32_t first_seg,
+                             uint32_t wv, uint32_t ln)
+    {
+        s0 = first_seg;
+        wave = wv;
+        nseg = min(first_seg + kFinSegs, S.nseg);
+        uint32_t raw[kSegsPerWave];
+#pragma unroll
+        for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[S.seg_base + seg(i)] : 0u;
+        uint32_t ovf = 0;
+#pragma unroll
+        for (int i = 0; i < kSegsPerWave; ++i) {
+            ovf |= raw[i] > S.cap ? 1u : 0u;
+            cnt[i] = min(raw[i], S.cap);
+            first[i] = (ln < cnt[i]) ? slots(a, S, i)[ln] : make_uint2(0, 0);
+        }
+        return ovf;
+    }
+};
+
 // k_fin_hist: histogram of the candidates' keys in bins of width 2^SH above G.
 __global__ __launch_bounds__(kBlock) void k_fin_hist(SparsifyArgs a)
 {
@@ -599,16 +636,12 @@ __global__ __launch_bounds__(kBlock) void k_fin_hist(SparsifyArgs a)
     const uint32_t ln = lane_id();
     for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) hist[b] = 0;
     __syncthreads();
-    const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
-    const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
-    uint32_t ovf = 0;
-    for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
-        const uint32_t c = a.seg_count[S.seg_base + s];
-        if (c > S.cap) ovf = 1;
-        const uint32_t cnt = min(c, S.cap);
-        const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
-        for (uint32_t p = ln; p < cnt; p += 64)
-            atomicAdd(&hist[cand_bin(slots[p].y & 0x7fffffffu, G, SH)], 1u);
+    WaveSegs ws;
+    const uint32_t ovf = ws.load(a, S, w.y, threadIdx.x >> 6, ln);
+    for (int i = 0; i < kSegsPerWave; ++i) {
+        if (ln < ws.cnt[i]) atomicAdd(&hist[cand_bin(ws.first[i].y & 0x7fffffffu, G, SH)], 1u);
+        for (uint32_t p = 64 + ln; p < ws.cnt[i]; p += 64)
+            atomicAdd(&hist[cand_bin(ws.slots(a, S, i)[p].y & 0x7fffffffu, G, SH)], 1u);
     }
     __syncthreads();
     for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
@@ -648,15 +681,17 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
 
     if (status == kStOk) {
         const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
-        const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
-        const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
+        WaveSegs ws;
+        ws.load(a, S, w.y, wv, ln);
         uint32_t wsum = 0;
-        for (uint32_t s = w.y + wv; s < s_end; s += kWaves) {
-            const uint32_t cnt = min(a.seg_count[S.seg_base + s], S.cap);
-            const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
+        for (int i = 0; i < kSegsPerWave; ++i) {
+            if (!ws.valid(i)) continue;
+            const uint32_t s = ws.seg(i);
+            const uint32_t cnt = ws.cnt[i];
+            const uint2 *slots = ws.slots(a, S, i);
             uint32_t D = 0;
             for (uint32_t p = ln; p < cnt; p += 64) {
-                const uint2 c = slots[p];
+                const uint2 c = (p < 64) ? ws.first[i] : slots[p];
                 const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
                 if (bin > bstar) {
                     ++D;
@@ -765,19 +800,21 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
             run += a.seg_sel[S.seg_base + s];
         }
     }
+    WaveSegs ws;
+    ws.load(a, S, w.y, threadIdx.x >> 6, ln);
     __syncthreads();
-    const uint64_t slot0 = ((uint64_t)S.slot_hi << 32) | S.slot_lo;
-    for (uint32_t s = w.y + (threadIdx.x >> 6); s < s_end; s += kWaves) {
-        const uint32_t cnt = min(a.seg_count[S.seg_base + s], S.cap);
-        const uint2 *slots = a.slots + slot0 + (uint64_t)s * S.cap;
-        const uint32_t base = sbase[s - w.y];
+    for (int i = 0; i < kSegsPerWave; ++i) {
+        if (!ws.valid(i)) continue;
+        const uint32_t cnt = ws.cnt[i];
+        const uint2 *slots = ws.slots(a, S, i);
+        const uint32_t base = sbase[ws.seg(i) - w.y];
         uint32_t run = 0;
         for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
             const uint32_t p = p0 + ln;
             bool sel = false;
             uint2 c = make_uint2(0, 0);
             if (p < cnt) {
-                c = slots[p];
+                c = (p < 64) ? ws.first[i] : slots[p];
                 const uint32_t key = c.y & 0x7fffffffu;
                 // candidates always lie in their layer; the range test keeps a
                 // damaged workspace from turning into a stray store
@@ -801,29 +838,36 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 // aggregate
 
 // k_agg_starts: for every worker p and message position j in [0, K], the
-// chunk of entry j; chunk starts are written where the chunk id changes.
+// chunk of entry j; chunk starts are written where the chunk id changes.  A
+// workgroup covers kStartsBlock positions of one worker; the layers they span
+// (at most kStartsBlock + 2, since every layer sends at least one entry) are
+// staged in LDS.
 __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
 {
-    __shared__ uint32_t t_off[kBlock + 2], t_n[kBlock + 2], t_moff[kBlock + 3], t_cb[kBlock + 2],
-        t_sh[kBlock + 2];
+    constexpr int PPT = kStartsBlock / kBlock;      // positions per thread
+    constexpr uint32_t TL = kStartsBlock + 2;
+    __shared__ uint32_t t_off[TL], t_n[TL], t_moff[TL + 1], t_cb[TL], t_sh[TL];
     __shared__ uint32_t lrange[2];
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) a.report[kRepBad + threadIdx.x] = 0;
     const uint32_t p = blockIdx.y;
-    const uint32_t j0 = blockIdx.x * kBlock;
-    const uint32_t j = j0 + threadIdx.x;
+    const uint32_t j0 = blockIdx.x * kStartsBlock;
     const uint32_t *row = a.msg_idx + (uint64_t)p * a.K;
     // message entries first: they do not depend on the layer lookup
-    const uint32_t x = (j < a.K) ? row[j] : 0u;
-    const uint32_t xp = (j > 0 && j <= a.K) ? row[j - 1] : 0u;
+    uint32_t x[PPT], xp[PPT];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+        const uint32_t j = j0 + threadIdx.x + q * kBlock;
+        x[q] = (j < a.K) ? row[j] : 0u;
+        xp[q] = (j > 0 && j <= a.K) ? row[j - 1] : 0u;
+    }
     if (threadIdx.x == 0) {
         const uint32_t l0 = a.pos_layer[blockIdx.x];
-        const uint32_t npb = gridDim.x;
-        const uint32_t l1 = (blockIdx.x + 1 < npb) ? a.pos_layer[blockIdx.x + 1] : a.L - 1;
+        const uint32_t l1 = (blockIdx.x + 1 < gridDim.x) ? a.pos_layer[blockIdx.x + 1] : a.L - 1;
         lrange[0] = l0 > 0 ? l0 - 1 : 0;   // the layer of position j0 - 1 may precede l0
         lrange[1] = l1;
     }
     __syncthreads();
-    const uint32_t la = lrange[0], nl = lrange[1] - la + 1;   // nl <= kBlock + 2
+    const uint32_t la = lrange[0], nl = lrange[1] - la + 1;
     for (uint32_t t = threadIdx.x; t < nl; t += kBlock) {
         const LayerInfo Li = a.linfo[la + t];
         t_off[t] = Li.off;
@@ -834,24 +878,28 @@ __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
     }
     if (threadIdx.x == 0) t_moff[nl] = a.moff[la + nl];
     __syncthreads();
-    if (j > a.K) return;
     auto chunk_of = [&](uint32_t xx, uint32_t t) -> uint32_t {
         uint32_t rel = xx - t_off[t];
         if (rel >= t_n[t]) rel = 0;          // invalid entry: counted by k_agg
         return t_cb[t] + (rel >> t_sh[t]);
     };
-    // local layer of position j: largest t with t_moff[t] <= j
-    uint32_t t = 0;
-    while (t + 1 < nl && t_moff[t + 1] <= j) ++t;
-    const uint32_t c = (j == a.K) ? a.NC : chunk_of(x, t);
-    uint32_t cp = 0xffffffffu;
-    if (j > 0) {
-        uint32_t tp = t;
-        while (tp > 0 && t_moff[tp] > j - 1) --tp;
-        cp = chunk_of(xp, tp);
-    }
+    auto layer_of = [&](uint32_t j) -> uint32_t {   // largest t in [0, nl) with t_moff[t] <= j
+        uint32_t lo = 0, hi = nl;
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (t_moff[mid] <= j) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
     uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
-    for (uint32_t cc = cp + 1u; cc <= c && cc <= a.NC; ++cc) srow[cc] = j;
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+        const uint32_t j = j0 + threadIdx.x + q * kBlock;
+        if (j > a.K) continue;
+        const uint32_t c = (j == a.K) ? a.NC : chunk_of(x[q], layer_of(j));
+        const uint32_t cp = (j == 0) ? 0xffffffffu : chunk_of(xp[q], layer_of(j - 1));
+        for (uint32_t cc = cp + 1u; cc <= c && cc <= a.NC; ++cc) srow[cc] = j;
+    }
 }
 
 // k_agg: one workgroup per index chunk [lo, hi) of one layer.  Dynamic LDS:
@@ -954,6 +1002,7 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
                 if (slot[q] >= 0 && wk[q] == p) vals[slot[q]] = vals[slot[q]] + v[q];
             __syncthreads();
         }
+        // apply at every touched index
         for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
             const uint32_t key = keys[t];
             if (key != 0xffffffffu) {
@@ -1039,7 +1088,7 @@ hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t 
 
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
 {
-    const uint32_t nx = (a.K + 1u + kBlock - 1u) / kBlock;
+    const uint32_t nx = (a.K + 1u + kStartsBlock - 1u) / kStartsBlock;
     hipLaunchKernelGGL(k_agg_starts, dim3(nx, a.P), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
