@@ -52,6 +52,21 @@ def main_kernel_bytes(wl, k):
     return int(12 * wl.n + 8 * int(k[whole].sum()))
 
 
+def counters_traffic(workload):
+    """HBM bytes per k_main launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a 1 GiB copy), or None if they
+    were taken on another workload or on a different kernel source."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "k_main_counters.json")))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "layer_wise_top_amd", "csrc", "lags_kernels.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(wl, k, budget_s=20.0):
     """The oracle (single thread, as it stands) on a bounded sample of the
     same workload: the first layers of the table up to ~budget of CPU time
@@ -213,7 +228,8 @@ def run_config(name, steps, warmup, do_cpu, flush):
         "roofline": {
             "kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None, "alg_bytes_per_launch": b_main, "avg_ms": main_ms,
+            "traffic": counters_traffic(wl.name), "alg_bytes_per_launch": b_main,
+            "avg_ms": main_ms,
         },
         "kernels_avg_ms": kernels,
         "report": rep,
