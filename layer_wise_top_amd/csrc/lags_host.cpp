@@ -41,7 +41,8 @@ struct lags_layout {
     std::vector<uint32_t> off, k, moff;
     std::vector<LayerInfo> linfo;
     std::vector<SampledInfo> sinfo;
-    std::vector<uint2> main_work, fin_work;
+    std::vector<MainWork> main_work;
+    std::vector<uint2> fin_work;
     std::vector<uint32_t> pos_layer;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
@@ -54,7 +55,8 @@ struct lags_layout {
     void *dev = nullptr;
     LayerInfo *d_linfo = nullptr;
     SampledInfo *d_sinfo = nullptr;
-    uint2 *d_main = nullptr, *d_fin = nullptr;
+    MainWork *d_main = nullptr;
+    uint2 *d_fin = nullptr;
     uint32_t *d_moff = nullptr;
     uint32_t *d_poslayer = nullptr;
     std::map<int32_t, AggTables> agg;
@@ -111,7 +113,14 @@ int build_plan(lags_layout *lo)
     lo->linfo.resize(L);
     uint32_t seg_base = 0;
     uint64_t slot_base = 0;
-    std::vector<uint2> small_work, stream_work;
+    std::vector<MainWork> small_work, stream_work;
+    auto work = [](uint32_t l, uint32_t cls, uint32_t tile) {
+        MainWork w{};
+        w.layer = l;
+        w.cls = cls;
+        w.tile = tile;
+        return w;
+    };
     for (int32_t l = 0; l < L; ++l) {
         LayerInfo &li = lo->linfo[l];
         li = LayerInfo{};
@@ -123,11 +132,11 @@ int build_plan(lags_layout *lo)
         if (li.n <= kSmallMax) {
             li.cls = kClsSmall;
             li.ntiles = 1;
-            small_work.push_back(make_uint2((uint32_t)l, 0));
+            small_work.push_back(work((uint32_t)l, kClsSmall, 0));
         } else if (li.k == li.n) {
             li.cls = kClsDense;
             li.ntiles = (li.n + kDenseTile - 1) / kDenseTile;
-            for (uint32_t t = 0; t < li.ntiles; ++t) stream_work.push_back(make_uint2((uint32_t)l, t));
+            for (uint32_t t = 0; t < li.ntiles; ++t) stream_work.push_back(work((uint32_t)l, kClsDense, t));
         } else {
             li.cls = kClsSampled;
             li.sid = (uint32_t)lo->sinfo.size();
@@ -162,7 +171,20 @@ int build_plan(lags_layout *lo)
             si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
             si.fin_first = (uint32_t)lo->fin_work.size();
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
-            for (uint32_t t = 0; t < li.ntiles; ++t) stream_work.push_back(make_uint2((uint32_t)l, t));
+            for (uint32_t t = 0; t < li.ntiles; ++t) {
+                MainWork w = work((uint32_t)l, kClsSampled, t);
+                w.sid = li.sid;
+                w.off = li.off;
+                w.end = li.off + li.n;
+                w.a4 = si.a4;
+                w.b4 = si.b4;
+                w.nseg = si.nseg;
+                w.seg_base = si.seg_base;
+                w.cap = si.cap;
+                w.slot_lo = si.slot_lo;
+                w.slot_hi = si.slot_hi;
+                stream_work.push_back(w);
+            }
             for (uint32_t b = 0; b < si.fin_nblocks; ++b)
                 lo->fin_work.push_back(make_uint2(li.sid, b * kFinSegs));
             seg_base += si.nseg;
@@ -228,7 +250,7 @@ int ensure_device(lags_layout *lo)
     if (lo->dev) return dev == lo->device ? LAGS_OK : LAGS_EDEVICE;
     const size_t b_l = align_up(lo->linfo.size() * sizeof(LayerInfo), kAlign);
     const size_t b_s = align_up(std::max<size_t>(1, lo->sinfo.size()) * sizeof(SampledInfo), kAlign);
-    const size_t b_m = align_up(std::max<size_t>(1, lo->main_work.size()) * sizeof(uint2), kAlign);
+    const size_t b_m = align_up(std::max<size_t>(1, lo->main_work.size()) * sizeof(MainWork), kAlign);
     const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(uint2), kAlign);
     const size_t b_o = align_up(lo->moff.size() * 4, kAlign);
     const size_t b_p = align_up(lo->pos_layer.size() * 4, kAlign);
@@ -237,7 +259,7 @@ int ensure_device(lags_layout *lo)
     std::memcpy(host.data(), lo->linfo.data(), lo->linfo.size() * sizeof(LayerInfo));
     if (!lo->sinfo.empty())
         std::memcpy(host.data() + b_l, lo->sinfo.data(), lo->sinfo.size() * sizeof(SampledInfo));
-    std::memcpy(host.data() + b_l + b_s, lo->main_work.data(), lo->main_work.size() * sizeof(uint2));
+    std::memcpy(host.data() + b_l + b_s, lo->main_work.data(), lo->main_work.size() * sizeof(MainWork));
     if (!lo->fin_work.empty())
         std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(uint2));
     std::memcpy(host.data() + b_l + b_s + b_m + b_f, lo->moff.data(), lo->moff.size() * 4);
@@ -253,7 +275,7 @@ int ensure_device(lags_layout *lo)
     lo->device = dev;
     lo->d_linfo = (LayerInfo *)p;
     lo->d_sinfo = (SampledInfo *)(p + b_l);
-    lo->d_main = (uint2 *)(p + b_l + b_s);
+    lo->d_main = (MainWork *)(p + b_l + b_s);
     lo->d_fin = (uint2 *)(p + b_l + b_s + b_m);
     lo->d_moff = (uint32_t *)(p + b_l + b_s + b_m + b_f);
     lo->d_poslayer = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o);

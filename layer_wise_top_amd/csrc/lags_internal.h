@@ -71,6 +71,22 @@ struct SampledInfo {      // one per sampled layer, device table
     uint32_t pad[2];
 };
 
+// One entry per k_main workgroup: everything a streaming tile needs, so one
+// load starts it (small and k == n layers use layer and tile only).
+struct MainWork {
+    uint32_t layer;
+    uint32_t cls;
+    uint32_t tile;        // tile index inside the layer
+    uint32_t sid;         // sampled-layer id
+    uint32_t off, end;    // layer range [off, end)
+    uint32_t a4, b4;      // 4-aligned interior of the layer
+    uint32_t nseg;        // segments of the layer
+    uint32_t seg_base;    // global id of the layer's segment 0
+    uint32_t cap;         // candidate slots per segment
+    uint32_t slot_lo, slot_hi;   // first slot of the layer
+    uint32_t pad[3];
+};
+
 struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t G;           // guess: candidates have key >= G
     uint32_t SH;          // histogram bin width 2^SH above G
@@ -97,7 +113,7 @@ struct SparsifyArgs {
     float *msg_val;
     const LayerInfo *linfo;
     const SampledInfo *sinfo;
-    const uint2 *main_work;   // (layer, tile) per main workgroup
+    const MainWork *main_work;   // one per main workgroup
     const uint2 *fin_work;    // (sid, first segment) per finishing workgroup
     uint32_t *report;
     SampledState *state;

@@ -394,70 +394,100 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
     return min((key - G) >> SH, kNBins - 1u);
 }
 
-// Append the flagged entries of a lane group (up to 4 per lane, index order
-// lane-major, then j) to the segment's slots.  Wave-uniform call.
-__device__ __forceinline__ void append_candidates(uint32_t cmask, const uint32_t *idx, const float *v,
-                                                  uint32_t &run, uint2 *slots, uint32_t cap)
-{
-    uint32_t tot;
-    const uint32_t pre = wave_prefix3((uint32_t)__popc(cmask), tot);
-    uint32_t pos = run + pre;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (cmask & (1u << j)) {
-            if (pos < cap) slots[pos] = make_uint2(idx[j], __float_as_uint(v[j]));
-            ++pos;
+// Candidates of one segment, in index order.  They are staged in the wave's
+// LDS buffer and written to the segment's slots in contiguous bursts: isolated
+// 8-byte stores would each cost a partial-line write in memory.
+constexpr uint32_t kStage = 256;   // per wave; one row holds at most 4 x 64 candidates
+
+struct CandWriter {
+    uint2 *slots;      // the segment's slots
+    uint2 *stage;      // the wave's LDS buffer
+    uint32_t cap;      // slots of the segment
+    uint32_t run;      // candidates so far (may exceed cap)
+    uint32_t flushed;  // candidates written to slots so far
+    uint32_t ln;
+
+    __device__ void flush()
+    {
+        const uint32_t n = run - flushed;   // staged, <= kStage
+        // other lanes' LDS writes before these reads, and these reads before
+        // the next appends overwrite the buffer (one wave: program order)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        for (uint32_t t = ln; t < n; t += 64) {
+            const uint32_t pos = flushed + t;
+            if (pos < cap) slots[pos] = stage[t];
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        flushed = run;
     }
-    run += tot;
-}
+
+    // Append the flagged entries of a lane group (up to 4 per lane, index
+    // order lane-major, then j).  Wave-uniform call.
+    __device__ void append(uint32_t cmask, const uint32_t *idx, const float *v)
+    {
+        uint32_t tot;
+        const uint32_t pre = wave_prefix3((uint32_t)__popc(cmask), tot);
+        if (run - flushed + tot > kStage) flush();
+        uint32_t pos = run - flushed + pre;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (cmask & (1u << j)) {
+                stage[pos] = make_uint2(idx[j], __float_as_uint(v[j]));
+                ++pos;
+            }
+        }
+        run += tot;
+    }
+};
 
 // One wave streams one segment of a sampled layer: acc = grad + residual is
 // written back to the residual buffer, and entries with key >= G are appended
-// in index order to the segment's candidate slots.
-__device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const SampledInfo &S,
-                                uint32_t seg, uint32_t G)
+// in index order to the segment's candidate slots.  Rows of 4 x 64 float4 per
+// iteration.
+__device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
+                                const uint32_t *Gp, uint2 *stage)
 {
-    constexpr int U = 2;
+    constexpr int U = 4;
     const uint32_t ln = lane_id();
-    const uint32_t e0 = S.a4 + seg * kSeg;
-    const uint32_t e1 = min(e0 + kSeg, S.b4);
-    const uint64_t slot0 = (((uint64_t)S.slot_hi << 32) | S.slot_lo) + (uint64_t)seg * S.cap;
-    uint2 *slots = a.slots + slot0;
-    const uint32_t cap = S.cap;
-    uint32_t run = 0;
+    const uint32_t e0 = w.a4 + seg * kSeg;
+    const uint32_t e1 = min(e0 + kSeg, w.b4);
+    const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * w.cap;
+    CandWriter cw{a.slots + slot0, stage, w.cap, 0u, 0u, ln};
+    const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
+    v4f *r4 = reinterpret_cast<v4f *>(a.res);
+    const uint32_t q1 = e1 / 4u;
+    uint32_t q0 = e0 / 4u;
+    // the first rows are requested before the guess arrives
+    v4f gv[U], rv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t q = q0 + u * 64u + ln;
+        if (q < q1) {
+            gv[u] = __builtin_nontemporal_load(g4 + q);
+            rv[u] = __builtin_nontemporal_load(r4 + q);
+        } else {
+            gv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+            rv[u] = gv[u];
+        }
+    }
+    const uint32_t G = *Gp;
     uint32_t idx[4];
     float v[4];
 
-    if (seg == 0 && L.off < S.a4) {          // unaligned head of the layer
-        const uint32_t i = L.off + ln;
+    if (seg == 0 && w.off < w.a4) {          // unaligned head of the layer
+        const uint32_t i = w.off + ln;
         uint32_t cm = 0;
         v[0] = v[1] = v[2] = v[3] = 0.0f;
         idx[0] = idx[1] = idx[2] = idx[3] = i;
-        if (i < S.a4) {
+        if (i < w.a4) {
             v[0] = a.grad[i] + a.res[i];
             a.res[i] = v[0];
             if (key_of(v[0]) >= G) cm = 1;
         }
-        append_candidates(cm, idx, v, run, slots, cap);
+        cw.append(cm, idx, v);
     }
 
-    const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
-    v4f *r4 = reinterpret_cast<v4f *>(a.res);
-    const uint32_t q1 = e1 / 4u;
-    for (uint32_t q0 = e0 / 4u; q0 < q1; q0 += 64u * U) {
-        v4f gv[U], rv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t q = q0 + u * 64u + ln;
-            if (q < q1) {
-                gv[u] = __builtin_nontemporal_load(g4 + q);
-                rv[u] = __builtin_nontemporal_load(r4 + q);
-            } else {
-                gv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-                rv[u] = gv[u];
-            }
-        }
+    while (true) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t q = q0 + u * 64u + ln;
@@ -475,37 +505,57 @@ __device__ void sampled_segment(const SparsifyArgs &a, const LayerInfo &L, const
                     idx[j] = 4u * q + j;
                     v[j] = acc[j];
                 }
-                append_candidates(cm, idx, v, run, slots, cap);
+                cw.append(cm, idx, v);
+            }
+        }
+        q0 += 64u * U;
+        if (q0 >= q1) break;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t q = q0 + u * 64u + ln;
+            if (q < q1) {
+                gv[u] = __builtin_nontemporal_load(g4 + q);
+                rv[u] = __builtin_nontemporal_load(r4 + q);
+            } else {
+                gv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                rv[u] = gv[u];
             }
         }
     }
 
-    const uint32_t end = L.off + L.n;
-    if (seg == S.nseg - 1 && S.b4 < end) {   // unaligned tail of the layer
-        const uint32_t i = S.b4 + ln;
+    if (seg == w.nseg - 1 && w.b4 < w.end) {   // unaligned tail of the layer
+        const uint32_t i = w.b4 + ln;
         uint32_t cm = 0;
         v[0] = v[1] = v[2] = v[3] = 0.0f;
         idx[0] = idx[1] = idx[2] = idx[3] = i;
-        if (i < end) {
+        if (i < w.end) {
             v[0] = a.grad[i] + a.res[i];
             a.res[i] = v[0];
             if (key_of(v[0]) >= G) cm = 1;
         }
-        append_candidates(cm, idx, v, run, slots, cap);
+        cw.append(cm, idx, v);
     }
-    if (ln == 0) a.seg_count[S.seg_base + seg] = run;
+    cw.flush();
+    if (ln == 0) a.seg_count[w.seg_base + seg] = cw.run;
 }
 
 __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 {
     __shared__ uint32_t hist[kNBins];
     __shared__ float acc_s[kSmallMax];
+    __shared__ uint2 stage[kWaves][kStage];
     __shared__ uint32_t tmp[kWaves];
     __shared__ uint32_t res[2];
 
-    const uint2 w = a.main_work[blockIdx.x];
-    const LayerInfo L = a.linfo[w.x];
+    const MainWork w = a.main_work[blockIdx.x];
 
+    if (w.cls == kClsSampled) {   // streaming tile w.tile: one segment per wave
+        const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
+        if (seg < w.nseg) sampled_segment(a, w, seg, &a.state[w.sid].G, stage[threadIdx.x >> 6]);
+        return;
+    }
+
+    const LayerInfo L = a.linfo[w.layer];
     if (L.cls == kClsSmall) {
         for (uint32_t i = threadIdx.x; i < L.n; i += kBlock)
             acc_s[i] = a.grad[L.off + i] + a.res[L.off + i];
@@ -523,23 +573,15 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
         return;
     }
 
-    if (L.cls == kClsDense) {
-        const uint32_t lo = L.off + w.y * kDenseTile;
-        const uint32_t hi = min(lo + kDenseTile, L.off + L.n);
-        for (uint32_t i = lo + threadIdx.x; i < hi; i += kBlock) {
-            const float x = a.grad[i] + a.res[i];
-            a.res[i] = 0.0f;
-            a.msg_idx[L.moff + (i - L.off)] = i;
-            a.msg_val[L.moff + (i - L.off)] = x;
-        }
-        return;
+    // k == n layer: every entry is sent
+    const uint32_t lo = L.off + w.tile * kDenseTile;
+    const uint32_t hi = min(lo + kDenseTile, L.off + L.n);
+    for (uint32_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+        const float x = a.grad[i] + a.res[i];
+        a.res[i] = 0.0f;
+        a.msg_idx[L.moff + (i - L.off)] = i;
+        a.msg_val[L.moff + (i - L.off)] = x;
     }
-
-    // sampled layer, streaming tile w.y: one segment per wave
-    const SampledInfo S = a.sinfo[L.sid];
-    const uint32_t G = a.state[L.sid].G;
-    const uint32_t seg = w.y * kTileSegs + (threadIdx.x >> 6);
-    if (seg < S.nseg) sampled_segment(a, L, S, seg, G);
 }
 
 // ---------------------------------------------------------------------------
