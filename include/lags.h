@@ -167,6 +167,8 @@ typedef struct lags_report {
     int32_t layers_exact;   /* of those, layers that fell back to the exact path */
     uint32_t bad_entries;   /* message entries the last aggregate skipped as invalid */
     uint32_t slow_chunks;   /* aggregate chunks above the fast-path capacity */
+    int32_t layers_wide_bin; /* sampled layers whose threshold bin was resolved from the
+                                workspace rather than LDS (last sparsify) */
 } lags_report;
 
 /* Synchronise `stream` and read the report kept in the workspace.  Only

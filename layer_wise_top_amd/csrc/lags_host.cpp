@@ -46,6 +46,7 @@ struct lags_layout {
     std::vector<uint32_t> pos_layer;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
+    uint64_t tbin_total = 0;
     // workspace plan (byte offsets)
     size_t ws_report = 0, ws_state = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
            ws_fintot = 0, ws_agg = 0;
@@ -113,6 +114,7 @@ int build_plan(lags_layout *lo)
     lo->linfo.resize(L);
     uint32_t seg_base = 0;
     uint64_t slot_base = 0;
+    uint64_t tbin_base = 0;
     std::vector<MainWork> small_work, stream_work;
     auto work = [](uint32_t l, uint32_t cls, uint32_t tile) {
         MainWork w{};
@@ -169,6 +171,9 @@ int build_plan(lags_layout *lo)
             si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
             si.slot_hi = (uint32_t)(slot_base >> 32);
             si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
+            si.tbin_cap = std::max<uint32_t>(kTbinCap, (li.k + 7) / 8);
+            si.tbin_base = (uint32_t)tbin_base;
+            tbin_base += si.tbin_cap;
             si.fin_first = (uint32_t)lo->fin_work.size();
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
             for (uint32_t t = 0; t < li.ntiles; ++t) {
@@ -197,6 +202,7 @@ int build_plan(lags_layout *lo)
     lo->main_work.insert(lo->main_work.end(), stream_work.begin(), stream_work.end());
     lo->nseg_total = seg_base;
     lo->slots_total = slot_base;
+    lo->tbin_total = tbin_base;
     // layer of every kStartsBlock-th message position (the aggregate's start pass)
     const uint64_t npb = (lo->K + 1 + kStartsBlock - 1) / kStartsBlock;
     lo->pos_layer.resize(npb);
@@ -219,7 +225,7 @@ int build_plan(lags_layout *lo)
     lo->ws_slots = at;
     at = align_up(at + (size_t)lo->slots_total * 8, kAlign);
     lo->ws_tbin = at;
-    at = align_up(at + ns * (size_t)kTbinCap * 8, kAlign);
+    at = align_up(at + (size_t)lo->tbin_total * 8, kAlign);
     lo->ws_fintot = at;
     at = align_up(at + lo->fin_work.size() * 4, kAlign);
     lo->ws_agg = at;
@@ -538,15 +544,16 @@ int lags_workspace_report(const lags_layout *lo, const void *ws, size_t ws_bytes
                           lags_report *out)
 {
     if (!lo || !ws || !out) return LAGS_EINVAL;
-    if (ws_bytes < lo->ws_report + 16) return LAGS_EWORKSPACE;
+    if (ws_bytes < lo->ws_report + 20) return LAGS_EWORKSPACE;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LAGS_EHIP;
-    uint32_t h[4];
+    uint32_t h[5];
     if (hipMemcpy(h, (const unsigned char *)ws + lo->ws_report, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
         return LAGS_EHIP;
     out->layers_sampled = (int32_t)h[kRepSampled];
     out->layers_exact = (int32_t)h[kRepExact];
     out->bad_entries = h[kRepBad];
     out->slow_chunks = h[kRepSlow];
+    out->layers_wide_bin = (int32_t)h[kRepWide];
     return LAGS_OK;
 }
 

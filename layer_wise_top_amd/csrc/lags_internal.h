@@ -19,7 +19,7 @@ constexpr uint32_t kDenseTile = 16384;   // entries per workgroup for k == n lay
 constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident)
 constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
 constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
-constexpr uint32_t kTbinCap = 4096;      // entries of the threshold bin kept per layer
+constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LDS (larger: global)
 constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup
 // aggregate
 constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
@@ -68,7 +68,8 @@ struct SampledInfo {      // one per sampled layer, device table
     uint32_t force_exact; // ratio too large for a guess: exact path
     uint32_t fin_nblocks; // finishing workgroups of this layer
     uint32_t fin_first;   // index of the layer's first finishing workgroup
-    uint32_t pad[2];
+    uint32_t tbin_base;   // first threshold-bin entry of the layer in the workspace
+    uint32_t tbin_cap;    // threshold-bin entries kept (max(kTbinCap, k/8))
 };
 
 // One entry per k_main workgroup: everything a streaming tile needs, so one
@@ -104,7 +105,7 @@ struct SampledState {     // per sampled layer, per call, in the workspace
 };
 
 // report counters at the head of the workspace
-enum : uint32_t { kRepSampled = 0, kRepExact = 1, kRepBad = 2, kRepSlow = 3, kRepWords = 64 };
+enum : uint32_t { kRepSampled = 0, kRepExact = 1, kRepBad = 2, kRepSlow = 3, kRepWide = 4, kRepWords = 64 };
 
 struct SparsifyArgs {
     const float *grad;

@@ -307,6 +307,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     __shared__ uint32_t res[2];
 
     if (blockIdx.x == 0 && threadIdx.x < 2) a.report[kRepSampled + threadIdx.x] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 2) a.report[kRepWide] = 0;
     if (blockIdx.x >= a.nsampled) return;
     const SampledInfo S = a.sinfo[blockIdx.x];
     const LayerInfo L = a.linfo[S.layer];
@@ -698,6 +699,33 @@ __global__ __launch_bounds__(kBlock) void k_fin_hist(SparsifyArgs a)
     if (last) finalize_hist(a, L, st, hist, tmp, res);
 }
 
+// Exact threshold and tie cut among the h entries of the threshold bin (the
+// need-th largest key; among keys equal to it, the lowest indices first), and
+// the per-segment and per-workgroup counts of the bin's selected entries.
+template <class KeyF, class IdxF>
+__device__ void resolve_tbin(const SparsifyArgs &a, const SampledInfo &S, uint32_t h, uint32_t need,
+                             const KeyF &key, const IdxF &idx, uint32_t *hist, uint32_t *tmp,
+                             uint32_t *res, uint32_t &T_out, uint32_t &cut_out)
+{
+    uint32_t e;
+    const uint32_t T = block_radix_select(key, [](uint32_t) { return true; }, h, need, hist, tmp, res, &e);
+    // e-th smallest index among keys == T  ==  e-th largest of ~index
+    uint32_t e2;
+    const uint32_t ncut = block_radix_select([&](uint32_t p) { return ~idx(p); },
+                                             [&](uint32_t p) { return key(p) == T; }, h, e, hist, tmp, res, &e2);
+    const uint32_t cut = ~ncut;
+    for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
+        const uint32_t kp = key(p), ip = idx(p);
+        if (kp > T || (kp == T && ip <= cut)) {
+            const uint32_t sg = seg_of(S, ip);
+            atomicAdd(&a.seg_sel[S.seg_base + sg], 1u);
+            atomicAdd(&a.fin_total[S.fin_first + sg / kFinSegs], 1u);
+        }
+    }
+    T_out = T;
+    cut_out = cut;
+}
+
 // k_fin_select: count, per segment, candidates above the threshold bin and
 // gather the threshold bin; the last workgroup of a layer resolves the exact
 // threshold key T and the tie cut, and turns per-workgroup counts into
@@ -739,8 +767,8 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
                     ++D;
                 } else if (bin == bstar) {
                     const uint32_t t = atomicAdd(&st->tbin_n, 1u);
-                    if (t < kTbinCap) {
-                        uint32_t *e = reinterpret_cast<uint32_t *>(a.tbin + (uint64_t)sid * kTbinCap + t);
+                    if (t < S.tbin_cap) {
+                        uint32_t *e = reinterpret_cast<uint32_t *>(a.tbin + (uint64_t)S.tbin_base + t);
                         st_coherent(e, c.x);
                         st_coherent(e + 1, c.y);
                     }
@@ -765,7 +793,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     if (!last) return;
 
     const uint32_t h = ld_coherent(&st->tbin_n);
-    if (status != kStOk || h > kTbinCap) {
+    if (status != kStOk || h > S.tbin_cap) {
         // exact multi-pass path over the accumulated values (the residual
         // buffer holds acc for every entry of the layer after k_main)
         if (threadIdx.x == 0) {
@@ -778,30 +806,25 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
         return;
     }
 
-    // resolve the threshold inside bin bstar
+    // resolve the threshold inside bin bstar: in LDS when the bin fits,
+    // otherwise straight from the workspace
     const uint32_t need = L.k - st->c_above;
-    for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
-        const uint32_t *e = reinterpret_cast<const uint32_t *>(a.tbin + (uint64_t)sid * kTbinCap + p);
-        ti[p] = ld_coherent(e);
-        tk[p] = ld_coherent(e + 1) & 0x7fffffffu;
-    }
-    __syncthreads();
-    uint32_t e;
-    const uint32_t T = block_radix_select([&](uint32_t p) { return tk[p]; }, [](uint32_t) { return true; },
-                                          h, need, hist, tmp, res, &e);
-    // e-th smallest index among keys == T  ==  e-th largest of ~index
-    uint32_t e2;
-    const uint32_t ncut = block_radix_select([&](uint32_t p) { return ~ti[p]; },
-                                             [&](uint32_t p) { return tk[p] == T; }, h, e, hist, tmp, res, &e2);
-    const uint32_t idx_cut = ~ncut;
-    const uint32_t fin_first = S.fin_first;
-    for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
-        if (tk[p] > T || (tk[p] == T && ti[p] <= idx_cut)) {
-            const uint32_t sg = seg_of(S, ti[p]);
-            atomicAdd(&a.seg_sel[S.seg_base + sg], 1u);
-            atomicAdd(&a.fin_total[fin_first + sg / kFinSegs], 1u);
+    const uint32_t *tb = reinterpret_cast<const uint32_t *>(a.tbin + (uint64_t)S.tbin_base);
+    uint32_t T, idx_cut;
+    if (h <= kTbinCap) {
+        for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
+            ti[p] = ld_coherent(tb + 2 * p);
+            tk[p] = ld_coherent(tb + 2 * p + 1) & 0x7fffffffu;
         }
+        __syncthreads();
+        resolve_tbin(a, S, h, need, [&](uint32_t p) { return tk[p]; }, [&](uint32_t p) { return ti[p]; },
+                     hist, tmp, res, T, idx_cut);
+    } else {
+        if (threadIdx.x == 0) atomicAdd(&a.report[kRepWide], 1u);
+        resolve_tbin(a, S, h, need, [&](uint32_t p) { return ld_coherent(tb + 2 * p + 1) & 0x7fffffffu; },
+                     [&](uint32_t p) { return ld_coherent(tb + 2 * p); }, hist, tmp, res, T, idx_cut);
     }
+    const uint32_t fin_first = S.fin_first;
     wait_mem_done();
     __syncthreads();
     // per-workgroup totals -> exclusive message offsets (in place)

@@ -38,7 +38,8 @@ class LagsError(RuntimeError):
 
 class Report(ctypes.Structure):
     _fields_ = [("layers_sampled", ctypes.c_int32), ("layers_exact", ctypes.c_int32),
-                ("bad_entries", ctypes.c_uint32), ("slow_chunks", ctypes.c_uint32)]
+                ("bad_entries", ctypes.c_uint32), ("slow_chunks", ctypes.c_uint32),
+                ("layers_wide_bin", ctypes.c_int32)]
 
 
 _lib = None

@@ -200,3 +200,42 @@ def test_determinism():
         outs.append((mi, bits(mv), bits(to_np_f32(r_d))))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+def _single_layer_case(oracle, n, num, den, values, P=4, steps=1):
+    import torch
+    off = np.array([0, n], np.int64)
+    k = _k(oracle, off, num, den)
+    run = GpuRunner(off, k, P)
+    rng = np.random.default_rng(n % 1000003)
+    r = np.zeros(n, np.float32)
+    w = W.adversarial_values(13, n, "normal")
+    for step in range(steps):
+        g = values(step)
+        oi = np.stack([np.sort(rng.choice(n, int(k[0]), replace=False)) for _ in range(P - 1)]).astype(np.uint32)
+        ov = rng.standard_normal(oi.shape).astype(np.float32)
+        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, tag=f"single n={n}/{step}")
+    return run.report()
+
+
+@pytest.mark.timeout(900)
+def test_single_layer_100m(oracle):
+    """One layer over 100M entries (whole-model selection, as SLGS-SGD does)."""
+    n = 100_000_000
+    rep = _single_layer_case(oracle, n, 1, 1000,
+                             lambda s: np.random.default_rng(7 + s).standard_normal(n, dtype=np.float32))
+    assert rep["layers_exact"] == 0, rep
+
+
+def test_large_threshold_bin(oracle):
+    """An outlier in the sampled region widens the candidate bins, so the
+    threshold bin holds more entries than fit in LDS and is resolved from the
+    workspace (still no exact fallback)."""
+    n = 20_000_003
+
+    def vals(s):
+        v = np.random.default_rng(11 + s).standard_normal(n).astype(np.float32)
+        v[0] = 1000.0
+        return v
+    rep = _single_layer_case(oracle, n, 1, 100, vals, P=3, steps=2)
+    assert rep["layers_exact"] == 0 and rep["layers_wide_bin"] == 1, rep
