@@ -19,8 +19,10 @@ the pages; it is the largest layout and sets the bandwidth-bound regime.
 Seeds.  Every array is drawn per tensor from
 ``Generator(PCG64(SeedSequence([cfg_id, step, worker, stream, layer])))`` with
 stream 0 = gradient, 1 = message indices, 2 = message values, 3 = initial
-weights.  Draws are float64, rounded to fp32 (the LSTM workload then rounds to
-bf16 and widens back to fp32, which creates heavy exact ties).
+weights; tensors above 2^24 entries (single-scale ones) are drawn in chunks of
+2^24 with the chunk index appended to the seed.  Draws are float64, rounded to
+fp32 (the LSTM workload then rounds to bf16 and widens back to fp32, which
+creates heavy exact ties).
 """
 from __future__ import annotations
 
@@ -214,9 +216,16 @@ WORKLOADS = {
         "(embedding 50304x2048 + 24 blocks of d=2048); N(0, 0.02^2); "
         "rho = 1/1000; P = 16; 1 step",
         _tfm1p3b_tensors(), "normal_const", "uniform", (1, 1000), P=16, steps=1),
+    "slgs1p3b": Workload(
+        6, "slgs1p3b",
+        "the 1.3B transformer gradient selected as one layer (whole-model top-k, "
+        "the single-layer SLGS-SGD comparison point of the LAGS review): "
+        "1,311,178,752 fp32 in 1 tensor; N(0, 0.02^2); rho = 1/1000; P = 16; 1 step",
+        (_T("all", 1_311_178_752, 2048),), "normal_const", "uniform", (1, 1000), P=16, steps=1),
 }
 
 ORDER = ("resnet20", "vgg16", "resnet50", "lstm", "tfm1p3b")
+EXTRA = ("slgs1p3b",)
 
 
 def get(name: str) -> Workload:
@@ -297,9 +306,25 @@ def _fill(n: int, jobs):
     return out
 
 
+CHUNK = 1 << 24   # tensors above this size are drawn in chunks with their own seeds
+
+
 def gen_grad_layer(wl: Workload, step: int, worker: int, layer: int) -> np.ndarray:
     t = wl.tensors[layer]
-    return draw_values(wl, t, rng_for(wl.cfg_id, step, worker, STREAM_GRAD, layer))
+    if t.n <= CHUNK or len(t.pieces) > 1:
+        return draw_values(wl, t, rng_for(wl.cfg_id, step, worker, STREAM_GRAD, layer))
+    out = np.empty(t.n, dtype=np.float32)
+
+    def run(c):
+        lo = c * CHUNK
+        cnt = min(CHUNK, t.n - lo)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+            [wl.cfg_id, step, worker, STREAM_GRAD, layer, c])))
+        out[lo:lo + cnt] = draw_values(wl, t, rng, count=cnt)
+    nch = (t.n + CHUNK - 1) // CHUNK
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(run, range(nch)))
+    return out
 
 
 def gen_grad(wl: Workload, step: int, worker: int = 0) -> np.ndarray:
@@ -312,6 +337,18 @@ def gen_grad(wl: Workload, step: int, worker: int = 0) -> np.ndarray:
 
 def gen_weights_layer(wl: Workload, layer: int) -> np.ndarray:
     t = wl.tensors[layer]
+    if wl.dist == "normal_const" and t.n > CHUNK:
+        out = np.empty(t.n, dtype=np.float32)
+
+        def run(c):
+            lo = c * CHUNK
+            cnt = min(CHUNK, t.n - lo)
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+                [wl.cfg_id, 0, 0, STREAM_W0, layer, c])))
+            out[lo:lo + cnt] = (rng.standard_normal(cnt) * wl.const_std).astype(np.float32)
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(run, range((t.n + CHUNK - 1) // CHUNK)))
+        return out
     rng = rng_for(wl.cfg_id, 0, 0, STREAM_W0, layer)
     if wl.dist == "normal_const":
         return (rng.standard_normal(t.n) * wl.const_std).astype(np.float32)
