@@ -239,3 +239,42 @@ def test_large_threshold_bin(oracle):
         return v
     rep = _single_layer_case(oracle, n, 1, 100, vals, P=3, steps=2)
     assert rep["layers_exact"] == 0 and rep["layers_wide_bin"] == 1, rep
+
+
+def test_aggregate_rejects_invalid_messages(oracle):
+    """Message entries that break the layout (an index outside its layer, an
+    index beyond n, a descending pair, a duplicate) are skipped and counted;
+    layers whose entries are all valid are updated exactly as the oracle does."""
+    import torch
+    sizes = [50000, 70001, 30000, 90000]
+    off = np.zeros(len(sizes) + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    n = int(off[-1])
+    k = _k(oracle, off, 1, 100)
+    moff = np.concatenate([[0], np.cumsum(k)])
+    P = 4
+    rng = np.random.default_rng(21)
+    idx = np.empty((P, int(k.sum())), np.uint32)
+    for p in range(P):
+        for l in range(len(sizes)):
+            idx[p, moff[l]:moff[l + 1]] = np.sort(rng.choice(sizes[l], int(k[l]), replace=False)) + off[l]
+    val = rng.standard_normal(idx.shape).astype(np.float32)
+    bad = idx.copy()
+    bad[1, moff[1] + 5] = off[3] + 7            # layer 1 entry pointing into layer 3
+    bad[2, moff[1] + 9] = 0xFFFFFFFF            # beyond n
+    bad[3, moff[1] + 20], bad[3, moff[1] + 21] = bad[3, moff[1] + 21], bad[3, moff[1] + 20]  # descending
+    bad[1, moff[1] + 30] = bad[1, moff[1] + 29]  # duplicate
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(bad))
+    run.msg_val.copy_(to_dev(val))
+    w = W.adversarial_values(31, n, "normal")
+    w_d = to_dev(w)
+    run.aggregate(w_d, 0.1)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["bad_entries"] >= 2, rep
+    w_g = to_np_f32(w_d)
+    for l in (0, 2):                             # layers whose entries are all valid
+        a, b = int(off[l]), int(off[l + 1])
+        w_o = oracle.aggregate(idx, val, w[a:b], 0.1, lo=a, hi=b)
+        assert_bits_equal(f"layer {l} weights", w_g[a:b], w_o)
