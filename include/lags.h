@@ -35,7 +35,8 @@
  *   - arguments are validated on the host before anything is launched; on a
  *     negative status nothing has been launched and nothing written;
  *   - device faults surface at the caller's next synchronisation (HIP rules);
- *   - one workspace must not be used by two calls that may overlap in time.
+ *   - one workspace must not be used by two calls that may overlap in time,
+ *     except range calls on disjoint layer ranges (see lags_sparsify_range).
  */
 #ifndef LAGS_H
 #define LAGS_H
@@ -160,6 +161,37 @@ int lags_aggregate_apply(const lags_layout *layout, float *weights,
                          const uint32_t *msg_idx, const float *msg_val,
                          int32_t P, float lr, void *ws, size_t ws_bytes,
                          void *stream);
+
+/*
+ * Layer-range forms of the two calls above, for layer-wise pipelining: a
+ * layer's messages can be produced and exchanged as soon as back-propagation
+ * has finished that layer (LAGS review, proposed method, bullet 3: the
+ * layer-wise selection is what lets communication overlap with the backward
+ * pass), and the MG-WFBP review's merged buckets are contiguous layer ranges.
+ *   l0, l1: the layers [l0, l1) of the layout, 0 <= l0 <= l1 <= L;
+ *           l0 == l1 validates the arguments and launches nothing.
+ * Every other argument is the same full-model buffer as in the full call (the
+ * layout's global indices and message offsets are used unchanged); the call
+ * reads and writes only the entries [off[l0], off[l1]) of grad / residual /
+ * weights and the message positions [msg_offset(l0), msg_offset(l1)) of
+ * msg_idx / msg_val (of every worker row for the aggregate).  Splitting
+ * [0, L) into ranges, called in any order, gives results bit-identical to
+ * the full call, since every layer's selection and every index's update
+ * depend on that layer alone.
+ * The workspace parts a range uses belong to its layers, so calls on
+ * disjoint ranges may share one workspace, also on different streams; the
+ * report counters are then shared and restarted by every call, so
+ * lags_workspace_report is only meaningful after calls that do not overlap.
+ * Returns as the full calls, plus LAGS_ERANGE for a bad range.
+ */
+int lags_sparsify_range(const lags_layout *layout, int32_t l0, int32_t l1,
+                        const float *grad, float *residual, uint32_t *msg_idx,
+                        float *msg_val, void *ws, size_t ws_bytes, uint32_t flags,
+                        void *stream);
+int lags_aggregate_range(const lags_layout *layout, int32_t l0, int32_t l1,
+                         float *weights, const uint32_t *msg_idx,
+                         const float *msg_val, int32_t P, float lr, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* What the last calls that used a workspace did. */
 typedef struct lags_report {

@@ -22,6 +22,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct AggTables {
     uint32_t NC = 0;
+    std::vector<uint32_t> h_cbase;    // [L+1], host copy
     void *dev = nullptr;
     uint32_t *cbase = nullptr;   // [L+1]
     uint32_t *csh = nullptr;     // [L]
@@ -44,6 +45,11 @@ struct lags_layout {
     std::vector<MainWork> main_work;
     std::vector<uint2> fin_work;
     std::vector<uint32_t> pos_layer;
+    // per-layer prefix counts of the work lists, for layer-range launches:
+    // small-layer work entries, streaming work entries, sampled layers and
+    // finishing workgroups before layer l
+    std::vector<uint32_t> small_pre, stream_pre, sid_pre, fin_pre;
+    uint32_t nsmall = 0;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
     uint64_t tbin_total = 0;
@@ -116,6 +122,10 @@ int build_plan(lags_layout *lo)
     uint64_t slot_base = 0;
     uint64_t tbin_base = 0;
     std::vector<MainWork> small_work, stream_work;
+    lo->small_pre.assign(L + 1, 0);
+    lo->stream_pre.assign(L + 1, 0);
+    lo->sid_pre.assign(L + 1, 0);
+    lo->fin_pre.assign(L + 1, 0);
     auto work = [](uint32_t l, uint32_t cls, uint32_t tile) {
         MainWork w{};
         w.layer = l;
@@ -124,6 +134,10 @@ int build_plan(lags_layout *lo)
         return w;
     };
     for (int32_t l = 0; l < L; ++l) {
+        lo->small_pre[l] = (uint32_t)small_work.size();
+        lo->stream_pre[l] = (uint32_t)stream_work.size();
+        lo->sid_pre[l] = (uint32_t)lo->sinfo.size();
+        lo->fin_pre[l] = (uint32_t)lo->fin_work.size();
         LayerInfo &li = lo->linfo[l];
         li = LayerInfo{};
         li.off = lo->off[l];
@@ -197,6 +211,11 @@ int build_plan(lags_layout *lo)
             lo->sinfo.push_back(si);
         }
     }
+    lo->small_pre[L] = (uint32_t)small_work.size();
+    lo->stream_pre[L] = (uint32_t)stream_work.size();
+    lo->sid_pre[L] = (uint32_t)lo->sinfo.size();
+    lo->fin_pre[L] = (uint32_t)lo->fin_work.size();
+    lo->nsmall = (uint32_t)small_work.size();
     // small layers first: they start while the streaming tiles fill the chip
     lo->main_work = small_work;
     lo->main_work.insert(lo->main_work.end(), stream_work.begin(), stream_work.end());
@@ -315,6 +334,7 @@ int ensure_agg(lags_layout *lo, int32_t P, AggTables **out)
     }
     AggTables t;
     t.NC = NC;
+    t.h_cbase = cb;
     t.dev = d;
     t.cbase = (uint32_t *)d;
     t.csh = (uint32_t *)((unsigned char *)d + b0);
@@ -436,12 +456,13 @@ size_t lags_workspace_bytes(const lags_layout *lo, int32_t P)
     return lo->ws_agg + agg_bytes(lo, P);
 }
 
-int lags_sparsify_layers(const lags_layout *clo, const float *grad, float *residual,
-                         uint32_t *msg_idx, float *msg_val, void *ws, size_t ws_bytes,
-                         uint32_t flags, void *stream)
+int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const float *grad,
+                        float *residual, uint32_t *msg_idx, float *msg_val, void *ws,
+                        size_t ws_bytes, uint32_t flags, void *stream)
 {
     lags_layout *lo = const_cast<lags_layout *>(clo);
     if (!lo || !grad || !residual || !msg_idx || !msg_val) return LAGS_EINVAL;
+    if (l0 < 0 || l1 > lo->L || l0 > l1) return LAGS_ERANGE;
     if (flags & ~LAGS_SPARSIFY_EXACT) return LAGS_EINVAL;
     if (!aligned16(grad) || !aligned16(residual) || !aligned16(msg_idx) || !aligned16(msg_val))
         return LAGS_EINVAL;
@@ -452,6 +473,7 @@ int lags_sparsify_layers(const lags_layout *clo, const float *grad, float *resid
     for (int i = 0; i < 5; ++i)
         for (int j = i + 1; j < 5; ++j)
             if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
+    if (l0 == l1) return LAGS_OK;
 
     std::lock_guard<std::mutex> g(lo->mu);
     int rc = ensure_device(lo);
@@ -474,30 +496,47 @@ int lags_sparsify_layers(const lags_layout *clo, const float *grad, float *resid
     a.slots = (uint2 *)(w + lo->ws_slots);
     a.tbin = (uint2 *)(w + lo->ws_tbin);
     a.fin_total = (uint32_t *)(w + lo->ws_fintot);
-    a.nsampled = (uint32_t)lo->sinfo.size();
     a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
+    a.sample_base = lo->sid_pre[l0];
+    a.nsampled = lo->sid_pre[l1] - lo->sid_pre[l0];
+    a.main_base_a = lo->small_pre[l0];
+    a.main_cnt_a = lo->small_pre[l1] - lo->small_pre[l0];
+    a.main_base_b = lo->nsmall + lo->stream_pre[l0];
+    a.fin_base = lo->fin_pre[l0];
     const uint32_t ns = a.nsampled;
+    const uint32_t nmain = a.main_cnt_a + (lo->stream_pre[l1] - lo->stream_pre[l0]);
+    const uint32_t nfin = lo->fin_pre[l1] - lo->fin_pre[l0];
     rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
     if (rc != LAGS_OK) return rc;
-    rc = traced(lo, kKMain, s, [&] { return launch_main(a, (uint32_t)lo->main_work.size(), s); });
+    rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
     if (rc != LAGS_OK) return rc;
     if (ns) {
-        rc = traced(lo, kKFinHist, s, [&] { return launch_fin_hist(a, (uint32_t)lo->fin_work.size(), s); });
+        rc = traced(lo, kKFinHist, s, [&] { return launch_fin_hist(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
-        rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, (uint32_t)lo->fin_work.size(), s); });
+        rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
-        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, (uint32_t)lo->fin_work.size(), s); });
+        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
     }
     return LAGS_OK;
 }
 
-int lags_aggregate_apply(const lags_layout *clo, float *weights, const uint32_t *msg_idx,
-                         const float *msg_val, int32_t P, float lr, void *ws, size_t ws_bytes,
-                         void *stream)
+int lags_sparsify_layers(const lags_layout *lo, const float *grad, float *residual,
+                         uint32_t *msg_idx, float *msg_val, void *ws, size_t ws_bytes,
+                         uint32_t flags, void *stream)
+{
+    if (!lo) return LAGS_EINVAL;
+    return lags_sparsify_range(lo, 0, lo->L, grad, residual, msg_idx, msg_val, ws, ws_bytes, flags,
+                               stream);
+}
+
+int lags_aggregate_range(const lags_layout *clo, int32_t l0, int32_t l1, float *weights,
+                         const uint32_t *msg_idx, const float *msg_val, int32_t P, float lr,
+                         void *ws, size_t ws_bytes, void *stream)
 {
     lags_layout *lo = const_cast<lags_layout *>(clo);
     if (!lo || !weights || !msg_idx || !msg_val) return LAGS_EINVAL;
+    if (l0 < 0 || l1 > lo->L || l0 > l1) return LAGS_ERANGE;
     if (P < 1 || P > LAGS_MAX_WORKERS) return LAGS_ERANGE;
     if ((uint64_t)P * lo->K >= (1ull << 40)) return LAGS_ERANGE;
     if (!aligned16(weights) || !aligned16(msg_idx) || !aligned16(msg_val)) return LAGS_EINVAL;
@@ -509,6 +548,7 @@ int lags_aggregate_apply(const lags_layout *clo, float *weights, const uint32_t 
     for (int i = 0; i < 4; ++i)
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
+    if (l0 == l1) return LAGS_OK;
 
     std::lock_guard<std::mutex> g(lo->mu);
     int rc = ensure_device(lo);
@@ -535,9 +575,23 @@ int lags_aggregate_apply(const lags_layout *clo, float *weights, const uint32_t 
     a.K = (uint32_t)lo->K;
     a.NC = t->NC;
     a.s = lr / (float)P;
+    a.j_lo = lo->moff[l0];
+    a.j_hi = lo->moff[l1];
+    a.c_lo = t->h_cbase[l0];
+    a.c_hi = t->h_cbase[l1];
+    a.npb = (uint32_t)lo->pos_layer.size();
     rc = traced(lo, kKAggStarts, s, [&] { return launch_agg_starts(a, s); });
     if (rc != LAGS_OK) return rc;
-    return traced(lo, kKAgg, s, [&] { return launch_agg(a, s); });
+    return traced(lo, kKAgg, s, [&] { return launch_agg(a, a.c_hi - a.c_lo, s); });
+}
+
+int lags_aggregate_apply(const lags_layout *lo, float *weights, const uint32_t *msg_idx,
+                         const float *msg_val, int32_t P, float lr, void *ws, size_t ws_bytes,
+                         void *stream)
+{
+    if (!lo) return LAGS_EINVAL;
+    return lags_aggregate_range(lo, 0, lo->L, weights, msg_idx, msg_val, P, lr, ws, ws_bytes,
+                                stream);
 }
 
 int lags_workspace_report(const lags_layout *lo, const void *ws, size_t ws_bytes, void *stream,

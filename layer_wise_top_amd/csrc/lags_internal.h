@@ -123,8 +123,14 @@ struct SparsifyArgs {
     uint2 *slots;
     uint2 *tbin;
     uint32_t *fin_total;      // per finishing workgroup: count, then message offset
-    uint32_t nsampled;
+    uint32_t nsampled;        // sampled layers in the launched range
     uint32_t force_exact;
+    // the launched layer range, as offsets into the layout's work lists
+    uint32_t sample_base;     // first sampled-layer id
+    uint32_t main_base_a;     // small-layer work entries: [base_a, base_a + cnt_a)
+    uint32_t main_cnt_a;
+    uint32_t main_base_b;     // streaming work entries follow the small ones in the grid
+    uint32_t fin_base;        // first finishing workgroup
 };
 
 struct AggArgs {
@@ -144,6 +150,10 @@ struct AggArgs {
     uint32_t K;
     uint32_t NC;
     float s;                    // lr / P, rounded to fp32 on the host
+    // the launched layer range: message positions [j_lo, j_hi], chunks [c_lo, c_hi)
+    uint32_t j_lo, j_hi;
+    uint32_t c_lo, c_hi;
+    uint32_t npb;               // entries of pos_layer
 };
 
 // kernel ids for tracing
@@ -159,6 +169,6 @@ hipError_t launch_fin_hist(const SparsifyArgs &a, uint32_t nblocks, hipStream_t 
 hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
-hipError_t launch_agg(const AggArgs &a, hipStream_t s);
+hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s);
 
 }  // namespace lags

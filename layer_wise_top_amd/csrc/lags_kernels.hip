@@ -309,9 +309,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     if (blockIdx.x == 0 && threadIdx.x < 2) a.report[kRepSampled + threadIdx.x] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 2) a.report[kRepWide] = 0;
     if (blockIdx.x >= a.nsampled) return;
-    const SampledInfo S = a.sinfo[blockIdx.x];
+    const uint32_t sid = a.sample_base + blockIdx.x;
+    const SampledInfo S = a.sinfo[sid];
     const LayerInfo L = a.linfo[S.layer];
-    SampledState *st = a.state + blockIdx.x;
+    SampledState *st = a.state + sid;
     uint32_t *stw = reinterpret_cast<uint32_t *>(st);
     for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += NT) stw[t] = 0;
     for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
@@ -443,12 +444,12 @@ struct CandWriter {
 
 // One wave streams one segment of a sampled layer: acc = grad + residual is
 // written back to the residual buffer, and entries with key >= G are appended
-// in index order to the segment's candidate slots.  Rows of 4 x 64 float4 per
-// iteration.
+// in index order to the segment's candidate slots.  Rows of 2 x 64 float4 per
+// iteration (measured fastest on gfx950 for this loop).
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
                                 const uint32_t *Gp, uint2 *stage)
 {
-    constexpr int U = 4;
+    constexpr int U = 2;
     const uint32_t ln = lane_id();
     const uint32_t e0 = w.a4 + seg * kSeg;
     const uint32_t e1 = min(e0 + kSeg, w.b4);
@@ -548,7 +549,9 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
     __shared__ uint32_t tmp[kWaves];
     __shared__ uint32_t res[2];
 
-    const MainWork w = a.main_work[blockIdx.x];
+    const uint32_t wi = (blockIdx.x < a.main_cnt_a) ? a.main_base_a + blockIdx.x
+                                                    : a.main_base_b + (blockIdx.x - a.main_cnt_a);
+    const MainWork w = a.main_work[wi];
 
     if (w.cls == kClsSampled) {   // streaming tile w.tile: one segment per wave
         const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
@@ -670,7 +673,8 @@ __global__ __launch_bounds__(kBlock) void k_fin_hist(SparsifyArgs a)
     __shared__ uint32_t res[2];
     __shared__ uint32_t last;
 
-    const uint2 w = a.fin_work[blockIdx.x];
+    const uint32_t fb = a.fin_base + blockIdx.x;
+    const uint2 w = a.fin_work[fb];
     const uint32_t sid = w.x;
     const SampledInfo S = a.sinfo[sid];
     const LayerInfo L = a.linfo[S.layer];
@@ -740,7 +744,8 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     __shared__ uint32_t res[2];
     __shared__ uint32_t last;
 
-    const uint2 w = a.fin_work[blockIdx.x];
+    const uint32_t fb = a.fin_base + blockIdx.x;
+    const uint2 w = a.fin_work[fb];
     const uint32_t sid = w.x;
     const SampledInfo S = a.sinfo[sid];
     const LayerInfo L = a.linfo[S.layer];
@@ -783,7 +788,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
         if (threadIdx.x == 0) {
             uint32_t t = 0;
             for (int i = 0; i < kWaves; ++i) t += wtot[i];
-            st_coherent(&a.fin_total[blockIdx.x], t);
+            st_coherent(&a.fin_total[fb], t);
         }
     }
     wait_mem_done();
@@ -848,7 +853,8 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
 __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 {
     __shared__ uint32_t sbase[kFinSegs];
-    const uint2 w = a.fin_work[blockIdx.x];
+    const uint32_t fb = a.fin_base + blockIdx.x;
+    const uint2 w = a.fin_work[fb];
     const uint32_t sid = w.x;
     const SampledState *st = a.state + sid;
     if (st->status != kStOk) return;
@@ -859,7 +865,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
     const uint32_t ln = lane_id();
     const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
     if (threadIdx.x == 0) {
-        uint32_t run = L.moff + a.fin_total[blockIdx.x];
+        uint32_t run = L.moff + a.fin_total[fb];
         for (uint32_t s = w.y; s < s_end; ++s) {
             sbase[s - w.y] = run;
             run += a.seg_sel[S.seg_base + s];
@@ -902,8 +908,12 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 // ---------------------------------------------------------------------------
 // aggregate
 
-// k_agg_starts: for every worker p and message position j in [0, K], the
-// chunk of entry j; chunk starts are written where the chunk id changes.  A
+// k_agg_starts: for every worker p and message position j in [j_lo, j_hi]
+// (the message range of the launched layers), the chunk of entry j; chunk
+// starts are written where the chunk id changes.  The range ends count as the
+// first and the one-past-last chunk of the range, so a call reads only its own
+// message entries and writes only the starts of chunks [c_lo, c_hi]; the
+// shared boundary start c_hi gets the same value from either neighbour.  A
 // workgroup covers kStartsBlock positions of one worker; the layers they span
 // (at most kStartsBlock + 2, since every layer sends at least one entry) are
 // staged in LDS.
@@ -915,19 +925,20 @@ __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
     __shared__ uint32_t lrange[2];
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) a.report[kRepBad + threadIdx.x] = 0;
     const uint32_t p = blockIdx.y;
-    const uint32_t j0 = blockIdx.x * kStartsBlock;
+    const uint32_t bb = a.j_lo / kStartsBlock + blockIdx.x;   // absolute position block
+    const uint32_t j0 = bb * kStartsBlock;
     const uint32_t *row = a.msg_idx + (uint64_t)p * a.K;
     // message entries first: they do not depend on the layer lookup
     uint32_t x[PPT], xp[PPT];
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const uint32_t j = j0 + threadIdx.x + q * kBlock;
-        x[q] = (j < a.K) ? row[j] : 0u;
-        xp[q] = (j > 0 && j <= a.K) ? row[j - 1] : 0u;
+        x[q] = (j >= a.j_lo && j < a.j_hi) ? row[j] : 0u;
+        xp[q] = (j > a.j_lo && j <= a.j_hi) ? row[j - 1] : 0u;
     }
     if (threadIdx.x == 0) {
-        const uint32_t l0 = a.pos_layer[blockIdx.x];
-        const uint32_t l1 = (blockIdx.x + 1 < gridDim.x) ? a.pos_layer[blockIdx.x + 1] : a.L - 1;
+        const uint32_t l0 = a.pos_layer[bb];
+        const uint32_t l1 = (bb + 1 < a.npb) ? a.pos_layer[bb + 1] : a.L - 1;
         lrange[0] = l0 > 0 ? l0 - 1 : 0;   // the layer of position j0 - 1 may precede l0
         lrange[1] = l1;
     }
@@ -960,9 +971,9 @@ __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const uint32_t j = j0 + threadIdx.x + q * kBlock;
-        if (j > a.K) continue;
-        const uint32_t c = (j == a.K) ? a.NC : chunk_of(x[q], layer_of(j));
-        const uint32_t cp = (j == 0) ? 0xffffffffu : chunk_of(xp[q], layer_of(j - 1));
+        if (j < a.j_lo || j > a.j_hi) continue;
+        const uint32_t c = (j == a.j_hi) ? a.c_hi : chunk_of(x[q], layer_of(j));
+        const uint32_t cp = (j == a.j_lo) ? a.c_lo - 1u : chunk_of(xp[q], layer_of(j - 1));
         for (uint32_t cc = cp + 1u; cc <= c && cc <= a.NC; ++cc) srow[cc] = j;
     }
 }
@@ -978,7 +989,7 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     uint32_t *pre = ws0 + a.P;
     __shared__ uint32_t tmp[kWaves];
 
-    const uint32_t c = blockIdx.x;
+    const uint32_t c = a.c_lo + blockIdx.x;
     const uint32_t l = a.chunk_layer[c];
     const LayerInfo L = a.linfo[l];
     const uint32_t sh = a.csh[l];
@@ -1153,15 +1164,15 @@ hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t 
 
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
 {
-    const uint32_t nx = (a.K + 1u + kStartsBlock - 1u) / kStartsBlock;
+    const uint32_t nx = a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u;
     hipLaunchKernelGGL(k_agg_starts, dim3(nx, a.P), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_agg(const AggArgs &a, hipStream_t s)
+hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s)
 {
     const size_t lds = (2u * kAggTable + 2u * a.P + 1u) * sizeof(uint32_t);
-    hipLaunchKernelGGL(k_agg, dim3(a.NC), dim3(kBlock), lds, s, a);
+    hipLaunchKernelGGL(k_agg, dim3(nchunks), dim3(kBlock), lds, s, a);
     return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ EXPORTED = (
     "lags_layout_num_elems", "lags_layout_total_k", "lags_layout_num_layers",
     "lags_layout_msg_offset", "lags_workspace_bytes", "lags_sparsify_layers",
     "lags_aggregate_apply", "lags_workspace_report", "lags_trace_enable",
-    "lags_trace_read", "lags_num_kernels", "lags_kernel_name",
+    "lags_trace_read", "lags_num_kernels", "lags_kernel_name", "lags_sparsify_range",
+    "lags_aggregate_range",
 )
 
 
@@ -76,6 +77,10 @@ def lib():
     L.lags_sparsify_layers.argtypes = [vp, vp, vp, vp, vp, vp, sz, u32, vp]
     L.lags_aggregate_apply.restype = ctypes.c_int
     L.lags_aggregate_apply.argtypes = [vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
+    L.lags_sparsify_range.restype = ctypes.c_int
+    L.lags_sparsify_range.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, sz, u32, vp]
+    L.lags_aggregate_range.restype = ctypes.c_int
+    L.lags_aggregate_range.argtypes = [vp, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
     L.lags_workspace_report.restype = ctypes.c_int
     L.lags_workspace_report.argtypes = [vp, vp, sz, vp, ctypes.POINTER(Report)]
     L.lags_trace_enable.restype = ctypes.c_int
@@ -206,6 +211,33 @@ def lags_aggregate_apply(layout: Layout, weights, msg_idx, msg_val, P: int, lr: 
     rc = lib().lags_aggregate_apply(layout.handle, wt, mi, mv, int(P), float(lr), w, ws.numel(),
                                     _stream_handle(stream))
     _check("lags_aggregate_apply", rc)
+
+
+def lags_sparsify_range(layout: Layout, l0: int, l1: int, grad, residual, msg_idx, msg_val, ws,
+                        flags: int = 0, stream=None):
+    """Layers [l0, l1) only; the buffers are the full-model ones."""
+    import torch
+    g = _dev_tensor(grad, torch.float32, layout.n, "grad")
+    r = _dev_tensor(residual, torch.float32, layout.n, "residual")
+    mi = _dev_tensor(msg_idx, torch.int32, layout.K, "msg_idx")
+    mv = _dev_tensor(msg_val, torch.float32, layout.K, "msg_val")
+    w = _dev_tensor(ws, torch.uint8, 1, "ws")
+    rc = lib().lags_sparsify_range(layout.handle, int(l0), int(l1), g, r, mi, mv, w, ws.numel(),
+                                   int(flags), _stream_handle(stream))
+    _check("lags_sparsify_range", rc)
+
+
+def lags_aggregate_range(layout: Layout, l0: int, l1: int, weights, msg_idx, msg_val, P: int,
+                         lr: float, ws, stream=None):
+    """Layers [l0, l1) only; the buffers are the full-model ones."""
+    import torch
+    wt = _dev_tensor(weights, torch.float32, layout.n, "weights")
+    mi = _dev_tensor(msg_idx, torch.int32, int(P) * layout.K, "msg_idx")
+    mv = _dev_tensor(msg_val, torch.float32, int(P) * layout.K, "msg_val")
+    w = _dev_tensor(ws, torch.uint8, 1, "ws")
+    rc = lib().lags_aggregate_range(layout.handle, int(l0), int(l1), wt, mi, mv, int(P), float(lr),
+                                    w, ws.numel(), _stream_handle(stream))
+    _check("lags_aggregate_range", rc)
 
 
 def lags_workspace_report(layout: Layout, ws, stream=None) -> dict:

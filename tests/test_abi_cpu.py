@@ -128,5 +128,14 @@ def test_calls_reject_bad_arguments_without_a_device():
     assert ag(h, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP - 1, None) == -3   # one byte short
     assert ag(h, g + 8, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == -1
     assert ag(h, g, mi, mi + 16, 4, ctypes.c_float(0.1), ws, wsP, None) == -1  # idx/val overlap
+    # layer ranges: bad ranges are rejected, an empty range launches nothing
+    spr, agr = L.lags_sparsify_range, L.lags_aggregate_range
+    for l0, l1 in ((-1, 1), (0, 3), (2, 1)):
+        assert spr(h, l0, l1, g, r, mi, mv, ws, ws_need, 0, None) == -2
+        assert agr(h, l0, l1, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == -2
+    assert spr(h, 1, 1, g, r, mi, mv, ws, ws_need, 0, None) == 0
+    assert agr(h, 2, 2, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == 0
+    assert spr(h, 0, 1, g, r, mi, mv, ws, 16, 0, None) == -3
+    assert agr(h, 0, 1, g, mi, mi + 16, 4, ctypes.c_float(0.1), ws, wsP, None) == -1
     assert L.lags_trace_enable(None, 1) == -1
     lay.close()
