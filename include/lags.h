@@ -193,6 +193,49 @@ int lags_aggregate_range(const lags_layout *layout, int32_t l0, int32_t l1,
                          const float *msg_val, int32_t P, float lr, void *ws,
                          size_t ws_bytes, void *stream);
 
+/*
+ * Merged-gradient message schedule (MG-WFBP review, proposed method,
+ * bullets 1-3 and 5: merge the messages of consecutive layers so that fewer
+ * of them pay the start-up cost; the schedule that minimises the iteration
+ * time is computed once, before training, by an O(L^2) dynamic programme).
+ * Host only: no HIP call, no device memory.
+ * Cost model (the pages give none; this is the plain reading):
+ *   - back-propagation produces layers L-1 .. 0; layer l takes
+ *     backward_time[l], so it is ready at backward_time[L-1] + ... +
+ *     backward_time[l] (summed in that order, in double);
+ *   - a message of B bytes holds the one link for alpha + beta * B;
+ *   - a run of consecutive layers is one message, sent when its lowest layer
+ *     is ready and the previous message has finished;
+ *   - the objective is the finish time of the last message.
+ *   backward_time: host double[L], finite, >= 0 (any time unit);
+ *   msg_bytes:     host int64[L], >= 0, sum <= 2^53 (for LAGS messages,
+ *                  8 * k[l] per worker);
+ *   alpha, beta:   finite, >= 0 (time per message, time per byte);
+ *   bounds:        out, host int32[L+1]: run j (in sending order) is the
+ *                  layer range [bounds[j+1], bounds[j]); bounds[0] = L,
+ *                  bounds[nruns] = 0.  Each run maps to one
+ *                  lags_sparsify_range / lags_aggregate_range call;
+ *   nruns, finish: out, the run count and the finish time of the schedule.
+ * The finish time is the minimum over all 2^(L-1) schedules, exactly (the
+ * same rounded operations as evaluating the returned schedule); among equally
+ * fast schedules the one with the shortest last runs is returned.  O(L^2)
+ * time, O(L) memory.
+ * Returns LAGS_OK, LAGS_EINVAL (null pointer, negative or non-finite input),
+ * LAGS_ERANGE (L outside [1, LAGS_MAX_LAYERS], byte total above 2^53),
+ * LAGS_ENOMEM.
+ */
+int lags_merge_schedule(int32_t L, const double *backward_time,
+                        const int64_t *msg_bytes, double alpha, double beta,
+                        int32_t *bounds, int32_t *nruns, double *finish);
+
+/* Finish time of a given schedule under the same model (for comparing with
+ * one message per layer, bounds = {L, L-1, ..., 0}, or one message for the
+ * whole model, bounds = {L, 0}).  bounds must strictly decrease from L to 0.
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_ERANGE, LAGS_ENOMEM. */
+int lags_schedule_finish(int32_t L, const double *backward_time,
+                         const int64_t *msg_bytes, double alpha, double beta,
+                         const int32_t *bounds, int32_t nruns, double *finish);
+
 /* What the last calls that used a workspace did. */
 typedef struct lags_report {
     int32_t layers_sampled; /* layers on the sampled-threshold path in the last sparsify */

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "liblags.so")
-SOURCES = [os.path.join(CSRC, "lags_host.cpp"), os.path.join(CSRC, "lags_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "lags_host.cpp"), os.path.join(CSRC, "lags_schedule.cpp"),
+           os.path.join(CSRC, "lags_kernels.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

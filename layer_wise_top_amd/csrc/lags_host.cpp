@@ -43,7 +43,7 @@ struct lags_layout {
     std::vector<LayerInfo> linfo;
     std::vector<SampledInfo> sinfo;
     std::vector<MainWork> main_work;
-    std::vector<uint2> fin_work;
+    std::vector<FinWork> fin_work;
     std::vector<uint32_t> pos_layer;
     // per-layer prefix counts of the work lists, for layer-range launches:
     // small-layer work entries, streaming work entries, sampled layers and
@@ -63,7 +63,7 @@ struct lags_layout {
     LayerInfo *d_linfo = nullptr;
     SampledInfo *d_sinfo = nullptr;
     MainWork *d_main = nullptr;
-    uint2 *d_fin = nullptr;
+    FinWork *d_fin = nullptr;
     uint32_t *d_moff = nullptr;
     uint32_t *d_poslayer = nullptr;
     std::map<int32_t, AggTables> agg;
@@ -204,8 +204,25 @@ int build_plan(lags_layout *lo)
                 w.slot_hi = si.slot_hi;
                 stream_work.push_back(w);
             }
-            for (uint32_t b = 0; b < si.fin_nblocks; ++b)
-                lo->fin_work.push_back(make_uint2(li.sid, b * kFinSegs));
+            for (uint32_t b = 0; b < si.fin_nblocks; ++b) {
+                FinWork f{};
+                f.sid = li.sid;
+                f.seg0 = b * kFinSegs;
+                f.nseg = si.nseg;
+                f.seg_base = si.seg_base;
+                f.cap = si.cap;
+                f.slot_lo = si.slot_lo;
+                f.slot_hi = si.slot_hi;
+                f.fin_first = si.fin_first;
+                f.off = li.off;
+                f.n = li.n;
+                f.moff = li.moff;
+                f.k = li.k;
+                f.tbin_base = si.tbin_base;
+                f.tbin_cap = si.tbin_cap;
+                f.a4 = si.a4;
+                lo->fin_work.push_back(f);
+            }
             seg_base += si.nseg;
             slot_base += (uint64_t)si.nseg * si.cap;
             lo->sinfo.push_back(si);
@@ -276,7 +293,7 @@ int ensure_device(lags_layout *lo)
     const size_t b_l = align_up(lo->linfo.size() * sizeof(LayerInfo), kAlign);
     const size_t b_s = align_up(std::max<size_t>(1, lo->sinfo.size()) * sizeof(SampledInfo), kAlign);
     const size_t b_m = align_up(std::max<size_t>(1, lo->main_work.size()) * sizeof(MainWork), kAlign);
-    const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(uint2), kAlign);
+    const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(FinWork), kAlign);
     const size_t b_o = align_up(lo->moff.size() * 4, kAlign);
     const size_t b_p = align_up(lo->pos_layer.size() * 4, kAlign);
     const size_t total = b_l + b_s + b_m + b_f + b_o + b_p;
@@ -286,7 +303,7 @@ int ensure_device(lags_layout *lo)
         std::memcpy(host.data() + b_l, lo->sinfo.data(), lo->sinfo.size() * sizeof(SampledInfo));
     std::memcpy(host.data() + b_l + b_s, lo->main_work.data(), lo->main_work.size() * sizeof(MainWork));
     if (!lo->fin_work.empty())
-        std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(uint2));
+        std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(FinWork));
     std::memcpy(host.data() + b_l + b_s + b_m + b_f, lo->moff.data(), lo->moff.size() * 4);
     std::memcpy(host.data() + b_l + b_s + b_m + b_f + b_o, lo->pos_layer.data(), lo->pos_layer.size() * 4);
     void *d = nullptr;
@@ -301,7 +318,7 @@ int ensure_device(lags_layout *lo)
     lo->d_linfo = (LayerInfo *)p;
     lo->d_sinfo = (SampledInfo *)(p + b_l);
     lo->d_main = (MainWork *)(p + b_l + b_s);
-    lo->d_fin = (uint2 *)(p + b_l + b_s + b_m);
+    lo->d_fin = (FinWork *)(p + b_l + b_s + b_m);
     lo->d_moff = (uint32_t *)(p + b_l + b_s + b_m + b_f);
     lo->d_poslayer = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o);
     return LAGS_OK;
@@ -511,9 +528,11 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
     if (rc != LAGS_OK) return rc;
     if (ns) {
-        rc = traced(lo, kKFinHist, s, [&] { return launch_fin_hist(a, nfin, s); });
+        rc = traced(lo, kKFinBins, s, [&] { return launch_fin_bins(a, ns, s); });
         if (rc != LAGS_OK) return rc;
         rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, nfin, s); });
+        if (rc != LAGS_OK) return rc;
+        rc = traced(lo, kKFinResolve, s, [&] { return launch_fin_resolve(a, ns, s); });
         if (rc != LAGS_OK) return rc;
         rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
@@ -649,8 +668,8 @@ int32_t lags_num_kernels(void) { return kNumKernels; }
 
 const char *lags_kernel_name(int32_t id)
 {
-    static const char *names[kNumKernels] = {"k_sample", "k_main", "k_fin_hist", "k_fin_select",
-                                             "k_fin_emit", "k_agg_starts", "k_agg"};
+    static const char *names[kNumKernels] = {"k_sample", "k_main", "k_fin_bins", "k_fin_select",
+                                             "k_fin_resolve", "k_fin_emit", "k_agg_starts", "k_agg"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 

@@ -19,6 +19,7 @@ constexpr uint32_t kDenseTile = 16384;   // entries per workgroup for k == n lay
 constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident)
 constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
 constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
+constexpr uint32_t kHistCopies = 8;      // copies of each layer's histogram (spread atomics)
 constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LDS (larger: global)
 constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup
 // aggregate
@@ -88,6 +89,23 @@ struct MainWork {
     uint32_t pad[3];
 };
 
+// One entry per finishing workgroup (k_fin_select, k_fin_emit): its segments
+// and the static fields of its layer, so one load starts it.
+struct FinWork {
+    uint32_t sid;         // sampled-layer id
+    uint32_t seg0;        // first segment of the workgroup (inside the layer)
+    uint32_t nseg;        // segments of the layer
+    uint32_t seg_base;    // first global segment id of the layer
+    uint32_t cap;         // candidate slots per segment
+    uint32_t slot_lo, slot_hi;   // first slot of the layer
+    uint32_t fin_first;   // first finishing workgroup of the layer
+    uint32_t off, n;      // the layer's entries
+    uint32_t moff, k;     // the layer's message
+    uint32_t tbin_base, tbin_cap;
+    uint32_t a4;          // 4-aligned start of the layer's interior
+    uint32_t pad;
+};
+
 struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t G;           // guess: candidates have key >= G
     uint32_t SH;          // histogram bin width 2^SH above G
@@ -95,13 +113,12 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t overflow;    // a segment had more candidates than slots
     uint32_t bstar;       // histogram bin holding the k-th largest candidate
     uint32_t c_above;     // candidates in bins above bstar
-    uint32_t done_hist;   // histogram workgroups finished
-    uint32_t done_fin;    // finishing workgroups finished
+    uint32_t reserved[2];
     uint32_t tbin_n;      // entries of bin bstar collected
     uint32_t T;           // k-th largest key of the layer
     uint32_t idx_cut;     // largest global index taken among keys == T
     uint32_t pad[5];
-    uint32_t hist[kNBins];
+    uint32_t hist[kHistCopies * kNBins];   // copy c at [c * kNBins, (c + 1) * kNBins)
 };
 
 // report counters at the head of the workspace
@@ -115,7 +132,7 @@ struct SparsifyArgs {
     const LayerInfo *linfo;
     const SampledInfo *sinfo;
     const MainWork *main_work;   // one per main workgroup
-    const uint2 *fin_work;    // (sid, first segment) per finishing workgroup
+    const FinWork *fin_work;  // one per finishing workgroup
     uint32_t *report;
     SampledState *state;
     uint32_t *seg_count;
@@ -158,15 +175,16 @@ struct AggArgs {
 
 // kernel ids for tracing
 enum : int32_t {
-    kKSample = 0, kKMain = 1, kKFinHist = 2, kKFinSelect = 3, kKFinEmit = 4,
-    kKAggStarts = 5, kKAgg = 6, kNumKernels = 7
+    kKSample = 0, kKMain = 1, kKFinBins = 2, kKFinSelect = 3, kKFinResolve = 4,
+    kKFinEmit = 5, kKAggStarts = 6, kKAgg = 7, kNumKernels = 8
 };
 
 // launchers (lags_kernels.hip)
 hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
-hipError_t launch_fin_hist(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_fin_bins(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_fin_resolve(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
 hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s);

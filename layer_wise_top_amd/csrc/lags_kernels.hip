@@ -16,17 +16,19 @@
 //   k_main        the streaming pass: acc = grad + residual is written back
 //                 to the residual buffer; entries with |acc| key >= G are
 //                 compacted, in index order, into per-segment candidate
-//                 slots.  Small layers (<= 4096 entries) are done start to
+//                 slots, and counted in the layer's histogram of bins above
+//                 G.  Small layers (<= 4096 entries) are done start to
 //                 finish by one workgroup (exact radix select in LDS); k == n
 //                 layers are sent whole.
-//   k_fin_hist    histogram of the candidates in bins above G; the last
-//                 workgroup of a layer finds the bin holding the k-th largest.
+//   k_fin_bins    one workgroup per sampled layer: finds the histogram bin
+//                 holding the k-th largest candidate.
 //   k_fin_select  counts, per segment, candidates above the threshold bin and
-//                 gathers the threshold bin's candidates; the last workgroup of
-//                 a layer resolves the exact threshold key T and the tie cut
-//                 (lowest indices first) and scans segment counts into message
-//                 offsets.  A layer whose guess failed (too few candidates or
-//                 a full segment) is done here by the exact multi-pass path.
+//                 gathers the threshold bin's candidates.
+//   k_fin_resolve one workgroup per sampled layer: resolves the exact
+//                 threshold key T and the tie cut (lowest indices first) and
+//                 scans segment counts into message offsets.  A layer whose
+//                 guess failed (too few candidates or a full segment) is done
+//                 here by the exact multi-pass path.
 //   k_fin_emit    writes the selected candidates of each segment, in index
 //                 order, to the message and zeroes their residual.
 //   k_agg_starts  for every worker, where each index chunk starts in its
@@ -398,12 +400,16 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
 
 // Candidates of one segment, in index order.  They are staged in the wave's
 // LDS buffer and written to the segment's slots in contiguous bursts: isolated
-// 8-byte stores would each cost a partial-line write in memory.
+// 8-byte stores would each cost a partial-line write in memory.  Every stored
+// candidate is also counted in the layer's bin histogram (device atomics; a
+// few per segment).
 constexpr uint32_t kStage = 256;   // per wave; one row holds at most 4 x 64 candidates
 
 struct CandWriter {
     uint2 *slots;      // the segment's slots
     uint2 *stage;      // the wave's LDS buffer
+    uint32_t *hist;    // the layer's kNBins bins above G (bin width 2^SH)
+    uint32_t G, SH;
     uint32_t cap;      // slots of the segment
     uint32_t run;      // candidates so far (may exceed cap)
     uint32_t flushed;  // candidates written to slots so far
@@ -417,7 +423,11 @@ struct CandWriter {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         for (uint32_t t = ln; t < n; t += 64) {
             const uint32_t pos = flushed + t;
-            if (pos < cap) slots[pos] = stage[t];
+            if (pos < cap) {
+                const uint2 c = stage[t];
+                slots[pos] = c;
+                atomicAdd(&hist[cand_bin(c.y & 0x7fffffffu, G, SH)], 1u);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         flushed = run;
@@ -447,14 +457,13 @@ struct CandWriter {
 // in index order to the segment's candidate slots.  Rows of 2 x 64 float4 per
 // iteration (measured fastest on gfx950 for this loop).
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
-                                const uint32_t *Gp, uint2 *stage)
+                                SampledState *st, uint32_t hcopy, uint2 *stage)
 {
     constexpr int U = 2;
     const uint32_t ln = lane_id();
     const uint32_t e0 = w.a4 + seg * kSeg;
     const uint32_t e1 = min(e0 + kSeg, w.b4);
     const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * w.cap;
-    CandWriter cw{a.slots + slot0, stage, w.cap, 0u, 0u, ln};
     const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
     v4f *r4 = reinterpret_cast<v4f *>(a.res);
     const uint32_t q1 = e1 / 4u;
@@ -472,7 +481,8 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
             rv[u] = gv[u];
         }
     }
-    const uint32_t G = *Gp;
+    const uint32_t G = st->G;
+    CandWriter cw{a.slots + slot0, stage, st->hist + hcopy, G, st->SH, w.cap, 0u, 0u, ln};
     uint32_t idx[4];
     float v[4];
 
@@ -538,7 +548,10 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         cw.append(cm, idx, v);
     }
     cw.flush();
-    if (ln == 0) a.seg_count[w.seg_base + seg] = cw.run;
+    if (ln == 0) {
+        a.seg_count[w.seg_base + seg] = cw.run;
+        if (cw.run > w.cap) atomicOr(&st->overflow, 1u);   // the layer takes the exact path
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
@@ -555,7 +568,11 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 
     if (w.cls == kClsSampled) {   // streaming tile w.tile: one segment per wave
         const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
-        if (seg < w.nseg) sampled_segment(a, w, seg, &a.state[w.sid].G, stage[threadIdx.x >> 6]);
+        // workgroups land on the XCDs round-robin: one histogram copy per XCD
+        // keeps the atomics on each bin spread
+        if (seg < w.nseg)
+            sampled_segment(a, w, seg, a.state + w.sid, (blockIdx.x % kHistCopies) * kNBins,
+                            stage[threadIdx.x >> 6]);
         return;
     }
 
@@ -590,28 +607,31 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 
 // ---------------------------------------------------------------------------
 // Finishing kernels.  fin_work lists, per sampled layer, workgroups of up to
-// kFinSegs consecutive segments; each wave of a workgroup takes every fourth.
+// kFinSegs consecutive segments; each wave of a workgroup takes every
+// kWaves-th.  Each entry carries everything static the workgroup needs, so
+// its first load is followed directly by the per-call loads.
 
-__device__ __forceinline__ uint32_t seg_of(const SampledInfo &S, uint32_t i)
+__device__ __forceinline__ uint32_t seg_of(const FinWork &f, uint32_t i)
 {
-    if (i < S.a4) return 0;
-    return min((i - S.a4) / kSeg, S.nseg - 1u);
+    if (i < f.a4) return 0;
+    return min((i - f.a4) / kSeg, f.nseg - 1u);
 }
 
-// Last workgroup of a layer after the histogram pass: locate the candidate
-// bin that holds the k-th largest, or mark the layer for the exact path.
+// Locate the candidate bin that holds the k-th largest, or mark the layer for
+// the exact path (too few candidates, or a segment ran out of slots).
 __device__ void finalize_hist(const SparsifyArgs &a, const LayerInfo &L, SampledState *st,
                               uint32_t *hist, uint32_t *tmp, uint32_t *res)
 {
     uint32_t part = 0;
     for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
-        hist[b] = ld_coherent(&st->hist[b]);
-        part += hist[b];
+        uint32_t h = 0;
+        for (uint32_t c = 0; c < kHistCopies; ++c) h += st->hist[c * kNBins + b];
+        hist[b] = h;
+        part += h;
     }
     uint32_t C;
     block_excl_scan(part, tmp, C);    // also orders the LDS writes above
-    const uint32_t overflow = ld_coherent(&st->overflow);
-    if (C < L.k || overflow) {
+    if (C < L.k || st->overflow) {
         if (threadIdx.x == 0) {
             st->status = kStExact;
             atomicAdd(&a.report[kRepSampled], 1u);
@@ -628,86 +648,119 @@ __device__ void finalize_hist(const SparsifyArgs &a, const LayerInfo &L, Sampled
     }
 }
 
-// The segments a wave handles in a finishing workgroup (every kWaves-th of the
-// workgroup's kFinSegs), with their candidate counts and first 64 slots loaded
-// up front so that one memory round trip serves all of them.
-constexpr int kSegsPerWave = kFinSegs / kWaves;
-struct WaveSegs {
-    uint32_t s0;                      // first segment of the workgroup
-    uint32_t wave;
-    uint32_t nseg;
-    uint32_t cnt[kSegsPerWave];
-    uint2 first[kSegsPerWave];
-    __device__ uint32_t seg(int i) const { return s0 + wave + (uint32_t)i * kWaves; }
-    __device__ bool valid(int i) const { return seg(i) < nseg; }
-    __device__ const uint2 *slots(const SparsifyArgs &a, const SampledInfo &S, int i) const
-    {
-        return a.slots + (((uint64_t)S.slot_hi << 32) | S.slot_lo) + (uint64_t)seg(i) * S.cap;
-    }
-    // returns 1 if a segment had more candidates than slots
-    __device__ uint32_t load(const SparsifyArgs &a, const SampledInfo &S, uint32_t first_seg,
-                             uint32_t wv, uint32_t ln)
-    {
-        s0 = first_seg;
-        wave = wv;
-        nseg = min(first_seg + kFinSegs, S.nseg);
-        uint32_t raw[kSegsPerWave];
-#pragma unroll
-        for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[S.seg_base + seg(i)] : 0u;
-        uint32_t ovf = 0;
-#pragma unroll
-        for (int i = 0; i < kSegsPerWave; ++i) {
-            ovf |= raw[i] > S.cap ? 1u : 0u;
-            cnt[i] = min(raw[i], S.cap);
-            first[i] = (ln < cnt[i]) ? slots(a, S, i)[ln] : make_uint2(0, 0);
-        }
-        return ovf;
-    }
-};
-
-// k_fin_hist: histogram of the candidates' keys in bins of width 2^SH above G.
-__global__ __launch_bounds__(kBlock) void k_fin_hist(SparsifyArgs a)
+// k_fin_bins: one workgroup per sampled layer, after the streaming pass has
+// filled the layer's histogram.
+__global__ __launch_bounds__(kBlock) void k_fin_bins(SparsifyArgs a)
 {
     __shared__ uint32_t hist[kNBins];
     __shared__ uint32_t tmp[kWaves];
     __shared__ uint32_t res[2];
-    __shared__ uint32_t last;
-
-    const uint32_t fb = a.fin_base + blockIdx.x;
-    const uint2 w = a.fin_work[fb];
-    const uint32_t sid = w.x;
+    if (blockIdx.x >= a.nsampled) return;
+    const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
     const LayerInfo L = a.linfo[S.layer];
-    SampledState *st = a.state + sid;
-    const uint32_t G = st->G, SH = st->SH;
+    finalize_hist(a, L, a.state + sid, hist, tmp, res);
+}
+
+// The segments a wave handles in a finishing workgroup, with their candidate
+// counts and first 64 slots loaded up front so that one memory round trip
+// serves all of them.
+constexpr int kSegsPerWave = kFinSegs / kWaves;
+struct WaveSegs {
+    uint32_t s0;                      // first segment of the workgroup
+    uint32_t wave;
+    uint32_t send;                    // end of the workgroup's segments
+    uint32_t cnt[kSegsPerWave];
+    uint2 first[kSegsPerWave];
+    __device__ uint32_t seg(int i) const { return s0 + wave + (uint32_t)i * kWaves; }
+    __device__ bool valid(int i) const { return seg(i) < send; }
+    __device__ const uint2 *slots(const SparsifyArgs &a, const FinWork &f, int i) const
+    {
+        return a.slots + (((uint64_t)f.slot_hi << 32) | f.slot_lo) + (uint64_t)seg(i) * f.cap;
+    }
+    __device__ void load(const SparsifyArgs &a, const FinWork &f, uint32_t wv, uint32_t ln)
+    {
+        s0 = f.seg0;
+        wave = wv;
+        send = min(f.seg0 + kFinSegs, f.nseg);
+        uint32_t raw[kSegsPerWave];
+#pragma unroll
+        for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[f.seg_base + seg(i)] : 0u;
+#pragma unroll
+        for (int i = 0; i < kSegsPerWave; ++i) {
+            cnt[i] = min(raw[i], f.cap);
+            first[i] = (ln < cnt[i]) ? slots(a, f, i)[ln] : make_uint2(0, 0);
+        }
+    }
+};
+
+// k_fin_select: per segment, the count of candidates above the threshold bin;
+// the threshold bin's candidates are gathered into the layer's list (one
+// reservation per wave).  Per workgroup, the total above the bin.
+__global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
+{
+    __shared__ uint32_t wtot[kWaves];
+    const FinWork f = a.fin_work[a.fin_base + blockIdx.x];
+    SampledState *st = a.state + f.sid;
     const uint32_t ln = lane_id();
-    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) hist[b] = 0;
-    __syncthreads();
+    const uint32_t wv = threadIdx.x >> 6;
     WaveSegs ws;
-    const uint32_t ovf = ws.load(a, S, w.y, threadIdx.x >> 6, ln);
+    ws.load(a, f, wv, ln);            // issued before the layer's status arrives
+    if (st->status != kStOk) return;  // the exact path takes the layer
+    const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
+    // pass 1: per segment, candidates above the threshold bin; per lane,
+    // candidates in it
+    uint32_t wsum = 0, nt = 0;
     for (int i = 0; i < kSegsPerWave; ++i) {
-        if (ln < ws.cnt[i]) atomicAdd(&hist[cand_bin(ws.first[i].y & 0x7fffffffu, G, SH)], 1u);
-        for (uint32_t p = 64 + ln; p < ws.cnt[i]; p += 64)
-            atomicAdd(&hist[cand_bin(ws.slots(a, S, i)[p].y & 0x7fffffffu, G, SH)], 1u);
+        if (!ws.valid(i)) continue;
+        const uint32_t cnt = ws.cnt[i];
+        const uint2 *slots = ws.slots(a, f, i);
+        uint32_t D = 0;
+        for (uint32_t p = ln; p < cnt; p += 64) {
+            const uint2 c = (p < 64) ? ws.first[i] : slots[p];
+            const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
+            D += (bin > bstar) ? 1u : 0u;
+            nt += (bin == bstar) ? 1u : 0u;
+        }
+        D = wave_sum(D);
+        if (ln == 0) a.seg_sel[f.seg_base + ws.seg(i)] = D;
+        wsum += D;
     }
-    __syncthreads();
-    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
-        const uint32_t v = hist[b];
-        if (v) atomicAdd(&st->hist[b], v);
+    // pass 2: one reservation per wave in the layer's threshold-bin list
+    const uint32_t incl = wave_incl_scan(nt);
+    const uint32_t wt = __shfl(incl, 63, 64);
+    if (wt) {
+        uint32_t base = 0;
+        if (ln == 0) base = atomicAdd(&st->tbin_n, wt);
+        uint32_t t = __shfl(base, 0, 64) + incl - nt;
+        uint2 *tb = a.tbin + f.tbin_base;
+        for (int i = 0; i < kSegsPerWave; ++i) {
+            if (!ws.valid(i)) continue;
+            const uint32_t cnt = ws.cnt[i];
+            const uint2 *slots = ws.slots(a, f, i);
+            for (uint32_t p = ln; p < cnt; p += 64) {
+                const uint2 c = (p < 64) ? ws.first[i] : slots[p];
+                if (cand_bin(c.y & 0x7fffffffu, G, SH) == bstar) {
+                    if (t < f.tbin_cap) tb[t] = c;
+                    ++t;
+                }
+            }
+        }
     }
-    if (ovf && ln == 0) atomicOr(&st->overflow, 1u);
-    wait_mem_done();
+    if (ln == 0) wtot[wv] = wsum;
     __syncthreads();
-    if (threadIdx.x == 0) last = (atomicAdd(&st->done_hist, 1u) == S.fin_nblocks - 1u) ? 1u : 0u;
-    __syncthreads();
-    if (last) finalize_hist(a, L, st, hist, tmp, res);
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int i = 0; i < kWaves; ++i) t += wtot[i];
+        a.fin_total[a.fin_base + blockIdx.x] = t;
+    }
 }
 
 // Exact threshold and tie cut among the h entries of the threshold bin (the
 // need-th largest key; among keys equal to it, the lowest indices first), and
 // the per-segment and per-workgroup counts of the bin's selected entries.
 template <class KeyF, class IdxF>
-__device__ void resolve_tbin(const SparsifyArgs &a, const SampledInfo &S, uint32_t h, uint32_t need,
+__device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t h, uint32_t need,
                              const KeyF &key, const IdxF &idx, uint32_t *hist, uint32_t *tmp,
                              uint32_t *res, uint32_t &T_out, uint32_t &cut_out)
 {
@@ -721,86 +774,38 @@ __device__ void resolve_tbin(const SparsifyArgs &a, const SampledInfo &S, uint32
     for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
         const uint32_t kp = key(p), ip = idx(p);
         if (kp > T || (kp == T && ip <= cut)) {
-            const uint32_t sg = seg_of(S, ip);
-            atomicAdd(&a.seg_sel[S.seg_base + sg], 1u);
-            atomicAdd(&a.fin_total[S.fin_first + sg / kFinSegs], 1u);
+            const uint32_t sg = seg_of(f, ip);
+            atomicAdd(&a.seg_sel[f.seg_base + sg], 1u);
+            atomicAdd(&a.fin_total[f.fin_first + sg / kFinSegs], 1u);
         }
     }
     T_out = T;
     cut_out = cut;
 }
 
-// k_fin_select: count, per segment, candidates above the threshold bin and
-// gather the threshold bin; the last workgroup of a layer resolves the exact
-// threshold key T and the tie cut, and turns per-workgroup counts into
-// message offsets.  A layer whose guess failed is done here exactly.
-__global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
+// k_fin_resolve: one workgroup per sampled layer.  Resolves the exact
+// threshold key T and the tie cut inside the threshold bin and turns the
+// per-workgroup counts into message offsets.  A layer whose guess failed
+// (status not Ok, or a threshold bin above its list's capacity) is done here
+// by the exact multi-pass path over the accumulated values.
+__global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
 {
     __shared__ uint32_t hist[kNBins];
     __shared__ uint32_t tk[kTbinCap];
     __shared__ uint32_t ti[kTbinCap];
     __shared__ uint32_t tmp[kWaves];
-    __shared__ uint32_t wtot[kWaves];
     __shared__ uint32_t res[2];
-    __shared__ uint32_t last;
-
-    const uint32_t fb = a.fin_base + blockIdx.x;
-    const uint2 w = a.fin_work[fb];
-    const uint32_t sid = w.x;
+    if (blockIdx.x >= a.nsampled) return;
+    const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
     const LayerInfo L = a.linfo[S.layer];
+    const FinWork f = a.fin_work[S.fin_first];     // the layer's static fields
     SampledState *st = a.state + sid;
     const uint32_t status = st->status;
-    const uint32_t ln = lane_id();
-    const uint32_t wv = threadIdx.x >> 6;
+    const uint32_t h = st->tbin_n;
 
-    if (status == kStOk) {
-        const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
-        WaveSegs ws;
-        ws.load(a, S, w.y, wv, ln);
-        uint32_t wsum = 0;
-        for (int i = 0; i < kSegsPerWave; ++i) {
-            if (!ws.valid(i)) continue;
-            const uint32_t s = ws.seg(i);
-            const uint32_t cnt = ws.cnt[i];
-            const uint2 *slots = ws.slots(a, S, i);
-            uint32_t D = 0;
-            for (uint32_t p = ln; p < cnt; p += 64) {
-                const uint2 c = (p < 64) ? ws.first[i] : slots[p];
-                const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
-                if (bin > bstar) {
-                    ++D;
-                } else if (bin == bstar) {
-                    const uint32_t t = atomicAdd(&st->tbin_n, 1u);
-                    if (t < S.tbin_cap) {
-                        uint32_t *e = reinterpret_cast<uint32_t *>(a.tbin + (uint64_t)S.tbin_base + t);
-                        st_coherent(e, c.x);
-                        st_coherent(e + 1, c.y);
-                    }
-                }
-            }
-            D = wave_sum(D);
-            if (ln == 0) st_coherent(&a.seg_sel[S.seg_base + s], D);
-            wsum += D;
-        }
-        if (ln == 0) wtot[wv] = wsum;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t t = 0;
-            for (int i = 0; i < kWaves; ++i) t += wtot[i];
-            st_coherent(&a.fin_total[fb], t);
-        }
-    }
-    wait_mem_done();
-    __syncthreads();
-    if (threadIdx.x == 0) last = (atomicAdd(&st->done_fin, 1u) == S.fin_nblocks - 1u) ? 1u : 0u;
-    __syncthreads();
-    if (!last) return;
-
-    const uint32_t h = ld_coherent(&st->tbin_n);
     if (status != kStOk || h > S.tbin_cap) {
-        // exact multi-pass path over the accumulated values (the residual
-        // buffer holds acc for every entry of the layer after k_main)
+        // the residual buffer holds acc for every entry of the layer
         if (threadIdx.x == 0) {
             if (status == kStOk) atomicAdd(&a.report[kRepExact], 1u);
             st->status = kStExact;
@@ -814,32 +819,33 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     // resolve the threshold inside bin bstar: in LDS when the bin fits,
     // otherwise straight from the workspace
     const uint32_t need = L.k - st->c_above;
-    const uint32_t *tb = reinterpret_cast<const uint32_t *>(a.tbin + (uint64_t)S.tbin_base);
+    const uint2 *tb = a.tbin + S.tbin_base;
     uint32_t T, idx_cut;
     if (h <= kTbinCap) {
         for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
-            ti[p] = ld_coherent(tb + 2 * p);
-            tk[p] = ld_coherent(tb + 2 * p + 1) & 0x7fffffffu;
+            const uint2 c = tb[p];
+            ti[p] = c.x;
+            tk[p] = c.y & 0x7fffffffu;
         }
         __syncthreads();
-        resolve_tbin(a, S, h, need, [&](uint32_t p) { return tk[p]; }, [&](uint32_t p) { return ti[p]; },
+        resolve_tbin(a, f, h, need, [&](uint32_t p) { return tk[p]; }, [&](uint32_t p) { return ti[p]; },
                      hist, tmp, res, T, idx_cut);
     } else {
         if (threadIdx.x == 0) atomicAdd(&a.report[kRepWide], 1u);
-        resolve_tbin(a, S, h, need, [&](uint32_t p) { return ld_coherent(tb + 2 * p + 1) & 0x7fffffffu; },
-                     [&](uint32_t p) { return ld_coherent(tb + 2 * p); }, hist, tmp, res, T, idx_cut);
+        resolve_tbin(a, f, h, need, [&](uint32_t p) { return tb[p].y & 0x7fffffffu; },
+                     [&](uint32_t p) { return tb[p].x; }, hist, tmp, res, T, idx_cut);
     }
-    const uint32_t fin_first = S.fin_first;
+    // the workgroup's own atomics above complete before the scan reads the totals
     wait_mem_done();
     __syncthreads();
     // per-workgroup totals -> exclusive message offsets (in place)
     uint32_t carry = 0;
     for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
         const uint32_t b = base + threadIdx.x;
-        const uint32_t v = (b < S.fin_nblocks) ? ld_coherent(&a.fin_total[fin_first + b]) : 0u;
+        const uint32_t v = (b < S.fin_nblocks) ? ld_coherent(&a.fin_total[S.fin_first + b]) : 0u;
         uint32_t tot;
         const uint32_t ex = block_excl_scan(v, tmp, tot);
-        if (b < S.fin_nblocks) a.fin_total[fin_first + b] = carry + ex;
+        if (b < S.fin_nblocks) a.fin_total[S.fin_first + b] = carry + ex;
         carry += tot;
     }
     if (threadIdx.x == 0) {
@@ -854,31 +860,28 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 {
     __shared__ uint32_t sbase[kFinSegs];
     const uint32_t fb = a.fin_base + blockIdx.x;
-    const uint2 w = a.fin_work[fb];
-    const uint32_t sid = w.x;
-    const SampledState *st = a.state + sid;
-    if (st->status != kStOk) return;
-    const SampledInfo S = a.sinfo[sid];
-    const LayerInfo L = a.linfo[S.layer];
-    const uint32_t T = st->T, cut = st->idx_cut;
-    const uint32_t mend = L.moff + L.k;
+    const FinWork f = a.fin_work[fb];
+    const SampledState *st = a.state + f.sid;
     const uint32_t ln = lane_id();
-    const uint32_t s_end = min(w.y + kFinSegs, S.nseg);
-    if (threadIdx.x == 0) {
-        uint32_t run = L.moff + a.fin_total[fb];
-        for (uint32_t s = w.y; s < s_end; ++s) {
-            sbase[s - w.y] = run;
-            run += a.seg_sel[S.seg_base + s];
-        }
-    }
     WaveSegs ws;
-    ws.load(a, S, w.y, threadIdx.x >> 6, ln);
+    ws.load(a, f, threadIdx.x >> 6, ln);      // issued before the status arrives
+    static_assert(kFinSegs <= 64, "one wave scans the segment counts");
+    const uint32_t s_end = min(f.seg0 + kFinSegs, f.nseg);
+    if (threadIdx.x < 64) {
+        const uint32_t s = f.seg0 + ln;
+        const uint32_t v = (s < s_end) ? a.seg_sel[f.seg_base + s] : 0u;
+        const uint32_t incl = wave_incl_scan(v);
+        if (s < s_end) sbase[ln] = f.moff + a.fin_total[fb] + incl - v;
+    }
+    if (st->status != kStOk) return;         // uniform over the workgroup
+    const uint32_t T = st->T, cut = st->idx_cut;
+    const uint32_t mend = f.moff + f.k;
     __syncthreads();
     for (int i = 0; i < kSegsPerWave; ++i) {
         if (!ws.valid(i)) continue;
         const uint32_t cnt = ws.cnt[i];
-        const uint2 *slots = ws.slots(a, S, i);
-        const uint32_t base = sbase[ws.seg(i) - w.y];
+        const uint2 *slots = ws.slots(a, f, i);
+        const uint32_t base = sbase[ws.seg(i) - f.seg0];
         uint32_t run = 0;
         for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
             const uint32_t p = p0 + ln;
@@ -889,7 +892,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
                 const uint32_t key = c.y & 0x7fffffffu;
                 // candidates always lie in their layer; the range test keeps a
                 // damaged workspace from turning into a stray store
-                sel = (c.x - L.off < L.n) && (key > T || (key == T && c.x <= cut));
+                sel = (c.x - f.off < f.n) && (key > T || (key == T && c.x <= cut));
             }
             const uint64_t m = __ballot(sel);
             if (sel) {
@@ -1144,15 +1147,21 @@ hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_fin_hist(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+hipError_t launch_fin_bins(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_fin_hist, dim3(nblocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_fin_bins, dim3(nblocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     hipLaunchKernelGGL(k_fin_select, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fin_resolve(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fin_resolve, dim3(nblocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 

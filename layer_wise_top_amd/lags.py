@@ -27,7 +27,7 @@ EXPORTED = (
     "lags_layout_msg_offset", "lags_workspace_bytes", "lags_sparsify_layers",
     "lags_aggregate_apply", "lags_workspace_report", "lags_trace_enable",
     "lags_trace_read", "lags_num_kernels", "lags_kernel_name", "lags_sparsify_range",
-    "lags_aggregate_range",
+    "lags_aggregate_range", "lags_merge_schedule", "lags_schedule_finish",
 )
 
 
@@ -81,6 +81,12 @@ def lib():
     L.lags_sparsify_range.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, sz, u32, vp]
     L.lags_aggregate_range.restype = ctypes.c_int
     L.lags_aggregate_range.argtypes = [vp, i32, i32, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
+    f64 = ctypes.c_double
+    L.lags_merge_schedule.restype = ctypes.c_int
+    L.lags_merge_schedule.argtypes = [i32, vp, vp, f64, f64, vp, ctypes.POINTER(i32),
+                                      ctypes.POINTER(f64)]
+    L.lags_schedule_finish.restype = ctypes.c_int
+    L.lags_schedule_finish.argtypes = [i32, vp, vp, f64, f64, vp, i32, ctypes.POINTER(f64)]
     L.lags_workspace_report.restype = ctypes.c_int
     L.lags_workspace_report.argtypes = [vp, vp, sz, vp, ctypes.POINTER(Report)]
     L.lags_trace_enable.restype = ctypes.c_int
@@ -238,6 +244,39 @@ def lags_aggregate_range(layout: Layout, l0: int, l1: int, weights, msg_idx, msg
     rc = lib().lags_aggregate_range(layout.handle, int(l0), int(l1), wt, mi, mv, int(P), float(lr),
                                     w, ws.numel(), _stream_handle(stream))
     _check("lags_aggregate_range", rc)
+
+
+def lags_merge_schedule(backward_time, msg_bytes, alpha: float, beta: float):
+    """Returns (runs, finish): runs is a list of (l0, l1) layer ranges in
+    sending order (the first holds the last layer), finish the modelled time."""
+    bt = np.ascontiguousarray(backward_time, dtype=np.float64)
+    nb = np.ascontiguousarray(msg_bytes, dtype=np.int64)
+    if bt.ndim != 1 or nb.shape != bt.shape:
+        raise ValueError("backward_time and msg_bytes must be 1-D of one length")
+    L = bt.size
+    bounds = np.empty(L + 1, dtype=np.int32)
+    nr = ctypes.c_int32()
+    fin = ctypes.c_double()
+    rc = lib().lags_merge_schedule(L, bt.ctypes.data, nb.ctypes.data, float(alpha), float(beta),
+                                   bounds.ctypes.data, ctypes.byref(nr), ctypes.byref(fin))
+    _check("lags_merge_schedule", rc)
+    runs = [(int(bounds[j + 1]), int(bounds[j])) for j in range(nr.value)]
+    return runs, fin.value
+
+
+def lags_schedule_finish(backward_time, msg_bytes, alpha: float, beta: float, runs) -> float:
+    """Modelled finish time of `runs` ((l0, l1) ranges in sending order)."""
+    bt = np.ascontiguousarray(backward_time, dtype=np.float64)
+    nb = np.ascontiguousarray(msg_bytes, dtype=np.int64)
+    L = bt.size
+    bounds = np.array([L] + [int(r[0]) for r in runs], dtype=np.int32)
+    if any(int(r[1]) != int(bounds[j]) for j, r in enumerate(runs)):
+        raise ValueError("runs are not consecutive in sending order")
+    fin = ctypes.c_double()
+    rc = lib().lags_schedule_finish(L, bt.ctypes.data, nb.ctypes.data, float(alpha), float(beta),
+                                    bounds.ctypes.data, len(runs), ctypes.byref(fin))
+    _check("lags_schedule_finish", rc)
+    return fin.value
 
 
 def lags_workspace_report(layout: Layout, ws, stream=None) -> dict:
