@@ -43,13 +43,13 @@ struct lags_layout {
     std::vector<LayerInfo> linfo;
     std::vector<SampledInfo> sinfo;
     std::vector<MainWork> main_work;
+    std::vector<uint32_t> small_layers;
     std::vector<FinWork> fin_work;
     std::vector<uint32_t> pos_layer;
     // per-layer prefix counts of the work lists, for layer-range launches:
     // small-layer work entries, streaming work entries, sampled layers and
     // finishing workgroups before layer l
     std::vector<uint32_t> small_pre, stream_pre, sid_pre, fin_pre;
-    uint32_t nsmall = 0;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
     uint64_t tbin_total = 0;
@@ -66,6 +66,7 @@ struct lags_layout {
     FinWork *d_fin = nullptr;
     uint32_t *d_moff = nullptr;
     uint32_t *d_poslayer = nullptr;
+    uint32_t *d_small = nullptr;
     std::map<int32_t, AggTables> agg;
     // tracing
     bool trace = false;
@@ -121,7 +122,7 @@ int build_plan(lags_layout *lo)
     uint32_t seg_base = 0;
     uint64_t slot_base = 0;
     uint64_t tbin_base = 0;
-    std::vector<MainWork> small_work, stream_work;
+    std::vector<MainWork> stream_work;
     lo->small_pre.assign(L + 1, 0);
     lo->stream_pre.assign(L + 1, 0);
     lo->sid_pre.assign(L + 1, 0);
@@ -134,7 +135,7 @@ int build_plan(lags_layout *lo)
         return w;
     };
     for (int32_t l = 0; l < L; ++l) {
-        lo->small_pre[l] = (uint32_t)small_work.size();
+        lo->small_pre[l] = (uint32_t)lo->small_layers.size();
         lo->stream_pre[l] = (uint32_t)stream_work.size();
         lo->sid_pre[l] = (uint32_t)lo->sinfo.size();
         lo->fin_pre[l] = (uint32_t)lo->fin_work.size();
@@ -148,7 +149,7 @@ int build_plan(lags_layout *lo)
         if (li.n <= kSmallMax) {
             li.cls = kClsSmall;
             li.ntiles = 1;
-            small_work.push_back(work((uint32_t)l, kClsSmall, 0));
+            lo->small_layers.push_back((uint32_t)l);
         } else if (li.k == li.n) {
             li.cls = kClsDense;
             li.ntiles = (li.n + kDenseTile - 1) / kDenseTile;
@@ -228,14 +229,11 @@ int build_plan(lags_layout *lo)
             lo->sinfo.push_back(si);
         }
     }
-    lo->small_pre[L] = (uint32_t)small_work.size();
+    lo->small_pre[L] = (uint32_t)lo->small_layers.size();
     lo->stream_pre[L] = (uint32_t)stream_work.size();
     lo->sid_pre[L] = (uint32_t)lo->sinfo.size();
     lo->fin_pre[L] = (uint32_t)lo->fin_work.size();
-    lo->nsmall = (uint32_t)small_work.size();
-    // small layers first: they start while the streaming tiles fill the chip
-    lo->main_work = small_work;
-    lo->main_work.insert(lo->main_work.end(), stream_work.begin(), stream_work.end());
+    lo->main_work = stream_work;
     lo->nseg_total = seg_base;
     lo->slots_total = slot_base;
     lo->tbin_total = tbin_base;
@@ -296,7 +294,8 @@ int ensure_device(lags_layout *lo)
     const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(FinWork), kAlign);
     const size_t b_o = align_up(lo->moff.size() * 4, kAlign);
     const size_t b_p = align_up(lo->pos_layer.size() * 4, kAlign);
-    const size_t total = b_l + b_s + b_m + b_f + b_o + b_p;
+    const size_t b_sm = align_up(std::max<size_t>(1, lo->small_layers.size()) * 4, kAlign);
+    const size_t total = b_l + b_s + b_m + b_f + b_o + b_p + b_sm;
     std::vector<unsigned char> host(total, 0);
     std::memcpy(host.data(), lo->linfo.data(), lo->linfo.size() * sizeof(LayerInfo));
     if (!lo->sinfo.empty())
@@ -306,6 +305,9 @@ int ensure_device(lags_layout *lo)
         std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(FinWork));
     std::memcpy(host.data() + b_l + b_s + b_m + b_f, lo->moff.data(), lo->moff.size() * 4);
     std::memcpy(host.data() + b_l + b_s + b_m + b_f + b_o, lo->pos_layer.data(), lo->pos_layer.size() * 4);
+    if (!lo->small_layers.empty())
+        std::memcpy(host.data() + b_l + b_s + b_m + b_f + b_o + b_p, lo->small_layers.data(),
+                    lo->small_layers.size() * 4);
     void *d = nullptr;
     if (hipMalloc(&d, total) != hipSuccess) return LAGS_ENOMEM;
     if (hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
@@ -321,6 +323,7 @@ int ensure_device(lags_layout *lo)
     lo->d_fin = (FinWork *)(p + b_l + b_s + b_m);
     lo->d_moff = (uint32_t *)(p + b_l + b_s + b_m + b_f);
     lo->d_poslayer = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o);
+    lo->d_small = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o + b_p);
     return LAGS_OK;
 }
 
@@ -516,24 +519,32 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
     a.sample_base = lo->sid_pre[l0];
     a.nsampled = lo->sid_pre[l1] - lo->sid_pre[l0];
-    a.main_base_a = lo->small_pre[l0];
-    a.main_cnt_a = lo->small_pre[l1] - lo->small_pre[l0];
-    a.main_base_b = lo->nsmall + lo->stream_pre[l0];
+    a.main_base = lo->stream_pre[l0];
     a.fin_base = lo->fin_pre[l0];
+    a.small_layers = lo->d_small;
+    a.small_base = lo->small_pre[l0];
+    a.nsmall = lo->small_pre[l1] - lo->small_pre[l0];
     const uint32_t ns = a.nsampled;
-    const uint32_t nmain = a.main_cnt_a + (lo->stream_pre[l1] - lo->stream_pre[l0]);
+    const uint32_t nmain = lo->stream_pre[l1] - lo->stream_pre[l0];
     const uint32_t nfin = lo->fin_pre[l1] - lo->fin_pre[l0];
+    // k_sample always runs: its first workgroup restarts the report counters
     rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
     if (rc != LAGS_OK) return rc;
-    rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
-    if (rc != LAGS_OK) return rc;
+    if (nmain) {
+        rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
+        if (rc != LAGS_OK) return rc;
+    }
     if (ns) {
         rc = traced(lo, kKFinBins, s, [&] { return launch_fin_bins(a, ns, s); });
         if (rc != LAGS_OK) return rc;
         rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
-        rc = traced(lo, kKFinResolve, s, [&] { return launch_fin_resolve(a, ns, s); });
+    }
+    if (ns + a.nsmall) {
+        rc = traced(lo, kKFinResolve, s, [&] { return launch_fin_resolve(a, ns + a.nsmall, s); });
         if (rc != LAGS_OK) return rc;
+    }
+    if (ns) {
         rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
     }

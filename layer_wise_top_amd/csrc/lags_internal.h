@@ -144,10 +144,11 @@ struct SparsifyArgs {
     uint32_t force_exact;
     // the launched layer range, as offsets into the layout's work lists
     uint32_t sample_base;     // first sampled-layer id
-    uint32_t main_base_a;     // small-layer work entries: [base_a, base_a + cnt_a)
-    uint32_t main_cnt_a;
-    uint32_t main_base_b;     // streaming work entries follow the small ones in the grid
+    uint32_t main_base;       // first streaming work entry
     uint32_t fin_base;        // first finishing workgroup
+    const uint32_t *small_layers;   // ids of the small layers (n <= kSmallMax), ascending
+    uint32_t small_base;      // first small layer of the range in that list
+    uint32_t nsmall;          // small layers in the range
 };
 
 struct AggArgs {
