@@ -43,13 +43,17 @@ def algorithmic_bytes(n, K, P, U):
     return 12 * n + 8 * K + 8 * P * K + 8 * U
 
 
+SMALL_MAX = 4096   # layers up to this size are finished outside the streaming pass
+
+
 def main_kernel_bytes(wl, k):
-    """Algorithmic bytes of one k_main launch: every entry's grad and residual
-    read and residual written, plus the message of layers it sends whole
-    (small layers and k == n layers)."""
+    """Algorithmic bytes of one k_main launch: grad and residual read and the
+    residual written for every entry of the layers it streams (all but the
+    small ones), plus the message of the k == n layers it sends whole."""
     n = np.diff(wl.offsets())
-    whole = (n <= 4096) | (k == n)
-    return int(12 * wl.n + 8 * int(k[whole].sum()))
+    streamed = n > SMALL_MAX
+    whole = streamed & (k == n)
+    return int(12 * int(n[streamed].sum()) + 8 * int(k[whole].sum()))
 
 
 def counters_traffic(workload):
