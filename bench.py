@@ -11,7 +11,12 @@ transformer gradient (1,311,178,752 fp32 entries in 193 tensors, rho = 1/1000,
 P = 16), the largest layout that fits one GPU.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
-                  [--no-cpu-baseline] [--flush]
+                  [--no-cpu-baseline] [--flush] [--pipeline]
+
+--pipeline adds a second measurement of the same step issued layer range by
+layer range (lags_sparsify_range / lags_aggregate_range, last layers first),
+with the ranges of the merged-message schedule (lags_merge_schedule) under a
+synthetic cost model stated in pipeline_model().
 """
 from __future__ import annotations
 
@@ -142,7 +147,41 @@ def cpu_baseline(wl, k, budget_s=20.0):
     }
 
 
-def run_config(name, steps, warmup, do_cpu, flush):
+def pipeline_model(wl, k):
+    """Synthetic inputs of the merged-message schedule (the pages give no
+    numbers): backward time of a tensor proportional to its size, 66 ps per
+    parameter (a 1.3B-parameter model then takes ~86 ms, 4 * n * 16384 tokens
+    at 1 PFLOP/s); each message costs a 50 us start-up plus its all-gather
+    bytes, (P - 1) * 8 * k_l, at 50 GB/s."""
+    n = np.diff(wl.offsets()).astype(np.float64)
+    backward = n * 66e-12
+    nbytes = (wl.P - 1) * 8 * np.asarray(k, np.int64)
+    return backward, nbytes, 50e-6, 1.0 / 50e9
+
+
+def stream_ceiling_gbs(n, reps=5):
+    """Practical HBM ceiling for this access pattern: a plain read-2/write-1
+    fp32 stream of n entries (torch.add), in GB/s."""
+    import torch
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.ones(n, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(a)
+    torch.add(a, b, out=c)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.add(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    return round(12 * n / (ms * 1e-3) / 1e9, 1)
+
+
+def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
     import torch
     from layer_wise_top_amd import lags, workloads as W
 
@@ -185,7 +224,8 @@ def run_config(name, steps, warmup, do_cpu, flush):
     # distinct touched indices of one step (messages of the last warm step)
     U = int(torch.unique(mi.view(-1)).numel())
 
-    # timed region: exactly `steps` steps bracketed by synchronisation
+    # timed region: exactly `steps` steps bracketed by synchronisation; the
+    # per-step events inside it add no synchronisation
     times = []
     if flush:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -200,15 +240,15 @@ def run_config(name, steps, warmup, do_cpu, flush):
         times = [a.elapsed_time(b) for a, b in ev]
         total_ms = sum(times)
     else:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
+        ev[0].record(stream)
+        for i in range(steps):
             step()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        total_ms = e0.elapsed_time(e1)
+        total_ms = ev[0].elapsed_time(ev[-1])
+        times = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     # per-kernel device time: the same steps again with the library's tracer,
     # which brackets every launch with HIP events on the launch stream
     lags.lags_trace_enable(lay, True)
@@ -258,8 +298,41 @@ def run_config(name, steps, warmup, do_cpu, flush):
     }
     if times:
         out["step_ms_min"] = round(min(times), 5)
+        out["step_ms_median"] = round(float(np.median(times)), 5)
+    if pipeline:
+        backward, nbytes, alpha, beta = pipeline_model(wl, k)
+        runs, finish = lags.lags_merge_schedule(backward, nbytes, alpha, beta)
+
+        def piped():
+            for l0, l1 in runs:
+                lags.lags_sparsify_range(lay, l0, l1, g_d, r_d, mi[0], mv[0], ws, 0, stream)
+                lags.lags_aggregate_range(lay, l0, l1, w_d, mi, mv, P, wl.lr, ws, stream)
+
+        for _ in range(warmup):
+            piped()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            piped()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_layer = [(l, l + 1) for l in range(wl.L - 1, -1, -1)]
+        out["pipeline"] = {
+            "runs": len(runs), "ms_per_step": round(e0.elapsed_time(e1) / steps, 5),
+            "model": "backward 66 ps/param, 50 us + all-gather bytes at 50 GB/s per message",
+            "modelled_comm_finish_ms": {
+                "merged": round(finish * 1e3, 4),
+                "per_layer": round(lags.lags_schedule_finish(backward, nbytes, alpha, beta,
+                                                             per_layer) * 1e3, 4),
+                "one_message": round(lags.lags_schedule_finish(backward, nbytes, alpha, beta,
+                                                               [(0, wl.L)]) * 1e3, 4),
+            },
+        }
     del g_d, w_d, r_d, mi, mv, ws, scratch
     torch.cuda.empty_cache()
+    out["stream_ceiling_gbs"] = stream_ceiling_gbs(wl.n)
     if do_cpu:
         log("timing the oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)
@@ -278,6 +351,8 @@ def main():
     ap.add_argument("--flush", action="store_true",
                     help="write 512 MiB between steps (outside the step events) to evict the "
                          "Infinity Cache; steps are then timed one by one")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="also time the step issued per merged-message layer range")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -298,13 +373,14 @@ def main():
                           "launches": 3}), flush=True)
         return
     from layer_wise_top_amd import workloads as W
-    names = list(W.ORDER) if args.config == "all" else [args.config]
+    names = list(W.ORDER) + list(W.EXTRA) if args.config == "all" else [args.config]
     for nm in names:
         if nm not in W.WORKLOADS:
             print(f"unknown workload {nm}; choose from {', '.join(W.WORKLOADS)} or all", file=sys.stderr)
             sys.exit(2)
     for name in names:
-        out = run_config(name, args.steps, args.warmup, not args.no_cpu_baseline, args.flush)
+        out = run_config(name, args.steps, args.warmup, not args.no_cpu_baseline, args.flush,
+                         args.pipeline)
         print(json.dumps(out), flush=True)
 
 

@@ -52,7 +52,6 @@ struct lags_layout {
     std::vector<uint32_t> small_pre, stream_pre, sid_pre, fin_pre;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
-    uint64_t tbin_total = 0;
     // workspace plan (byte offsets)
     size_t ws_report = 0, ws_state = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
            ws_fintot = 0, ws_agg = 0;
@@ -121,7 +120,6 @@ int build_plan(lags_layout *lo)
     lo->linfo.resize(L);
     uint32_t seg_base = 0;
     uint64_t slot_base = 0;
-    uint64_t tbin_base = 0;
     std::vector<MainWork> stream_work;
     lo->small_pre.assign(L + 1, 0);
     lo->stream_pre.assign(L + 1, 0);
@@ -186,9 +184,9 @@ int build_plan(lags_layout *lo)
             si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
             si.slot_hi = (uint32_t)(slot_base >> 32);
             si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
-            si.tbin_cap = std::max<uint32_t>(kTbinCap, (li.k + 7) / 8);
-            si.tbin_base = (uint32_t)tbin_base;
-            tbin_base += si.tbin_cap;
+            // every candidate the layer can store fits its threshold-bin list,
+            // so a large bin (many equal keys) never forces the exact path
+            si.tbin_cap = si.nseg * si.cap;
             si.fin_first = (uint32_t)lo->fin_work.size();
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
             for (uint32_t t = 0; t < li.ntiles; ++t) {
@@ -219,7 +217,6 @@ int build_plan(lags_layout *lo)
                 f.n = li.n;
                 f.moff = li.moff;
                 f.k = li.k;
-                f.tbin_base = si.tbin_base;
                 f.tbin_cap = si.tbin_cap;
                 f.a4 = si.a4;
                 lo->fin_work.push_back(f);
@@ -236,7 +233,6 @@ int build_plan(lags_layout *lo)
     lo->main_work = stream_work;
     lo->nseg_total = seg_base;
     lo->slots_total = slot_base;
-    lo->tbin_total = tbin_base;
     // layer of every kStartsBlock-th message position (the aggregate's start pass)
     const uint64_t npb = (lo->K + 1 + kStartsBlock - 1) / kStartsBlock;
     lo->pos_layer.resize(npb);
@@ -259,7 +255,7 @@ int build_plan(lags_layout *lo)
     lo->ws_slots = at;
     at = align_up(at + (size_t)lo->slots_total * 8, kAlign);
     lo->ws_tbin = at;
-    at = align_up(at + (size_t)lo->tbin_total * 8, kAlign);
+    at = align_up(at + (size_t)lo->slots_total * 8, kAlign);   // same offsets as the slots
     lo->ws_fintot = at;
     at = align_up(at + lo->fin_work.size() * 4, kAlign);
     lo->ws_agg = at;

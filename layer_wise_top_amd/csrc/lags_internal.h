@@ -69,8 +69,9 @@ struct SampledInfo {      // one per sampled layer, device table
     uint32_t force_exact; // ratio too large for a guess: exact path
     uint32_t fin_nblocks; // finishing workgroups of this layer
     uint32_t fin_first;   // index of the layer's first finishing workgroup
-    uint32_t tbin_base;   // first threshold-bin entry of the layer in the workspace
-    uint32_t tbin_cap;    // threshold-bin entries kept (max(kTbinCap, k/8))
+    uint32_t tbin_cap;    // threshold-bin entries the layer can keep: all its slots
+                          // (the list sits at the layer's slot offset in its own region)
+    uint32_t pad;
 };
 
 // One entry per k_main workgroup: everything a streaming tile needs, so one
@@ -101,7 +102,7 @@ struct FinWork {
     uint32_t fin_first;   // first finishing workgroup of the layer
     uint32_t off, n;      // the layer's entries
     uint32_t moff, k;     // the layer's message
-    uint32_t tbin_base, tbin_cap;
+    uint32_t tbin_cap, pad0;
     uint32_t a4;          // 4-aligned start of the layer's interior
     uint32_t pad;
 };

@@ -205,11 +205,21 @@ __device__ uint32_t block_radix_select(const Val &val, const Match &match, uint3
         const uint32_t top = sh + widths[lev];   // bits above this digit: [top, 32)
         for (uint32_t b = threadIdx.x; b < nb; b += kBlock) hist[b] = 0;
         __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n; i += kBlock) {
-            if (!match(i)) continue;
-            const uint32_t v = val(i);
-            const bool same = (top >= 32u) ? true : ((v >> top) == (prefix >> top));
-            if (same) atomicAdd(&hist[(v >> sh) & (nb - 1)], 1u);
+        // four items per thread per round: their loads are in flight together
+        for (uint32_t i0 = threadIdx.x; i0 < n; i0 += 4u * kBlock) {
+            uint32_t v[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = i0 + (uint32_t)u * kBlock;
+                ok[u] = i < n && match(i);
+                v[u] = ok[u] ? val(i) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool same = (top >= 32u) ? true : ((v[u] >> top) == (prefix >> top));
+                if (ok[u] && same) atomicAdd(&hist[(v[u] >> sh) & (nb - 1)], 1u);
+            }
         }
         __syncthreads();
         block_find_rank(hist, nb < (uint32_t)kBlock ? (uint32_t)kBlock : nb, rank, res, tmp);
@@ -711,7 +721,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
         uint32_t base = 0;
         if (ln == 0) base = atomicAdd(&st->tbin_n, wt);
         uint32_t t = __shfl(base, 0, 64) + incl - nt;
-        uint2 *tb = a.tbin + f.tbin_base;
+        uint2 *tb = a.tbin + (((uint64_t)f.slot_hi << 32) | f.slot_lo);
         for (int i = 0; i < kSegsPerWave; ++i) {
             if (!ws.valid(i)) continue;
             const uint32_t cnt = ws.cnt[i];
@@ -818,7 +828,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     // resolve the threshold inside bin bstar: in LDS when the bin fits,
     // otherwise straight from the workspace
     const uint32_t need = L.k - st->c_above;
-    const uint2 *tb = a.tbin + S.tbin_base;
+    const uint2 *tb = a.tbin + (((uint64_t)S.slot_hi << 32) | S.slot_lo);
     uint32_t T, idx_cut;
     if (h <= kTbinCap) {
         for (uint32_t p = threadIdx.x; p < h; p += kBlock) {

@@ -241,6 +241,25 @@ def test_large_threshold_bin(oracle):
     assert rep["layers_exact"] == 0 and rep["layers_wide_bin"] == 1, rep
 
 
+def test_threshold_bin_of_many_equal_keys(oracle):
+    """Thousands of entries share the threshold key, spread thinly enough that
+    no segment runs out of candidate slots: the threshold bin far exceeds the
+    LDS buffer and k/8, and is resolved from the workspace without the exact
+    fallback.  Repeated or bf16-valued gradients produce such bins."""
+    n = 2_000_003
+
+    def vals(s):
+        rng = np.random.default_rng(41 + s)
+        v = (0.25 * rng.standard_normal(n)).astype(np.float32)
+        v = np.clip(v, -0.9, 0.9)                          # everything else below 1.0
+        pos = rng.choice(n, 23_000, replace=False)
+        v[pos[:15_000]] = np.float32(2.0) * np.sign(rng.standard_normal(15_000)).astype(np.float32)
+        v[pos[15_000:]] = np.float32(1.0)                  # 8000 ties at the threshold
+        return v
+    rep = _single_layer_case(oracle, n, 1, 100, vals, P=2, steps=1)
+    assert rep["layers_exact"] == 0 and rep["layers_wide_bin"] == 1, rep
+
+
 def test_aggregate_rejects_invalid_messages(oracle):
     """Message entries that break the layout (an index outside its layer, an
     index beyond n, a descending pair, a duplicate) are skipped and counted;
