@@ -236,6 +236,30 @@ int lags_schedule_finish(int32_t L, const double *backward_time,
                          const int64_t *msg_bytes, double alpha, double beta,
                          const int32_t *bounds, int32_t nruns, double *finish);
 
+/*
+ * Adaptive per-layer message sizes (LAGS review, proposed method, bullets 2
+ * and 3: each layer's sparsification ratio adapts to that layer's
+ * communication-to-computation ratio so that layer-wise pipelined
+ * communication hides behind back-propagation).  Host only.
+ * Reading (the pages give no formula): while layer l's message is
+ * exchanged, back-propagation computes layer l-1 (backward_time[l-1]); an
+ * all-gather of k entries costs alpha + beta * B with B = 8 * (P - 1) * k
+ * bytes; k[l] is the largest k whose exchange fits that window,
+ *   floor((backward_time[l-1] - alpha) / (beta * (8 * (P - 1)))),
+ * kept in [ceil(n_l * rmin_num / rmin_den), n_l] (double arithmetic in that
+ * order, bounds in exact integers).  Layer 0 has no window and takes the
+ * lower bound; with P == 1 or beta == 0 every layer is sent whole.
+ *   layer_off:     host int64[L+1], 0 = layer_off[0] < ... < layer_off[L] < 2^40;
+ *   backward_time: host double[L], finite, >= 0;
+ *   P:             1..LAGS_MAX_WORKERS;  alpha, beta: finite, >= 0;
+ *   rmin_num/rmin_den: lower bound of the ratio, 1 <= num <= den;
+ *   k:             out, host int64[L], ready for lags_layout_create.
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_ERANGE.
+ */
+int lags_adaptive_k(int32_t L, const int64_t *layer_off, const double *backward_time,
+                    int32_t P, double alpha, double beta, int64_t rmin_num,
+                    int64_t rmin_den, int64_t *k);
+
 /* What the last calls that used a workspace did. */
 typedef struct lags_report {
     int32_t layers_sampled; /* layers on the sampled-threshold path in the last sparsify */

@@ -1,5 +1,7 @@
-// Merged-gradient message schedule (host only).
+// Host-only planning for layer-wise pipelining: the merged-gradient message
+// schedule and the adaptive per-layer message sizes.
 //
+// Merged-gradient message schedule.
 // MG-WFBP review, proposed method: the gradients of consecutive layers may be
 // merged into one message so that fewer messages pay the start-up cost; the
 // schedule that minimises the iteration time is found once, before training,
@@ -154,6 +156,53 @@ int lags_schedule_finish(int32_t L, const double *backward_time, const int64_t *
         *finish = link_free;
     } catch (const std::bad_alloc &) {
         return LAGS_ENOMEM;
+    }
+    return LAGS_OK;
+}
+
+// Adaptive per-layer message sizes (LAGS review, proposed method, bullets 2
+// and 3: each layer's ratio follows its communication-to-computation ratio,
+// so that pipelined communication hides behind back-propagation).  Plain
+// reading, the pages giving no formula: while layer l is exchanged, the
+// backward pass computes layer l-1, which takes backward_time[l-1]; an
+// all-gather of k entries (8 bytes each, P - 1 messages received) costs
+// alpha + beta * 8 * (P - 1) * k; k[l] is the largest k that fits, kept in
+// [ceil(n_l * rmin_num / rmin_den), n_l].  Layer 0 has no window and takes
+// the lower bound; with P == 1 or beta == 0 nothing is exchanged and every
+// layer is sent whole.
+int lags_adaptive_k(int32_t L, const int64_t *layer_off, const double *backward_time, int32_t P,
+                    double alpha, double beta, int64_t rmin_num, int64_t rmin_den, int64_t *k)
+{
+    if (!layer_off || !backward_time || !k) return LAGS_EINVAL;
+    if (L < 1 || L > LAGS_MAX_LAYERS || P < 1 || P > LAGS_MAX_WORKERS) return LAGS_ERANGE;
+    if (!std::isfinite(alpha) || !std::isfinite(beta) || alpha < 0.0 || beta < 0.0) return LAGS_EINVAL;
+    if (rmin_num < 1 || rmin_den < 1 || rmin_num > rmin_den) return LAGS_EINVAL;
+    if (layer_off[0] != 0) return LAGS_EINVAL;
+    for (int32_t l = 0; l < L; ++l) {
+        if (layer_off[l + 1] <= layer_off[l]) return LAGS_EINVAL;
+        if (layer_off[l + 1] >= (int64_t(1) << 40)) return LAGS_ERANGE;
+        if (!std::isfinite(backward_time[l]) || backward_time[l] < 0.0) return LAGS_EINVAL;
+    }
+    const double per_entry = beta * (double)(8 * (int64_t)(P - 1));
+    for (int32_t l = 0; l < L; ++l) {
+        const int64_t n = layer_off[l + 1] - layer_off[l];
+        const int64_t lo = (int64_t)(((__int128)n * rmin_num + rmin_den - 1) / rmin_den);
+        int64_t kl;
+        if (per_entry == 0.0) {
+            kl = n;
+        } else if (l == 0) {
+            kl = lo;
+        } else {
+            const double budget = backward_time[l - 1] - alpha;
+            if (budget <= 0.0) {
+                kl = lo;
+            } else {
+                const double q = budget / per_entry;
+                const int64_t fit = (q >= (double)n) ? n : (int64_t)std::floor(q);
+                kl = fit < lo ? lo : (fit > n ? n : fit);
+            }
+        }
+        k[l] = kl;
     }
     return LAGS_OK;
 }

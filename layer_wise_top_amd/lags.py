@@ -27,7 +27,7 @@ EXPORTED = (
     "lags_layout_msg_offset", "lags_workspace_bytes", "lags_sparsify_layers",
     "lags_aggregate_apply", "lags_workspace_report", "lags_trace_enable",
     "lags_trace_read", "lags_num_kernels", "lags_kernel_name", "lags_sparsify_range",
-    "lags_aggregate_range", "lags_merge_schedule", "lags_schedule_finish",
+    "lags_aggregate_range", "lags_merge_schedule", "lags_schedule_finish", "lags_adaptive_k",
 )
 
 
@@ -87,6 +87,8 @@ def lib():
                                       ctypes.POINTER(f64)]
     L.lags_schedule_finish.restype = ctypes.c_int
     L.lags_schedule_finish.argtypes = [i32, vp, vp, f64, f64, vp, i32, ctypes.POINTER(f64)]
+    L.lags_adaptive_k.restype = ctypes.c_int
+    L.lags_adaptive_k.argtypes = [i32, vp, vp, i32, f64, f64, i64, i64, vp]
     L.lags_workspace_report.restype = ctypes.c_int
     L.lags_workspace_report.argtypes = [vp, vp, sz, vp, ctypes.POINTER(Report)]
     L.lags_trace_enable.restype = ctypes.c_int
@@ -277,6 +279,21 @@ def lags_schedule_finish(backward_time, msg_bytes, alpha: float, beta: float, ru
                                     bounds.ctypes.data, len(runs), ctypes.byref(fin))
     _check("lags_schedule_finish", rc)
     return fin.value
+
+
+def lags_adaptive_k(off, backward_time, P: int, alpha: float, beta: float,
+                    rmin=(1, 1000)) -> np.ndarray:
+    """Per-layer k from each layer's overlap window (int64 [L])."""
+    off = np.ascontiguousarray(off, dtype=np.int64)
+    bt = np.ascontiguousarray(backward_time, dtype=np.float64)
+    L = off.size - 1
+    if bt.shape != (L,):
+        raise ValueError("backward_time must have one entry per layer")
+    k = np.empty(L, dtype=np.int64)
+    rc = lib().lags_adaptive_k(L, off.ctypes.data, bt.ctypes.data, int(P), float(alpha),
+                               float(beta), int(rmin[0]), int(rmin[1]), k.ctypes.data)
+    _check("lags_adaptive_k", rc)
+    return k
 
 
 def lags_workspace_report(layout: Layout, ws, stream=None) -> dict:

@@ -12,6 +12,7 @@ import pytest
 
 from gpu_helpers import GpuRunner, assert_bits_equal, to_dev, to_np_f32
 from layer_wise_top_amd import workloads as W
+from oracle import ratio_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +150,32 @@ def test_disjoint_ranges_on_two_streams(oracle):
     main.wait_stream(s2)
     torch.cuda.synchronize()
     _compare("two streams", run, r_d, w_d, _expect(oracle, off, k, g, r, w, oi, ov, 0.1))
+
+
+def test_adaptive_sizes_then_pipelined_ranges(oracle):
+    """VGG-16 with per-layer sizes from lags_adaptive_k (backward time
+    proportional to tensor size, synthetic) and the step issued per range of
+    the merged-message schedule, last range first: the oracle's results."""
+    import torch
+    from layer_wise_top_amd import lags
+    wl = W.get("vgg16")
+    off = wl.offsets()
+    c = np.diff(off) * 66e-12
+    k = lags.lags_adaptive_k(off, c, wl.P, 20e-6, 1.0 / 50e9, (1, 1000))
+    assert k.tolist() == ratio_oracle.adaptive_k(np.diff(off).tolist(), c.tolist(), wl.P, 20e-6,
+                                                 1.0 / 50e9, 1, 1000)
+    runs, _ = lags.lags_merge_schedule(c, 8 * (wl.P - 1) * k, 20e-6, 1.0 / 50e9)
+    _say(f"[vgg16 adaptive] K={int(k.sum())} runs={len(runs)}")
+    P = wl.P
+    run = GpuRunner(off, k, P)
+    g = W.gen_grad(wl, 0)
+    w = W.gen_weights(wl)
+    r = np.zeros(wl.n, np.float32)
+    oi, ov = W.gen_messages(wl, 0, k)
+    run.set_others(oi, ov)
+    g_d, r_d, w_d = to_dev(g), to_dev(r), to_dev(w)
+    for l0, l1 in runs:
+        lags.lags_sparsify_range(run.layout, l0, l1, g_d, r_d, run.msg_idx[0], run.msg_val[0], run.ws)
+        lags.lags_aggregate_range(run.layout, l0, l1, w_d, run.msg_idx, run.msg_val, P, wl.lr, run.ws)
+    torch.cuda.synchronize()
+    _compare("vgg16 adaptive", run, r_d, w_d, _expect(oracle, off, k, g, r, w, oi, ov, wl.lr))
