@@ -319,6 +319,34 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
         e1.record(stream)
         torch.cuda.synchronize()
         per_layer = [(l, l + 1) for l in range(wl.L - 1, -1, -1)]
+        # the same, with per-layer sizes from each layer's overlap window
+        k_ad = lags.lags_adaptive_k(off, backward, P, alpha, beta, (1, 1000))
+        runs_ad, _ = lags.lags_merge_schedule(backward, (P - 1) * 8 * k_ad, alpha, beta)
+        lay_ad = lags.Layout(off, k_ad)
+        oi, ov = W.gen_messages(wl, 0, k_ad)
+        mi_ad = torch.empty((P, lay_ad.K), dtype=torch.int32, device=dev)
+        mv_ad = torch.empty((P, lay_ad.K), dtype=torch.float32, device=dev)
+        if P > 1:
+            mi_ad[1:].copy_(torch.from_numpy(oi.view(np.int32)))
+            mv_ad[1:].copy_(torch.from_numpy(ov))
+        del oi, ov
+        ws_ad = lags.workspace(lay_ad, P, device=dev)
+
+        def piped_ad():
+            for l0, l1 in runs_ad:
+                lags.lags_sparsify_range(lay_ad, l0, l1, g_d, r_d, mi_ad[0], mv_ad[0], ws_ad, 0, stream)
+                lags.lags_aggregate_range(lay_ad, l0, l1, w_d, mi_ad, mv_ad, P, wl.lr, ws_ad, stream)
+
+        for _ in range(warmup):
+            piped_ad()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            piped_ad()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_ad = e0.elapsed_time(e1) / steps
+        del mi_ad, mv_ad, ws_ad
         out["pipeline"] = {
             "runs": len(runs), "ms_per_step": round(e0.elapsed_time(e1) / steps, 5),
             "model": "backward 66 ps/param, 50 us + all-gather bytes at 50 GB/s per message",
@@ -329,6 +357,8 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
                 "one_message": round(lags.lags_schedule_finish(backward, nbytes, alpha, beta,
                                                                [(0, wl.L)]) * 1e3, 4),
             },
+            "adaptive_k": {"sent_per_worker": int(k_ad.sum()), "runs": len(runs_ad),
+                           "ms_per_step": round(ms_ad, 5)},
         }
     del g_d, w_d, r_d, mi, mv, ws, scratch
     torch.cuda.empty_cache()

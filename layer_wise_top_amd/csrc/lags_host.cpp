@@ -52,8 +52,9 @@ struct lags_layout {
     std::vector<uint32_t> small_pre, stream_pre, sid_pre, fin_pre;
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
+    uint64_t hist_words = 0;
     // workspace plan (byte offsets)
-    size_t ws_report = 0, ws_state = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
+    size_t ws_report = 0, ws_state = 0, ws_hist = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
            ws_fintot = 0, ws_agg = 0;
     // device tables, built on first use
     std::mutex mu;
@@ -189,6 +190,12 @@ int build_plan(lags_layout *lo)
             si.tbin_cap = si.nseg * si.cap;
             si.fin_first = (uint32_t)lo->fin_work.size();
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
+            // histogram copies grow with the layer, so that the streaming
+            // workgroups' atomics on its hottest bins stay spread
+            si.hcopies = 1;
+            while (si.hcopies < kHistMaxCopies && si.hcopies * kTilesPerCopy < li.ntiles) si.hcopies *= 2;
+            si.hist_off = (uint32_t)lo->hist_words;
+            lo->hist_words += (uint64_t)si.hcopies * kNBins;
             for (uint32_t t = 0; t < li.ntiles; ++t) {
                 MainWork w = work((uint32_t)l, kClsSampled, t);
                 w.sid = li.sid;
@@ -201,6 +208,8 @@ int build_plan(lags_layout *lo)
                 w.cap = si.cap;
                 w.slot_lo = si.slot_lo;
                 w.slot_hi = si.slot_hi;
+                w.hist_off = si.hist_off;
+                w.hcopies = si.hcopies;
                 stream_work.push_back(w);
             }
             for (uint32_t b = 0; b < si.fin_nblocks; ++b) {
@@ -248,6 +257,8 @@ int build_plan(lags_layout *lo)
     at = align_up(at + kRepWords * 4, kAlign);
     lo->ws_state = at;
     at = align_up(at + ns * sizeof(SampledState), kAlign);
+    lo->ws_hist = at;
+    at = align_up(at + (size_t)lo->hist_words * 4, kAlign);
     lo->ws_segcount = at;
     at = align_up(at + (size_t)lo->nseg_total * 4, kAlign);
     lo->ws_segsel = at;
@@ -507,6 +518,7 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     a.fin_work = lo->d_fin;
     a.report = (uint32_t *)(w + lo->ws_report);
     a.state = (SampledState *)(w + lo->ws_state);
+    a.hist = (uint32_t *)(w + lo->ws_hist);
     a.seg_count = (uint32_t *)(w + lo->ws_segcount);
     a.seg_sel = (uint32_t *)(w + lo->ws_segsel);
     a.slots = (uint2 *)(w + lo->ws_slots);

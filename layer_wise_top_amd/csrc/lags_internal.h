@@ -19,7 +19,8 @@ constexpr uint32_t kDenseTile = 16384;   // entries per workgroup for k == n lay
 constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident)
 constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
 constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
-constexpr uint32_t kHistCopies = 8;      // copies of each layer's histogram (spread atomics)
+constexpr uint32_t kHistMaxCopies = 64;  // copies of a layer's histogram, at most (spread atomics)
+constexpr uint32_t kTilesPerCopy = 128;  // streaming workgroups per histogram copy, about
 constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LDS (larger: global)
 constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup
 // aggregate
@@ -71,7 +72,9 @@ struct SampledInfo {      // one per sampled layer, device table
     uint32_t fin_first;   // index of the layer's first finishing workgroup
     uint32_t tbin_cap;    // threshold-bin entries the layer can keep: all its slots
                           // (the list sits at the layer's slot offset in its own region)
-    uint32_t pad;
+    uint32_t hist_off;    // first word of the layer's histogram copies in the workspace
+    uint32_t hcopies;     // copies (a power of two), kNBins words each
+    uint32_t pad[3];
 };
 
 // One entry per k_main workgroup: everything a streaming tile needs, so one
@@ -87,7 +90,8 @@ struct MainWork {
     uint32_t seg_base;    // global id of the layer's segment 0
     uint32_t cap;         // candidate slots per segment
     uint32_t slot_lo, slot_hi;   // first slot of the layer
-    uint32_t pad[3];
+    uint32_t hist_off, hcopies;  // the layer's histogram copies
+    uint32_t pad;
 };
 
 // One entry per finishing workgroup (k_fin_select, k_fin_emit): its segments
@@ -119,7 +123,6 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t T;           // k-th largest key of the layer
     uint32_t idx_cut;     // largest global index taken among keys == T
     uint32_t pad[5];
-    uint32_t hist[kHistCopies * kNBins];   // copy c at [c * kNBins, (c + 1) * kNBins)
 };
 
 // report counters at the head of the workspace
@@ -136,6 +139,7 @@ struct SparsifyArgs {
     const FinWork *fin_work;  // one per finishing workgroup
     uint32_t *report;
     SampledState *state;
+    uint32_t *hist;           // candidate histograms (SampledInfo::hist_off, hcopies)
     uint32_t *seg_count;
     uint32_t *seg_sel;
     uint2 *slots;

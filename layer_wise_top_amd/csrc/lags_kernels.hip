@@ -18,8 +18,9 @@
 //                 compacted, in index order, into per-segment candidate
 //                 slots, and counted in the layer's histogram of bins above
 //                 G.  k == n layers are sent whole.
-//   k_fin_bins    one workgroup per sampled layer: finds the histogram bin
-//                 holding the k-th largest candidate.
+//   k_fin_bins    one workgroup per sampled layer: sums the layer's
+//                 histogram copies and finds the bin holding the k-th largest
+//                 candidate.
 //   k_fin_select  counts, per segment, candidates above the threshold bin and
 //                 gathers the threshold bin's candidates.
 //   k_fin_resolve one workgroup per sampled layer: resolves the exact
@@ -327,6 +328,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     SampledState *st = a.state + sid;
     uint32_t *stw = reinterpret_cast<uint32_t *>(st);
     for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += NT) stw[t] = 0;
+    uint32_t *lh = a.hist + S.hist_off;
+    for (uint32_t t = threadIdx.x; t < S.hcopies * kNBins; t += NT) lh[t] = 0;
     for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
     __syncthreads();
     if (S.force_exact || a.force_exact) {
@@ -467,7 +470,7 @@ struct CandWriter {
 // in index order to the segment's candidate slots.  Rows of 2 x 64 float4 per
 // iteration (measured fastest on gfx950 for this loop).
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
-                                SampledState *st, uint32_t hcopy, uint2 *stage)
+                                SampledState *st, uint32_t *hist, uint2 *stage)
 {
     constexpr int U = 2;
     const uint32_t ln = lane_id();
@@ -492,7 +495,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         }
     }
     const uint32_t G = st->G;
-    CandWriter cw{a.slots + slot0, stage, st->hist + hcopy, G, st->SH, w.cap, 0u, 0u, ln};
+    CandWriter cw{a.slots + slot0, stage, hist, G, st->SH, w.cap, 0u, 0u, ln};
     uint32_t idx[4];
     float v[4];
 
@@ -573,10 +576,10 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 
     if (w.cls == kClsSampled) {   // streaming tile w.tile: one segment per wave
         const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
-        // workgroups land on the XCDs round-robin: one histogram copy per XCD
-        // keeps the atomics on each bin spread
+        // consecutive workgroups take consecutive histogram copies
         if (seg < w.nseg)
-            sampled_segment(a, w, seg, a.state + w.sid, (blockIdx.x % kHistCopies) * kNBins,
+            sampled_segment(a, w, seg, a.state + w.sid,
+                            a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins,
                             stage[threadIdx.x >> 6]);
         return;
     }
@@ -605,20 +608,40 @@ __device__ __forceinline__ uint32_t seg_of(const FinWork &f, uint32_t i)
     return min((i - f.a4) / kSeg, f.nseg - 1u);
 }
 
-// Locate the candidate bin that holds the k-th largest, or mark the layer for
-// the exact path (too few candidates, or a segment ran out of slots).
-__device__ void finalize_hist(const SparsifyArgs &a, const LayerInfo &L, SampledState *st,
-                              uint32_t *hist, uint32_t *tmp, uint32_t *res)
+// k_fin_bins: one 1024-thread workgroup per sampled layer, after the
+// streaming pass has filled the layer's histogram copies.  Sums the copies
+// (eight loads in flight per thread), then locates the candidate bin that
+// holds the k-th largest, or marks the layer for the exact path (too few
+// candidates, or a segment ran out of slots).
+constexpr int kBinsThreads = 1024;
+
+__global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
 {
+    constexpr int NT = kBinsThreads;
+    __shared__ uint32_t hist[kNBins];
+    __shared__ uint32_t tmp[NT / 64];
+    __shared__ uint32_t res[2];
+    if (blockIdx.x >= a.nsampled) return;
+    const uint32_t sid = a.sample_base + blockIdx.x;
+    const SampledInfo S = a.sinfo[sid];
+    const LayerInfo L = a.linfo[S.layer];
+    SampledState *st = a.state + sid;
+    const uint32_t *lh = a.hist + S.hist_off;
     uint32_t part = 0;
-    for (uint32_t b = threadIdx.x; b < kNBins; b += kBlock) {
+    for (uint32_t b = threadIdx.x; b < kNBins; b += NT) {
         uint32_t h = 0;
-        for (uint32_t c = 0; c < kHistCopies; ++c) h += st->hist[c * kNBins + b];
+        for (uint32_t c0 = 0; c0 < S.hcopies; c0 += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) v[u] = (c0 + u < S.hcopies) ? lh[(c0 + u) * kNBins + b] : 0u;
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) h += v[u];
+        }
         hist[b] = h;
         part += h;
     }
     uint32_t C;
-    block_excl_scan(part, tmp, C);    // also orders the LDS writes above
+    block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above
     if (C < L.k || st->overflow) {
         if (threadIdx.x == 0) {
             st->status = kStExact;
@@ -627,27 +650,13 @@ __device__ void finalize_hist(const SparsifyArgs &a, const LayerInfo &L, Sampled
         }
         return;
     }
-    block_find_rank(hist, kNBins, L.k, res, tmp);
+    block_find_rank<NT>(hist, kNBins, L.k, res, tmp);
     if (threadIdx.x == 0) {
         st->bstar = res[0];
         st->c_above = res[1];
         st->status = kStOk;
         atomicAdd(&a.report[kRepSampled], 1u);
     }
-}
-
-// k_fin_bins: one workgroup per sampled layer, after the streaming pass has
-// filled the layer's histogram.
-__global__ __launch_bounds__(kBlock) void k_fin_bins(SparsifyArgs a)
-{
-    __shared__ uint32_t hist[kNBins];
-    __shared__ uint32_t tmp[kWaves];
-    __shared__ uint32_t res[2];
-    if (blockIdx.x >= a.nsampled) return;
-    const uint32_t sid = a.sample_base + blockIdx.x;
-    const SampledInfo S = a.sinfo[sid];
-    const LayerInfo L = a.linfo[S.layer];
-    finalize_hist(a, L, a.state + sid, hist, tmp, res);
 }
 
 // The segments a wave handles in a finishing workgroup, with their candidate
@@ -1162,7 +1171,7 @@ hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 
 hipError_t launch_fin_bins(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_fin_bins, dim3(nblocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_fin_bins, dim3(nblocks), dim3(kBinsThreads), 0, s, a);
     return hipGetLastError();
 }
 
