@@ -318,6 +318,7 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
             piped()
         e1.record(stream)
         torch.cuda.synchronize()
+        ms_piped = e0.elapsed_time(e1) / steps
         per_layer = [(l, l + 1) for l in range(wl.L - 1, -1, -1)]
         # the same, with per-layer sizes from each layer's overlap window
         k_ad = lags.lags_adaptive_k(off, backward, P, alpha, beta, (1, 1000))
@@ -348,7 +349,7 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
         ms_ad = e0.elapsed_time(e1) / steps
         del mi_ad, mv_ad, ws_ad
         out["pipeline"] = {
-            "runs": len(runs), "ms_per_step": round(e0.elapsed_time(e1) / steps, 5),
+            "runs": len(runs), "ms_per_step": round(ms_piped, 5),
             "model": "backward 66 ps/param, 50 us + all-gather bytes at 50 GB/s per message",
             "modelled_comm_finish_ms": {
                 "merged": round(finish * 1e3, 4),
