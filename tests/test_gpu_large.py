@@ -1,5 +1,6 @@
 """Full-size parity on the 1.3B-parameter transformer gradient (the benchmark's
-workload, in the benchmark's launch configuration).
+workload, in the benchmark's launch configuration), layer-wise and as one
+whole-model layer.
 
 The oracle recomputes a sample of layers one by one (every layer's selection
 depends only on that layer): the 103M-entry embedding, all eight tensors of
@@ -101,3 +102,75 @@ def test_tfm1p3b_full_size(oracle):
         ai[0, moff[l + 1]:] = 0xFFFFFFFF
         w_o = oracle.aggregate(ai, av, w0[a:b], wl.lr, lo=a, hi=b)
         assert_bits_equal(f"layer {l} weights", w_h[a:b], w_o)
+
+
+@pytest.mark.timeout(1200)
+def test_slgs1p3b_full_size(oracle):
+    """Whole-model selection (SLGS-SGD): the same 1.31B entries as one layer.
+    The oracle's sort cannot take 1.31B keys in a test, so the expected
+    selection comes from its definition evaluated on the host with a library
+    partition (the k-th largest key, then the lowest-index ties): the GPU must
+    send exactly that set, with the residual and value bits it implies, and
+    its weights must match the oracle's aggregate on three windows of one
+    million indices (worker 0's entries there taken from the host
+    selection)."""
+    import torch
+    wl = W.get("slgs1p3b")
+    off = wl.offsets()
+    num, den = wl.ratios()
+    k = oracle.k_for_ratio(np.diff(off), num, den)
+    P = wl.P
+    K = int(k[0])
+    _say("generating inputs")
+    g = W.gen_grad(wl, 0)
+    w0 = W.gen_weights(wl)
+    oi, ov = W.gen_messages(wl, 0, k)
+    run = GpuRunner(off, k, P)
+    g_d = to_dev(g)
+    r_d = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
+    w_d = to_dev(w0)
+    w0_d = w_d.clone()
+    run.set_others(oi, ov)
+    _say("running one step")
+    run.sparsify(g_d, r_d)
+    run.aggregate(w_d, wl.lr)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["layers_exact"] == 0 and rep["bad_entries"] == 0, rep
+
+    _say("host selection (acc = grad: the residual starts at zero)")
+    key_h = g.view(np.int32) & np.int32(0x7FFFFFFF)
+    T = int(np.partition(key_h, wl.n - K)[wl.n - K])       # the K-th largest key
+    above = np.flatnonzero(key_h > T)
+    tied = np.flatnonzero(key_h == T)
+    e = K - above.size
+    assert 1 <= e <= tied.size
+    sel = np.sort(np.concatenate([above, tied[:e]])).astype(np.uint32)
+    del key_h, above, tied
+
+    _say("message, residual and untouched weights")
+    assert_bits_equal("msg_idx", to_np_u32(run.msg_idx[0, :K]), sel)
+    assert_bits_equal("msg_val", to_np_f32(run.msg_val[0, :K]), g[sel])
+    sel_d = to_dev(sel).long() & 0xFFFFFFFF
+    sent = torch.zeros(wl.n, dtype=torch.bool, device="cuda")
+    sent[sel_d] = True
+    rb = r_d.view(torch.int32)
+    assert bool((rb[sent] == 0).all()) and bool((rb[~sent] == g_d.view(torch.int32)[~sent]).all())
+    del sent, sel_d
+    touched = torch.zeros(wl.n, dtype=torch.bool, device="cuda")
+    touched[run.msg_idx.reshape(-1).long() & 0xFFFFFFFF] = True
+    assert bool((w_d.view(torch.int32)[~touched] == w0_d.view(torch.int32)[~touched]).all())
+    del touched
+
+    _say("aggregate windows against the oracle")
+    ai = np.full((P, K), 0xFFFFFFFF, np.uint32)
+    av = np.zeros((P, K), np.float32)
+    ai[0] = sel
+    av[0] = g[sel]
+    ai[1:] = oi
+    av[1:] = ov
+    for a in (0, wl.n // 2, wl.n - 1_000_000):
+        b = a + 1_000_000
+        wi = np.where((ai >= a) & (ai < b), ai, np.uint32(0xFFFFFFFF))
+        w_o = oracle.aggregate(wi, av, w0[a:b], wl.lr, lo=a, hi=b)
+        assert_bits_equal(f"weights [{a}, {b})", to_np_f32(w_d[a:b]), w_o)
