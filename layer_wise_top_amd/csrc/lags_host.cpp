@@ -54,8 +54,8 @@ struct lags_layout {
     uint64_t slots_total = 0;
     uint64_t hist_words = 0;
     // workspace plan (byte offsets)
-    size_t ws_report = 0, ws_state = 0, ws_hist = 0, ws_segcount = 0, ws_segsel = 0, ws_slots = 0, ws_tbin = 0,
-           ws_fintot = 0, ws_agg = 0;
+    size_t ws_report = 0, ws_state = 0, ws_hist = 0, ws_segcount = 0, ws_segsel = 0,
+           ws_slots = 0, ws_tbin = 0, ws_fintot = 0, ws_fineq = 0, ws_agg = 0;
     // device tables, built on first use
     std::mutex mu;
     int device = -1;
@@ -268,6 +268,8 @@ int build_plan(lags_layout *lo)
     lo->ws_tbin = at;
     at = align_up(at + (size_t)lo->slots_total * 8, kAlign);   // same offsets as the slots
     lo->ws_fintot = at;
+    at = align_up(at + lo->fin_work.size() * 4, kAlign);
+    lo->ws_fineq = at;
     at = align_up(at + lo->fin_work.size() * 4, kAlign);
     lo->ws_agg = at;
     return LAGS_OK;
@@ -524,6 +526,7 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     a.slots = (uint2 *)(w + lo->ws_slots);
     a.tbin = (uint2 *)(w + lo->ws_tbin);
     a.fin_total = (uint32_t *)(w + lo->ws_fintot);
+    a.fin_eq = (uint32_t *)(w + lo->ws_fineq);
     a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
     a.sample_base = lo->sid_pre[l0];
     a.nsampled = lo->sid_pre[l1] - lo->sid_pre[l0];

@@ -44,6 +44,8 @@ enum : uint32_t {
     kStPending = 0,
     kStOk = 1,        // candidates hold the top k; threshold bin resolved
     kStExact = 2,     // the exact multi-pass path handled the layer
+    kStZero = 3,      // guess G = 0 and fewer than k nonzero keys: T = 0, all nonzero
+                      // entries plus the lowest-index zeros are sent
 };
 
 struct LayerInfo {        // one per layer, device table
@@ -145,6 +147,7 @@ struct SparsifyArgs {
     uint2 *slots;
     uint2 *tbin;
     uint32_t *fin_total;      // per finishing workgroup: count, then message offset
+    uint32_t *fin_eq;         // per finishing workgroup (zero mode): zeros, then zeros before it
     uint32_t nsampled;        // sampled layers in the launched range
     uint32_t force_exact;
     // the launched layer range, as offsets into the layout's work lists

@@ -467,8 +467,10 @@ struct CandWriter {
 
 // One wave streams one segment of a sampled layer: acc = grad + residual is
 // written back to the residual buffer, and entries with key >= G are appended
-// in index order to the segment's candidate slots.  Rows of 2 x 64 float4 per
-// iteration (measured fastest on gfx950 for this loop).
+// in index order to the segment's candidate slots.  When the guess is G = 0
+// (most of the layer may be zero), only nonzero keys are stored: the
+// segment's zeros are then its length minus its candidates.  Rows of 2 x 64
+// float4 per iteration (measured fastest on gfx950 for this loop).
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
                                 SampledState *st, uint32_t *hist, uint2 *stage)
 {
@@ -495,6 +497,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         }
     }
     const uint32_t G = st->G;
+    const uint32_t Gs = G ? G : 1u;           // stored candidates: key >= Gs
     CandWriter cw{a.slots + slot0, stage, hist, G, st->SH, w.cap, 0u, 0u, ln};
     uint32_t idx[4];
     float v[4];
@@ -507,7 +510,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         if (i < w.a4) {
             v[0] = a.grad[i] + a.res[i];
             a.res[i] = v[0];
-            if (key_of(v[0]) >= G) cm = 1;
+            if (key_of(v[0]) >= Gs) cm = 1;
         }
         cw.append(cm, idx, v);
     }
@@ -522,7 +525,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
                 __builtin_nontemporal_store(acc, r4 + q);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (key_of(acc[j]) >= G) cm |= 1u << j;
+                    if (key_of(acc[j]) >= Gs) cm |= 1u << j;
             }
             if (__ballot(cm != 0)) {
 #pragma unroll
@@ -533,6 +536,10 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
                 cw.append(cm, idx, v);
             }
         }
+        // let this iteration's stores drain before the next rows are
+        // requested: without the wait the pass measured ~3% slower (stores
+        // piling up behind the loads)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt untouched
         q0 += 64u * U;
         if (q0 >= q1) break;
 #pragma unroll
@@ -556,7 +563,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         if (i < w.end) {
             v[0] = a.grad[i] + a.res[i];
             a.res[i] = v[0];
-            if (key_of(v[0]) >= G) cm = 1;
+            if (key_of(v[0]) >= Gs) cm = 1;
         }
         cw.append(cm, idx, v);
     }
@@ -608,6 +615,18 @@ __device__ __forceinline__ uint32_t seg_of(const FinWork &f, uint32_t i)
     return min((i - f.a4) / kSeg, f.nseg - 1u);
 }
 
+// Entries of segment s of the layer (segment 0 also holds the unaligned head,
+// the last one the tail).
+__device__ __forceinline__ uint32_t seg_len(const FinWork &f, uint32_t s)
+{
+    const uint32_t end = f.off + f.n, b4 = end & ~3u;
+    const uint32_t lo = f.a4 + s * kSeg;
+    uint32_t len = min(lo + kSeg, b4) - lo;
+    if (s == 0) len += f.a4 - f.off;
+    if (s == f.nseg - 1u) len += end - b4;
+    return len;
+}
+
 // k_fin_bins: one 1024-thread workgroup per sampled layer, after the
 // streaming pass has filled the layer's histogram copies.  Sums the copies
 // (eight loads in flight per thread), then locates the candidate bin that
@@ -642,11 +661,22 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     }
     uint32_t C;
     block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above
-    if (C < L.k || st->overflow) {
+    if (st->overflow || (C < L.k && st->G != 0)) {
         if (threadIdx.x == 0) {
             st->status = kStExact;
             atomicAdd(&a.report[kRepSampled], 1u);
             atomicAdd(&a.report[kRepExact], 1u);
+        }
+        return;
+    }
+    if (C < L.k) {
+        // G = 0 and fewer than k nonzero keys: the k-th largest key is 0, so
+        // every stored (nonzero) candidate is sent, plus the k - C zeros of
+        // lowest index
+        if (threadIdx.x == 0) {
+            st->status = kStZero;
+            st->c_above = C;
+            atomicAdd(&a.report[kRepSampled], 1u);
         }
         return;
     }
@@ -697,13 +727,40 @@ struct WaveSegs {
 __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
 {
     __shared__ uint32_t wtot[kWaves];
+    __shared__ uint32_t wzero[kWaves];
     const FinWork f = a.fin_work[a.fin_base + blockIdx.x];
     SampledState *st = a.state + f.sid;
     const uint32_t ln = lane_id();
     const uint32_t wv = threadIdx.x >> 6;
     WaveSegs ws;
     ws.load(a, f, wv, ln);            // issued before the layer's status arrives
-    if (st->status != kStOk) return;  // the exact path takes the layer
+    const uint32_t status = st->status;   // uniform over the workgroup
+    if (status == kStZero) {
+        // every stored candidate is sent; count the workgroup's zeros
+        uint32_t wsum = 0, wz = 0;
+        for (int i = 0; i < kSegsPerWave; ++i) {
+            if (!ws.valid(i)) continue;
+            if (ln == 0) a.seg_sel[f.seg_base + ws.seg(i)] = ws.cnt[i];
+            wsum += ws.cnt[i];
+            wz += seg_len(f, ws.seg(i)) - ws.cnt[i];   // no overflow: every nonzero was stored
+        }
+        if (ln == 0) {
+            wtot[wv] = wsum;
+            wzero[wv] = wz;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t t = 0, z = 0;
+            for (int i = 0; i < kWaves; ++i) {
+                t += wtot[i];
+                z += wzero[i];
+            }
+            a.fin_total[a.fin_base + blockIdx.x] = t;
+            a.fin_eq[a.fin_base + blockIdx.x] = z;
+        }
+        return;
+    }
+    if (status != kStOk) return;      // the exact path takes the layer
     const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
     // pass 1: per segment, candidates above the threshold bin; per lane,
     // candidates in it
@@ -822,6 +879,35 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     const uint32_t status = st->status;
     const uint32_t h = st->tbin_n;
 
+    if (status == kStZero) {
+        // T = 0: the first e zeros (index order) are sent with every stored
+        // candidate.  Per finishing workgroup: zeros before it, zeros it
+        // sends, message offset.
+        const uint32_t e = L.k - st->c_above;
+        uint32_t zcarry = 0, carry = 0;
+        for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
+            const uint32_t b = base + threadIdx.x;
+            const bool in = b < S.fin_nblocks;
+            const uint32_t z = in ? a.fin_eq[S.fin_first + b] : 0u;
+            const uint32_t t = in ? a.fin_total[S.fin_first + b] : 0u;
+            uint32_t ztot, tot;
+            const uint32_t zpre = zcarry + block_excl_scan(z, tmp, ztot);
+            const uint32_t take = (zpre >= e) ? 0u : min(z, e - zpre);
+            const uint32_t ex = block_excl_scan(t + take, tmp, tot);
+            if (in) {
+                a.fin_total[S.fin_first + b] = carry + ex;
+                a.fin_eq[S.fin_first + b] = zpre;
+            }
+            zcarry += ztot;
+            carry += tot;
+        }
+        if (threadIdx.x == 0) {
+            st->T = 0;
+            st->idx_cut = e;          // zero mode: the number of zeros sent
+        }
+        return;
+    }
+
     if (status != kStOk || h > S.tbin_cap) {
         // the residual buffer holds acc for every entry of the layer
         if (threadIdx.x == 0) {
@@ -872,34 +958,129 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     }
 }
 
+// Zero mode, one segment by one wave: every nonzero entry of the segment and
+// its first ztake zeros (index order), re-read from the residual buffer
+// (which holds acc after the streaming pass), go to the message from
+// position base on; their residual becomes +0.0.
+__device__ void emit_rescan(const SparsifyArgs &a, const FinWork &f, uint32_t seg, uint32_t ztake,
+                            uint32_t base)
+{
+    const uint32_t ln = lane_id();
+    const uint32_t end = f.off + f.n;
+    const uint32_t b4 = end & ~3u;
+    const uint32_t mend = f.moff + f.k;
+    uint32_t run = 0, zrun = 0;
+    uint32_t idx[4];
+    float v[4];
+    // entries j of this lane with (valid >> j) & 1, in index order lane-major;
+    // wave-uniform call
+    auto group = [&](uint32_t valid) {
+        uint32_t zm = 0, nzm = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (valid & (1u << j)) {
+                if (key_of(v[j]) == 0u) zm |= 1u << j;
+                else nzm |= 1u << j;
+            }
+        }
+        uint32_t ztot, stot;
+        uint32_t zr = zrun + wave_prefix3((uint32_t)__popc(zm), ztot);
+        uint32_t sel = nzm;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (zm & (1u << j)) {
+                if (zr < ztake) sel |= 1u << j;
+                ++zr;
+            }
+        }
+        uint32_t pos = base + run + wave_prefix3((uint32_t)__popc(sel), stot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (sel & (1u << j)) {
+                if (pos < mend) {            // the layer's selection holds exactly k entries
+                    a.msg_idx[pos] = idx[j];
+                    a.msg_val[pos] = v[j];
+                }
+                a.res[idx[j]] = 0.0f;
+                ++pos;
+            }
+        }
+        run += stot;
+        zrun += ztot;
+    };
+    if (seg == 0 && f.off < f.a4) {          // unaligned head of the layer
+        const uint32_t i = f.off + ln;
+        idx[0] = i;
+        v[0] = (i < f.a4) ? a.res[i] : 0.0f;
+        group((i < f.a4) ? 1u : 0u);
+    }
+    const uint32_t q0 = (f.a4 + seg * kSeg) / 4u;
+    const uint32_t q1 = min(f.a4 + (seg + 1u) * kSeg, b4) / 4u;
+    const v4f *r4 = reinterpret_cast<const v4f *>(a.res);
+    for (uint32_t qb = q0; qb < q1; qb += 64u) {
+        const uint32_t q = qb + ln;
+        const v4f x = (q < q1) ? r4[q] : (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            idx[j] = 4u * q + j;
+            v[j] = x[j];
+        }
+        group((q < q1) ? 0xfu : 0u);
+    }
+    if (seg == f.nseg - 1 && b4 < end) {     // unaligned tail of the layer
+        const uint32_t i = b4 + ln;
+        idx[0] = i;
+        v[0] = (i < end) ? a.res[i] : 0.0f;
+        group((i < end) ? 1u : 0u);
+    }
+}
+
 // k_fin_emit: write the selected candidates of each segment, in index order,
-// and zero their residual.
+// and zero their residual.  In zero mode a segment that sends zeros is
+// re-read whole instead (its zeros were not stored).
 __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 {
     __shared__ uint32_t sbase[kFinSegs];
+    __shared__ uint32_t ztake[kFinSegs];
     const uint32_t fb = a.fin_base + blockIdx.x;
     const FinWork f = a.fin_work[fb];
     const SampledState *st = a.state + f.sid;
     const uint32_t ln = lane_id();
     WaveSegs ws;
     ws.load(a, f, threadIdx.x >> 6, ln);      // issued before the status arrives
+    const uint32_t status = st->status;       // uniform over the workgroup
+    if (status != kStOk && status != kStZero) return;
+    const bool zero = status == kStZero;
     static_assert(kFinSegs <= 64, "one wave scans the segment counts");
     const uint32_t s_end = min(f.seg0 + kFinSegs, f.nseg);
     if (threadIdx.x < 64) {
         const uint32_t s = f.seg0 + ln;
-        const uint32_t v = (s < s_end) ? a.seg_sel[f.seg_base + s] : 0u;
+        const bool in = s < s_end;
+        uint32_t v = in ? a.seg_sel[f.seg_base + s] : 0u;
+        uint32_t zt = 0;
+        if (zero) {
+            const uint32_t e = st->idx_cut;            // zeros the layer sends
+            const uint32_t z = in ? seg_len(f, s) - (v) : 0u;      // v = stored (nonzero) entries
+            const uint32_t zb = a.fin_eq[fb] + wave_incl_scan(z) - z;   // zeros before segment s
+            zt = (zb >= e) ? 0u : min(z, e - zb);
+            v += zt;
+        }
         const uint32_t incl = wave_incl_scan(v);
-        if (s < s_end) sbase[ln] = f.moff + a.fin_total[fb] + incl - v;
+        if (in) {
+            sbase[ln] = f.moff + a.fin_total[fb] + incl - v;
+            ztake[ln] = zt;
+        }
     }
-    if (st->status != kStOk) return;         // uniform over the workgroup
-    const uint32_t T = st->T, cut = st->idx_cut;
+    const uint32_t T = zero ? 0u : st->T, cut = zero ? 0u : st->idx_cut;
     const uint32_t mend = f.moff + f.k;
     __syncthreads();
+#pragma unroll
     for (int i = 0; i < kSegsPerWave; ++i) {
         if (!ws.valid(i)) continue;
+        const uint32_t base = sbase[ws.seg(i) - f.seg0];
+        if (zero && ztake[ws.seg(i) - f.seg0] != 0u) continue;   // re-read below
         const uint32_t cnt = ws.cnt[i];
         const uint2 *slots = ws.slots(a, f, i);
-        const uint32_t base = sbase[ws.seg(i) - f.seg0];
         uint32_t run = 0;
         for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
             const uint32_t p = p0 + ln;
@@ -922,6 +1103,12 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
                 a.res[c.x] = 0.0f;
             }
             run += (uint32_t)__popcll(m);
+        }
+    }
+    if (zero) {
+        for (uint32_t s = f.seg0 + (threadIdx.x >> 6); s < s_end; s += kWaves) {
+            const uint32_t zt = ztake[s - f.seg0];
+            if (zt != 0u) emit_rescan(a, f, s, zt, sbase[s - f.seg0]);
         }
     }
 }

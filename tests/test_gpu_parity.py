@@ -260,6 +260,42 @@ def test_threshold_bin_of_many_equal_keys(oracle):
     assert rep["layers_exact"] == 0 and rep["layers_wide_bin"] == 1, rep
 
 
+def test_mostly_zero_layers(oracle):
+    """Layers with fewer than k nonzero entries (sparse gradients): the k-th
+    largest key is 0, every nonzero entry is sent with the lowest-index zeros
+    (signed zeros keep their bits in the message), without the exact path."""
+    import zlib
+    sizes = [3_000_000, 200_000, 50_000, 20_000]
+    off = np.zeros(len(sizes) + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    n = int(off[-1])
+    num = np.array([1, 1, 1, 1])
+    den = np.array([1000, 1000, 100, 100])
+    k = oracle.k_for_ratio(np.diff(off), num, den)
+    P = 3
+    run = GpuRunner(off, k, P)
+    rng = np.random.default_rng(zlib.crc32(b"mostly zero"))
+    nonzero = [1000, 0, 49, int(k[3])]       # the last layer has exactly k nonzero entries
+    r = np.zeros(n, np.float32)
+    w = W.adversarial_values(17, n, "normal")
+    K = int(k.sum())
+    moff = np.concatenate([[0], np.cumsum(k)])
+    for step in range(2):
+        _progress(f"[mostly zero] step {step}")
+        g = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        for l, m in enumerate(nonzero):
+            pos = off[l] + rng.choice(sizes[l], m, replace=False)
+            g[pos] = rng.standard_normal(m).astype(np.float32)
+        oi = np.empty((P - 1, K), np.uint32)
+        ov = rng.standard_normal((P - 1, K)).astype(np.float32)
+        for p in range(P - 1):
+            for l in range(len(sizes)):
+                oi[p, moff[l]:moff[l + 1]] = np.sort(rng.choice(sizes[l], int(k[l]), replace=False)) + off[l]
+        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, tag=f"mostly zero/{step}")
+        rep = run.report()
+        assert rep["layers_exact"] == 0, rep
+
+
 def test_aggregate_rejects_invalid_messages(oracle):
     """Message entries that break the layout (an index outside its layer, an
     index beyond n, a descending pair, a duplicate) are skipped and counted;
