@@ -151,9 +151,13 @@ int lags_sparsify_layers(const lags_layout *layout, const float *grad,
  *   msg_val: device fp32[P][K];
  *   P:       1..LAGS_MAX_WORKERS;  lr: learning rate (s = lr / P in fp32);
  *   ws:      device workspace of ws_bytes >= lags_workspace_bytes(layout, P).
- * A message entry that breaks the layout (index outside its layer, or not
- * ascending) is skipped and counted in lags_report.bad_entries; it can never
- * cause an out-of-bounds access.
+ * Messages that break the layout (an index outside its layer, indices not
+ * strictly ascending) never cause an out-of-bounds access and never change
+ * the weights of another layer: an entry found outside the index chunk it
+ * is summed in (every entry outside its layer, and out-of-order entries that
+ * land outside their chunk) is skipped and counted in
+ * lags_report.bad_entries; the weights of a layer with malformed entries are
+ * otherwise unspecified (e.g. for a repeated index).
  * Returns LAGS_OK, LAGS_EINVAL, LAGS_ERANGE (P), LAGS_EWORKSPACE,
  * LAGS_EDEVICE, LAGS_EHIP, LAGS_ENOMEM (first use with this P: device tables).
  */

@@ -14,10 +14,11 @@
 //                 layer exceed with overwhelming probability; also clears the
 //                 layer's per-call state.
 //   k_main        the streaming pass: acc = grad + residual is written back
-//                 to the residual buffer; entries with |acc| key >= G are
-//                 compacted, in index order, into per-segment candidate
-//                 slots, and counted in the layer's histogram of bins above
-//                 G.  k == n layers are sent whole.
+//                 to the residual buffer; entries with |acc| key >= G (>= 1
+//                 when G = 0: zeros are not stored) are compacted, in index
+//                 order, into per-segment candidate slots, and counted in the
+//                 layer's histogram of bins above G.  k == n layers are sent
+//                 whole.
 //   k_fin_bins    one workgroup per sampled layer: sums the layer's
 //                 histogram copies and finds the bin holding the k-th largest
 //                 candidate.
@@ -31,7 +32,10 @@
 //                 small layer (<= 4096 entries) does that layer start to
 //                 finish (exact radix select in LDS).
 //   k_fin_emit    writes the selected candidates of each segment, in index
-//                 order, to the message and zeroes their residual.
+//                 order, to the message and zeroes their residual.  A layer
+//                 with fewer than k nonzero keys (G = 0, "zero mode") sends
+//                 every nonzero entry and its lowest-index zeros; segments
+//                 that send zeros are re-read from the residual buffer.
 //   k_agg_starts  for every worker, where each index chunk starts in its
 //                 message (messages ascend per layer).
 //   k_agg         one workgroup per index chunk: worker-ordered sums in an LDS
@@ -53,21 +57,18 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Cross-workgroup handoff inside one kernel.  The L2 of each XCD is not
-// coherent with the others for plain stores, and an agent-scope fence writes
-// back and invalidates the whole L2, which costs far more than the data
-// involved.  So data that another workgroup reads within the same kernel is
-// written with agent-scope atomics (stores with sc1, or read-modify-writes),
-// read with agent-scope atomic loads, and a writer waits for its own memory
-// operations to complete before it bumps the completion counter.
+// Memory ordering.  No kernel hands data from one workgroup to another while
+// both run: every such dependency is a kernel boundary (the histogram filled
+// by k_main's atomics is read by k_fin_bins, and so on).  The one ordering
+// inside a workgroup that plain program order does not give is k_fin_resolve
+// reading counters its own threads just incremented with device atomics: each
+// thread waits for its memory operations to complete, the workgroup meets at a
+// barrier, and the counters are then read with device-scope atomic loads.  No
+// agent-scope fence is used: on gfx950 it writes back and invalidates the
+// whole L2 of the XCD.
 __device__ __forceinline__ uint32_t ld_coherent(const uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void st_coherent(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void wait_mem_done()
