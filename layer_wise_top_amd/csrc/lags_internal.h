@@ -117,7 +117,7 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t G;           // guess: candidates have key >= G
     uint32_t SH;          // histogram bin width 2^SH above G
     uint32_t status;
-    uint32_t overflow;    // a segment had more candidates than slots
+    uint32_t spare;
     uint32_t bstar;       // histogram bin holding the k-th largest candidate
     uint32_t c_above;     // candidates in bins above bstar
     uint32_t reserved[2];

@@ -414,9 +414,9 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
 
 // Candidates of one segment, in index order.  They are staged in the wave's
 // LDS buffer and written to the segment's slots in contiguous bursts: isolated
-// 8-byte stores would each cost a partial-line write in memory.  Every stored
-// candidate is also counted in the layer's bin histogram (device atomics; a
-// few per segment).
+// 8-byte stores would each cost a partial-line write in memory.  Every
+// candidate, stored or beyond the segment's slots, is also counted in the
+// layer's bin histogram (device atomics; a few per segment).
 constexpr uint32_t kStage = 256;   // per wave; one row holds at most 4 x 64 candidates
 
 struct CandWriter {
@@ -437,11 +437,9 @@ struct CandWriter {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         for (uint32_t t = ln; t < n; t += 64) {
             const uint32_t pos = flushed + t;
-            if (pos < cap) {
-                const uint2 c = stage[t];
-                slots[pos] = c;
-                atomicAdd(&hist[cand_bin(c.y & 0x7fffffffu, G, SH)], 1u);
-            }
+            const uint2 c = stage[t];
+            if (pos < cap) slots[pos] = c;      // a full segment is re-read later
+            atomicAdd(&hist[cand_bin(c.y & 0x7fffffffu, G, SH)], 1u);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         flushed = run;
@@ -478,7 +476,7 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
     constexpr int U = 2;
     const uint32_t ln = lane_id();
     const uint32_t e0 = w.a4 + seg * kSeg;
-    const uint32_t e1 = min(e0 + kSeg, w.b4);
+    const uint32_t e1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4);
     const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * w.cap;
     const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
     v4f *r4 = reinterpret_cast<v4f *>(a.res);
@@ -569,10 +567,9 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         cw.append(cm, idx, v);
     }
     cw.flush();
-    if (ln == 0) {
-        a.seg_count[w.seg_base + seg] = cw.run;
-        if (cw.run > w.cap) atomicOr(&st->overflow, 1u);   // the layer takes the exact path
-    }
+    // all candidates, also those beyond the slots: the finishing kernels
+    // re-read a segment whose count exceeds its slots
+    if (ln == 0) a.seg_count[w.seg_base + seg] = cw.run;
 }
 
 // Only the candidate staging buffers live in LDS; the launch sets residency.
@@ -622,7 +619,7 @@ __device__ __forceinline__ uint32_t seg_len(const FinWork &f, uint32_t s)
 {
     const uint32_t end = f.off + f.n, b4 = end & ~3u;
     const uint32_t lo = f.a4 + s * kSeg;
-    uint32_t len = min(lo + kSeg, b4) - lo;
+    uint32_t len = (uint32_t)min((uint64_t)lo + kSeg, (uint64_t)b4) - lo;
     if (s == 0) len += f.a4 - f.off;
     if (s == f.nseg - 1u) len += end - b4;
     return len;
@@ -631,8 +628,8 @@ __device__ __forceinline__ uint32_t seg_len(const FinWork &f, uint32_t s)
 // k_fin_bins: one 1024-thread workgroup per sampled layer, after the
 // streaming pass has filled the layer's histogram copies.  Sums the copies
 // (eight loads in flight per thread), then locates the candidate bin that
-// holds the k-th largest, or marks the layer for the exact path (too few
-// candidates, or a segment ran out of slots).
+// holds the k-th largest, or marks the layer for zero mode or (too few
+// candidates above a nonzero guess) for the exact path.
 constexpr int kBinsThreads = 1024;
 
 __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
@@ -662,7 +659,7 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     }
     uint32_t C;
     block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above
-    if (st->overflow || (C < L.k && st->G != 0)) {
+    if (C < L.k && st->G != 0) {
         if (threadIdx.x == 0) {
             st->status = kStExact;
             atomicAdd(&a.report[kRepSampled], 1u);
@@ -690,6 +687,51 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     }
 }
 
+// Walk segment seg of a sampled layer in index order, one wave: fn(valid,
+// idx, v) is called wave-uniformly for the unaligned head (segment 0), each
+// row of 64 float4 of the aligned interior, and the unaligned tail (last
+// segment); lane entries j with (valid >> j) & 1 are real.  Values come from
+// the residual buffer, which holds acc after the streaming pass.
+template <class F>
+__device__ void walk_segment(const SparsifyArgs &a, const FinWork &f, uint32_t seg, F &&fn)
+{
+    const uint32_t ln = lane_id();
+    const uint32_t end = f.off + f.n, b4 = end & ~3u;
+    uint32_t idx[4];
+    float v[4];
+    if (seg == 0 && f.off < f.a4) {
+        const uint32_t i = f.off + ln;
+        const bool in = i < f.a4;
+        idx[0] = idx[1] = idx[2] = idx[3] = i;
+        v[0] = in ? a.res[i] : 0.0f;
+        v[1] = v[2] = v[3] = 0.0f;
+        fn(in ? 1u : 0u, idx, v);
+    }
+    const uint32_t lo = f.a4 + seg * kSeg;
+    const uint32_t q0 = lo / 4u;
+    const uint32_t q1 = (uint32_t)min((uint64_t)lo + kSeg, (uint64_t)b4) / 4u;
+    const v4f *r4 = reinterpret_cast<const v4f *>(a.res);
+    for (uint32_t qb = q0; qb < q1; qb += 64u) {
+        const uint32_t q = qb + ln;
+        const bool in = q < q1;
+        const v4f x = in ? r4[q] : (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            idx[j] = 4u * q + j;
+            v[j] = x[j];
+        }
+        fn(in ? 0xfu : 0u, idx, v);
+    }
+    if (seg == f.nseg - 1u && b4 < end) {
+        const uint32_t i = b4 + ln;
+        const bool in = i < end;
+        idx[0] = idx[1] = idx[2] = idx[3] = i;
+        v[0] = in ? a.res[i] : 0.0f;
+        v[1] = v[2] = v[3] = 0.0f;
+        fn(in ? 1u : 0u, idx, v);
+    }
+}
+
 // The segments a wave handles in a finishing workgroup, with their candidate
 // counts and first 64 slots loaded up front so that one memory round trip
 // serves all of them.
@@ -698,7 +740,8 @@ struct WaveSegs {
     uint32_t s0;                      // first segment of the workgroup
     uint32_t wave;
     uint32_t send;                    // end of the workgroup's segments
-    uint32_t cnt[kSegsPerWave];
+    uint32_t raw[kSegsPerWave];       // candidates of the segment (may exceed its slots)
+    uint32_t cnt[kSegsPerWave];       // of those, stored
     uint2 first[kSegsPerWave];
     __device__ uint32_t seg(int i) const { return s0 + wave + (uint32_t)i * kWaves; }
     __device__ bool valid(int i) const { return seg(i) < send; }
@@ -706,12 +749,12 @@ struct WaveSegs {
     {
         return a.slots + (((uint64_t)f.slot_hi << 32) | f.slot_lo) + (uint64_t)seg(i) * f.cap;
     }
+    __device__ bool full(int i) const { return raw[i] > cnt[i]; }   // re-read from acc
     __device__ void load(const SparsifyArgs &a, const FinWork &f, uint32_t wv, uint32_t ln)
     {
         s0 = f.seg0;
         wave = wv;
         send = min(f.seg0 + kFinSegs, f.nseg);
-        uint32_t raw[kSegsPerWave];
 #pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[f.seg_base + seg(i)] : 0u;
 #pragma unroll
@@ -737,13 +780,14 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     ws.load(a, f, wv, ln);            // issued before the layer's status arrives
     const uint32_t status = st->status;   // uniform over the workgroup
     if (status == kStZero) {
-        // every stored candidate is sent; count the workgroup's zeros
+        // every candidate (every nonzero entry) is sent; count the
+        // workgroup's zeros
         uint32_t wsum = 0, wz = 0;
         for (int i = 0; i < kSegsPerWave; ++i) {
             if (!ws.valid(i)) continue;
-            if (ln == 0) a.seg_sel[f.seg_base + ws.seg(i)] = ws.cnt[i];
-            wsum += ws.cnt[i];
-            wz += seg_len(f, ws.seg(i)) - ws.cnt[i];   // no overflow: every nonzero was stored
+            if (ln == 0) a.seg_sel[f.seg_base + ws.seg(i)] = ws.raw[i];
+            wsum += ws.raw[i];
+            wz += seg_len(f, ws.seg(i)) - ws.raw[i];
         }
         if (ln == 0) {
             wtot[wv] = wsum;
@@ -763,19 +807,36 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
     }
     if (status != kStOk) return;      // the exact path takes the layer
     const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
+    const uint32_t Gs = G ? G : 1u;           // candidates: key >= Gs
     // pass 1: per segment, candidates above the threshold bin; per lane,
-    // candidates in it
+    // candidates in it.  A segment with more candidates than slots is
+    // re-read from acc.
     uint32_t wsum = 0, nt = 0;
+#pragma unroll
     for (int i = 0; i < kSegsPerWave; ++i) {
         if (!ws.valid(i)) continue;
-        const uint32_t cnt = ws.cnt[i];
-        const uint2 *slots = ws.slots(a, f, i);
         uint32_t D = 0;
-        for (uint32_t p = ln; p < cnt; p += 64) {
-            const uint2 c = (p < 64) ? ws.first[i] : slots[p];
-            const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
-            D += (bin > bstar) ? 1u : 0u;
-            nt += (bin == bstar) ? 1u : 0u;
+        if (ws.full(i)) {
+            walk_segment(a, f, ws.seg(i), [&](uint32_t valid, const uint32_t *, const float *v) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t key = key_of(v[j]);
+                    if ((valid & (1u << j)) && key >= Gs) {
+                        const uint32_t bin = cand_bin(key, G, SH);
+                        D += (bin > bstar) ? 1u : 0u;
+                        nt += (bin == bstar) ? 1u : 0u;
+                    }
+                }
+            });
+        } else {
+            const uint32_t cnt = ws.cnt[i];
+            const uint2 *slots = ws.slots(a, f, i);
+            for (uint32_t p = ln; p < cnt; p += 64) {
+                const uint2 c = (p < 64) ? ws.first[i] : slots[p];
+                const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
+                D += (bin > bstar) ? 1u : 0u;
+                nt += (bin == bstar) ? 1u : 0u;
+            }
         }
         D = wave_sum(D);
         if (ln == 0) a.seg_sel[f.seg_base + ws.seg(i)] = D;
@@ -789,8 +850,22 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
         if (ln == 0) base = atomicAdd(&st->tbin_n, wt);
         uint32_t t = __shfl(base, 0, 64) + incl - nt;
         uint2 *tb = a.tbin + (((uint64_t)f.slot_hi << 32) | f.slot_lo);
+#pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) {
             if (!ws.valid(i)) continue;
+            if (ws.full(i)) {
+                walk_segment(a, f, ws.seg(i), [&](uint32_t valid, const uint32_t *idx, const float *v) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t key = key_of(v[j]);
+                        if ((valid & (1u << j)) && key >= Gs && cand_bin(key, G, SH) == bstar) {
+                            if (t < f.tbin_cap) tb[t] = make_uint2(idx[j], __float_as_uint(v[j]));
+                            ++t;
+                        }
+                    }
+                });
+                continue;
+            }
             const uint32_t cnt = ws.cnt[i];
             const uint2 *slots = ws.slots(a, f, i);
             for (uint32_t p = ln; p < cnt; p += 64) {
@@ -959,41 +1034,44 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     }
 }
 
-// Zero mode, one segment by one wave: every nonzero entry of the segment and
-// its first ztake zeros (index order), re-read from the residual buffer
-// (which holds acc after the streaming pass), go to the message from
-// position base on; their residual becomes +0.0.
-__device__ void emit_rescan(const SparsifyArgs &a, const FinWork &f, uint32_t seg, uint32_t ztake,
-                            uint32_t base)
+// Re-read one segment from acc (the residual buffer) and emit its selection
+// in index order from message position base on, one wave; sent entries'
+// residual becomes +0.0.  Used for a segment with more candidates than slots
+// and, in zero mode, for a segment that sends zeros (they are never stored).
+// ZERO: every nonzero entry and the segment's first ztake zeros are sent;
+// otherwise the entries with key > T, or key == T and index <= cut.
+template <bool ZERO>
+__device__ void emit_rescan(const SparsifyArgs &a, const FinWork &f, uint32_t seg, uint32_t base,
+                            uint32_t ztake, uint32_t T, uint32_t cut)
 {
-    const uint32_t ln = lane_id();
-    const uint32_t end = f.off + f.n;
-    const uint32_t b4 = end & ~3u;
     const uint32_t mend = f.moff + f.k;
     uint32_t run = 0, zrun = 0;
-    uint32_t idx[4];
-    float v[4];
-    // entries j of this lane with (valid >> j) & 1, in index order lane-major;
-    // wave-uniform call
-    auto group = [&](uint32_t valid) {
-        uint32_t zm = 0, nzm = 0;
+    walk_segment(a, f, seg, [&](uint32_t valid, const uint32_t *idx, const float *v) {
+        uint32_t sel = 0, zm = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (valid & (1u << j)) {
-                if (key_of(v[j]) == 0u) zm |= 1u << j;
-                else nzm |= 1u << j;
+            if (!(valid & (1u << j))) continue;
+            const uint32_t key = key_of(v[j]);
+            if (ZERO) {
+                if (key == 0u) zm |= 1u << j;
+                else sel |= 1u << j;
+            } else if (key > T || (key == T && idx[j] <= cut)) {
+                sel |= 1u << j;
             }
         }
-        uint32_t ztot, stot;
-        uint32_t zr = zrun + wave_prefix3((uint32_t)__popc(zm), ztot);
-        uint32_t sel = nzm;
+        if (ZERO) {
+            uint32_t ztot;
+            uint32_t zr = zrun + wave_prefix3((uint32_t)__popc(zm), ztot);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (zm & (1u << j)) {
-                if (zr < ztake) sel |= 1u << j;
-                ++zr;
+            for (int j = 0; j < 4; ++j) {
+                if (zm & (1u << j)) {
+                    if (zr < ztake) sel |= 1u << j;
+                    ++zr;
+                }
             }
+            zrun += ztot;
         }
+        uint32_t stot;
         uint32_t pos = base + run + wave_prefix3((uint32_t)__popc(sel), stot);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1007,42 +1085,17 @@ __device__ void emit_rescan(const SparsifyArgs &a, const FinWork &f, uint32_t se
             }
         }
         run += stot;
-        zrun += ztot;
-    };
-    if (seg == 0 && f.off < f.a4) {          // unaligned head of the layer
-        const uint32_t i = f.off + ln;
-        idx[0] = i;
-        v[0] = (i < f.a4) ? a.res[i] : 0.0f;
-        group((i < f.a4) ? 1u : 0u);
-    }
-    const uint32_t q0 = (f.a4 + seg * kSeg) / 4u;
-    const uint32_t q1 = min(f.a4 + (seg + 1u) * kSeg, b4) / 4u;
-    const v4f *r4 = reinterpret_cast<const v4f *>(a.res);
-    for (uint32_t qb = q0; qb < q1; qb += 64u) {
-        const uint32_t q = qb + ln;
-        const v4f x = (q < q1) ? r4[q] : (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            idx[j] = 4u * q + j;
-            v[j] = x[j];
-        }
-        group((q < q1) ? 0xfu : 0u);
-    }
-    if (seg == f.nseg - 1 && b4 < end) {     // unaligned tail of the layer
-        const uint32_t i = b4 + ln;
-        idx[0] = i;
-        v[0] = (i < end) ? a.res[i] : 0.0f;
-        group((i < end) ? 1u : 0u);
-    }
+    });
 }
 
 // k_fin_emit: write the selected candidates of each segment, in index order,
-// and zero their residual.  In zero mode a segment that sends zeros is
-// re-read whole instead (its zeros were not stored).
+// and zero their residual.  Segments with more candidates than slots, and in
+// zero mode segments that send zeros, are re-read whole instead.
 __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 {
     __shared__ uint32_t sbase[kFinSegs];
     __shared__ uint32_t ztake[kFinSegs];
+    __shared__ uint32_t redo[kFinSegs];
     const uint32_t fb = a.fin_base + blockIdx.x;
     const FinWork f = a.fin_work[fb];
     const SampledState *st = a.state + f.sid;
@@ -1058,10 +1111,11 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
         const uint32_t s = f.seg0 + ln;
         const bool in = s < s_end;
         uint32_t v = in ? a.seg_sel[f.seg_base + s] : 0u;
+        const uint32_t raw = in ? a.seg_count[f.seg_base + s] : 0u;
         uint32_t zt = 0;
         if (zero) {
             const uint32_t e = st->idx_cut;            // zeros the layer sends
-            const uint32_t z = in ? seg_len(f, s) - (v) : 0u;      // v = stored (nonzero) entries
+            const uint32_t z = in ? seg_len(f, s) - raw : 0u;   // every nonzero is a candidate
             const uint32_t zb = a.fin_eq[fb] + wave_incl_scan(z) - z;   // zeros before segment s
             zt = (zb >= e) ? 0u : min(z, e - zb);
             v += zt;
@@ -1070,6 +1124,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
         if (in) {
             sbase[ln] = f.moff + a.fin_total[fb] + incl - v;
             ztake[ln] = zt;
+            redo[ln] = (raw > f.cap || zt != 0u) ? 1u : 0u;
         }
     }
     const uint32_t T = zero ? 0u : st->T, cut = zero ? 0u : st->idx_cut;
@@ -1079,7 +1134,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
     for (int i = 0; i < kSegsPerWave; ++i) {
         if (!ws.valid(i)) continue;
         const uint32_t base = sbase[ws.seg(i) - f.seg0];
-        if (zero && ztake[ws.seg(i) - f.seg0] != 0u) continue;   // re-read below
+        if (redo[ws.seg(i) - f.seg0]) continue;   // re-read below
         const uint32_t cnt = ws.cnt[i];
         const uint2 *slots = ws.slots(a, f, i);
         uint32_t run = 0;
@@ -1106,11 +1161,10 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
             run += (uint32_t)__popcll(m);
         }
     }
-    if (zero) {
-        for (uint32_t s = f.seg0 + (threadIdx.x >> 6); s < s_end; s += kWaves) {
-            const uint32_t zt = ztake[s - f.seg0];
-            if (zt != 0u) emit_rescan(a, f, s, zt, sbase[s - f.seg0]);
-        }
+    for (uint32_t s = f.seg0 + (threadIdx.x >> 6); s < s_end; s += kWaves) {
+        if (!redo[s - f.seg0]) continue;
+        if (zero) emit_rescan<true>(a, f, s, sbase[s - f.seg0], ztake[s - f.seg0], 0u, 0u);
+        else emit_rescan<false>(a, f, s, sbase[s - f.seg0], 0u, T, cut);
     }
 }
 

@@ -296,6 +296,43 @@ def test_mostly_zero_layers(oracle):
         assert rep["layers_exact"] == 0, rep
 
 
+def test_clustered_candidates(oracle):
+    """The large entries of a layer sit in one contiguous block (as in an
+    embedding's touched rows), so the block's segments hold far more
+    candidates than their slots; those segments are re-read from acc instead
+    of taking the exact path.  Layer 0: a block of bf16-valued (tied) large
+    values; layer 1: fewer than k nonzero entries, all in one block (zero
+    mode with full segments)."""
+    import zlib
+    sizes = [4_000_003, 3_000_000]
+    off = np.zeros(len(sizes) + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    n = int(off[-1])
+    k = oracle.k_for_ratio(np.diff(off), 1, 1000)
+    P = 2
+    run = GpuRunner(off, k, P)
+    rng = np.random.default_rng(zlib.crc32(b"clustered"))
+    r = np.zeros(n, np.float32)
+    w = W.adversarial_values(19, n, "normal")
+    K = int(k.sum())
+    moff = np.concatenate([[0], np.cumsum(k)])
+    for step in range(2):
+        _progress(f"[clustered] step {step}")
+        g = np.zeros(n, np.float32)
+        g[:sizes[0]] = (0.01 * rng.standard_normal(sizes[0])).astype(np.float32)
+        blk = 1_000_001 + 4096 * step
+        g[blk:blk + 65536] = W._to_bf16_values(rng.standard_normal(65536))
+        nz = 100_000 + rng.choice(10_000, 2000, replace=False)
+        g[off[1] + nz] = rng.standard_normal(2000).astype(np.float32)
+        oi = np.empty((P - 1, K), np.uint32)
+        ov = rng.standard_normal((P - 1, K)).astype(np.float32)
+        for l in range(len(sizes)):
+            oi[0, moff[l]:moff[l + 1]] = np.sort(rng.choice(sizes[l], int(k[l]), replace=False)) + off[l]
+        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, tag=f"clustered/{step}")
+        rep = run.report()
+        assert rep["layers_exact"] == 0, rep
+
+
 def test_aggregate_rejects_invalid_messages(oracle):
     """Message entries that break the layout (an index outside its layer, an
     index beyond n, a descending pair, a duplicate) are skipped and counted;
