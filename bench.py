@@ -102,7 +102,7 @@ def cpu_baseline(wl, k, budget_s=20.0):
         return {"value": round(m / t / 1e9, 6), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
                 "sample": f"{wl.name}: the first {m:,} entries of its single tensor as one layer "
                           f"(k = {km:,}), one sparsify + aggregate step with P={wl.P}, "
-                          f"{t:.1f} s single-threaded"}
+                          f"{t:.1f} s single-threaded on {cpu_model()}"}, None
     # calibrate on the smallest prefix with at least ~2M entries
     def run_prefix(nl):
         sub_off = off[: nl + 1]
@@ -143,7 +143,64 @@ def cpu_baseline(wl, k, budget_s=20.0):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{wl.name}: first {nl2} of {wl.L} tensors ({n2:,} entries), one "
-                  f"sparsify + aggregate step with P={wl.P}, {t2:.1f} s single-threaded",
+                  f"sparsify + aggregate step with P={wl.P}, {t2:.1f} s single-threaded "
+                  f"on {cpu_model()}",
+    }, run_prefix_threaded(wl, k, nl2)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def run_prefix_threaded(wl, k, nl):
+    """The same oracle step on the same tensors, its per-layer selections and
+    disjoint index windows of the aggregate run by a pool of threads (the
+    oracle's C calls release the interpreter lock)."""
+    import concurrent.futures as cf
+    import oracle as O
+    from layer_wise_top_amd import workloads as W
+    orc = O.default()
+    off = wl.offsets()
+    sub_off = off[: nl + 1]
+    n = int(sub_off[-1])
+    threads = max(1, min(16, os.cpu_count() or 1))
+    g = [W.gen_grad_layer(wl, 0, 0, l) for l in range(nl)]
+    w = np.concatenate([W.gen_weights_layer(wl, l) for l in range(nl)])
+    P = wl.P
+    sub_k = k[:nl]
+    Ks = int(sub_k.sum())
+    moff = np.concatenate([[0], np.cumsum(sub_k)])
+    oi = np.empty((P - 1, Ks), np.uint32)
+    ov = np.empty((P - 1, Ks), np.float32)
+    for p in range(1, P):
+        for l in range(nl):
+            i, v = W.gen_message_layer(wl, 0, p, l, int(sub_k[l]))
+            oi[p - 1, moff[l]:moff[l + 1]] = i
+            ov[p - 1, moff[l]:moff[l + 1]] = v
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda l: orc.sparsify([0, len(g[l])], [int(sub_k[l])], g[l],
+                                                   np.zeros(len(g[l]), np.float32)), range(nl)))
+        mi = np.concatenate([p_[0].astype(np.uint32) + np.uint32(sub_off[l]) for l, p_ in enumerate(parts)])
+        mv = np.concatenate([p_[1] for p_ in parts])
+        ai = np.concatenate([mi[None], oi], 0)
+        av = np.concatenate([mv[None], ov], 0)
+        cuts = np.linspace(0, n, threads + 1).astype(np.int64)
+        list(ex.map(lambda t: orc.aggregate(ai, av, w[cuts[t]:cuts[t + 1]], wl.lr,
+                                            lo=int(cuts[t]), hi=int(cuts[t + 1])),
+                    [t for t in range(threads) if cuts[t + 1] > cuts[t]]))
+    t = time.perf_counter() - t0
+    return {
+        "value": round(n / t / 1e9, 6), "unit": "Gelem/s", "cores": threads, "kind": "oracle",
+        "sample": f"{wl.name}: the same {nl} tensors ({n:,} entries), per-layer selections and "
+                  f"{threads} aggregate windows on {threads} threads, {t:.1f} s",
     }
 
 
@@ -366,7 +423,9 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
     out["stream_ceiling_gbs"] = stream_ceiling_gbs(wl.n)
     if do_cpu:
         log("timing the oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(wl, k)
+        out["cpu_baseline"], threaded = cpu_baseline(wl, k)
+        if threaded is not None:
+            out["cpu_baseline_threads"] = threaded
     return out
 
 
