@@ -187,7 +187,7 @@ int build_plan(lags_layout *lo)
             si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
             // every candidate the layer can store fits its threshold-bin list,
             // so a large bin (many equal keys) never forces the exact path
-            si.tbin_cap = si.nseg * si.cap;
+            si.tbin_cap = (uint32_t)std::min<uint64_t>((uint64_t)si.nseg * si.cap, 0xffffffffu);
             si.fin_first = (uint32_t)lo->fin_work.size();
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
             // histogram copies grow with the layer, so that the streaming
