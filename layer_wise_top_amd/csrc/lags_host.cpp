@@ -102,17 +102,16 @@ void plan_agg(const lags_layout *lo, int32_t P, std::vector<uint32_t> &cbase,
 // Threshold-guess plan for a sampled layer of n entries sending k: sample s
 // keys and take the j-th largest, with j = m * k * s / n and the margin m the
 // smallest that keeps (1 - 1/m) * sqrt(j) >= 6 (six standard deviations of the
-// sample count above the guess).  Returns false if the ratio is too large for
-// a guess to pay off.
-bool plan_guess(uint32_t n, uint32_t k, uint32_t s, uint32_t &j, double &m)
+// sample count above the guess).  When that rank is beyond the sample (k
+// close to n), j = s asks for the guess G = 0: every nonzero entry is a
+// candidate.
+void plan_guess(uint32_t n, uint32_t k, uint32_t s, uint32_t &j, double &m)
 {
     const double lam = (double)k * (double)s / (double)n;
     m = 1.05;
     while (m < 1e6 && (1.0 - 1.0 / m) * std::sqrt(m * lam) < 6.0) m *= 1.05;
     const double jj = std::ceil(m * lam);
-    if (jj > s / 4.0) return false;
-    j = (uint32_t)std::max(1.0, jj);
-    return true;
+    j = (uint32_t)std::min<double>(std::max(1.0, jj), (double)s);
 }
 
 int build_plan(lags_layout *lo)
@@ -170,17 +169,14 @@ int build_plan(lags_layout *lo)
             } else {
                 si.nchunk = kSampleMax / kSampleChunk;
                 uint32_t j = 0;
-                if (plan_guess(li.n, li.k, si.nchunk * kSampleChunk, j, m)) {
-                    si.j = j;
-                    const double mu = m * (double)li.k * kSeg / (double)li.n;
-                    size_t cap = (size_t)std::ceil(mu + 8.0 * std::sqrt(mu) + 32.0);
-                    cap = align_up(cap, 32);
-                    si.cap = (uint32_t)std::min<size_t>(cap, kSeg);
-                } else {
-                    si.force_exact = 1;
-                    si.cap = 1;
-                    si.j = 1;
-                }
+                plan_guess(li.n, li.k, si.nchunk * kSampleChunk, j, m);
+                si.j = j;
+                // slots for the expected candidates plus eight standard
+                // deviations; a segment beyond them is re-read instead
+                const double mu = std::min(m * (double)li.k, (double)li.n) * kSeg / (double)li.n;
+                size_t cap = (size_t)std::ceil(mu + 8.0 * std::sqrt(mu) + 32.0);
+                cap = align_up(cap, 32);
+                si.cap = (uint32_t)std::min<size_t>(cap, kCapMax);
             }
             si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
             si.slot_hi = (uint32_t)(slot_base >> 32);

@@ -18,6 +18,8 @@ constexpr uint32_t kSmallMax = 4096;     // layers up to this size: one workgrou
 constexpr uint32_t kDenseTile = 16384;   // entries per workgroup for k == n layers
 constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident)
 constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
+constexpr uint32_t kCapMax = 1024;       // candidate slots per segment, at most (beyond:
+                                         // the segment is re-read)
 constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
 constexpr uint32_t kHistMaxCopies = 64;  // copies of a layer's histogram, at most (spread atomics)
 constexpr uint32_t kTilesPerCopy = 128;  // streaming workgroups per histogram copy, about
@@ -69,7 +71,7 @@ struct SampledInfo {      // one per sampled layer, device table
     uint32_t full_sample; // 1: the sample is the whole layer (guess = exact k-th key)
     uint32_t nchunk;      // sample chunks (when not full)
     uint32_t j;           // rank of the guess inside the sample (1-based, from the top)
-    uint32_t force_exact; // ratio too large for a guess: exact path
+    uint32_t spare;
     uint32_t fin_nblocks; // finishing workgroups of this layer
     uint32_t fin_first;   // index of the layer's first finishing workgroup
     uint32_t tbin_cap;    // threshold-bin entries the layer can keep: all its slots

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     for (uint32_t t = threadIdx.x; t < S.hcopies * kNBins; t += NT) lh[t] = 0;
     for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
     __syncthreads();
-    if (S.force_exact || a.force_exact) {
+    if (a.force_exact) {
         if (threadIdx.x == 0) {
             st->G = 0xffffffffu;   // no key reaches it: the layer takes the exact path
             st->SH = 0;
@@ -383,6 +383,17 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     }
     __syncthreads();
     const uint32_t M = block_max<NT>(m, tmp);
+    if (rank >= cnt) {
+        // k close to n: the rank is beyond the sample, so every nonzero
+        // entry is a candidate (G = 0)
+        if (threadIdx.x == 0) {
+            uint32_t sh = 0;
+            while (sh < 31u && (uint64_t)M >= ((uint64_t)kNBins << sh)) ++sh;
+            st->G = 0;
+            st->SH = sh;
+        }
+        return;
+    }
     block_find_rank<NT>(hist, kSampleBins, rank, res, tmp);
     const uint32_t b1 = res[0];
     const uint32_t rank2 = rank - res[1];
