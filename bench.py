@@ -351,6 +351,8 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
             "avg_ms": main_ms,
         },
         "kernels_avg_ms": kernels,
+        "sparsify_ms": round(sum(v for kk, v in kernels.items() if not kk.startswith("k_agg")), 5),
+        "aggregate_ms": round(sum(v for kk, v in kernels.items() if kk.startswith("k_agg")), 5),
         "report": rep,
     }
     if times:

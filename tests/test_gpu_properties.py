@@ -1,0 +1,113 @@
+"""GPU properties through the C ABI: random layouts against the oracle, and
+checkpoint/resume (the library keeps no state between calls apart from the
+caller's residual and weights)."""
+import zlib
+
+import numpy as np
+import pytest
+
+from gpu_helpers import GpuRunner, assert_bits_equal, to_dev, to_np_f32
+from layer_wise_top_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["normal", "ties", "bf16", "zeros", "int", "equal"]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_random_layouts(oracle, seed):
+    """Random layer sizes (1 .. 400000), random k in [1, n], a random value
+    kind per step, random P: messages, residuals and weights bit-exact."""
+    import torch
+    rng = np.random.default_rng(zlib.crc32(f"random layout {seed}".encode()))
+    L = int(rng.integers(1, 40))
+    scale = rng.choice([300, 5000, 60000, 400000])
+    sizes = rng.integers(1, scale + 1, size=L)
+    off = np.zeros(L + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    n = int(off[-1])
+    mode = seed % 3
+    if mode == 0:
+        k = np.array([int(rng.integers(1, s + 1)) for s in sizes], np.int64)
+    else:
+        den = 100 if mode == 1 else 1000
+        k = oracle.k_for_ratio(sizes, 1, den)
+    P = int(rng.integers(1, 6))
+    run = GpuRunner(off, k, P)
+    K = int(k.sum())
+    moff = np.concatenate([[0], np.cumsum(k)])
+    r = np.zeros(n, np.float32)
+    w = W.adversarial_values(1000 + seed, n, "normal")
+    for step in range(2):
+        kind = KINDS[int(rng.integers(0, len(KINDS)))]
+        _say(f"[random layout {seed}] L={L} n={n} K={K} P={P} step {step} {kind}")
+        g = W.adversarial_values(2000 + 10 * seed + step, n, kind)
+        oi = np.empty((P - 1, K), np.uint32)
+        ov = rng.standard_normal((P - 1, K)).astype(np.float32)
+        for p in range(P - 1):
+            for l in range(L):
+                oi[p, moff[l]:moff[l + 1]] = np.sort(rng.choice(int(sizes[l]), int(k[l]), replace=False)) + off[l]
+        g_d, r_d, w_d = to_dev(g), to_dev(r), to_dev(w)
+        run.sparsify(g_d, r_d)
+        if P > 1:
+            run.set_others(oi, ov)
+        run.aggregate(w_d, 0.05)
+        torch.cuda.synchronize()
+        mi_o, mv_o, r_o = oracle.sparsify(off, k, g, r)
+        mi_g, mv_g = run.message()
+        assert_bits_equal("msg_idx", mi_g, mi_o)
+        assert_bits_equal("msg_val", mv_g, mv_o)
+        assert_bits_equal("residual", to_np_f32(r_d), r_o)
+        ai = np.concatenate([mi_o[None], oi], 0) if P > 1 else mi_o[None]
+        av = np.concatenate([mv_o[None], ov], 0) if P > 1 else mv_o[None]
+        w_o = oracle.aggregate(ai, av, w, 0.05)
+        assert_bits_equal("weights", to_np_f32(w_d), w_o)
+        r, w = r_o, w_o
+
+
+def test_resume_equals_continuous_run():
+    """ResNet-50: ten steps in one go equal five steps, a save of (weights,
+    residual) to the host, a fresh layout and workspace, and five more steps
+    — bit for bit."""
+    import torch
+    from layer_wise_top_amd import lags
+    wl = W.get("resnet50")
+    off = wl.offsets()
+    num, den = wl.ratios()
+    k = lags.k_table(off, num, den)
+    P = wl.P
+    grads = [to_dev(W.gen_grad(wl, s)) for s in range(10)]
+    msgs = [W.gen_messages(wl, s, k) for s in range(10)]
+    w0 = W.gen_weights(wl)
+
+    def run_steps(run, r_d, w_d, steps):
+        for s in steps:
+            run.set_others(*msgs[s])
+            run.sparsify(grads[s], r_d)
+            run.aggregate(w_d, wl.lr)
+        torch.cuda.synchronize()
+
+    a = GpuRunner(off, k, P)
+    r_a = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
+    w_a = to_dev(w0)
+    run_steps(a, r_a, w_a, range(10))
+
+    b = GpuRunner(off, k, P)
+    r_b = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
+    w_b = to_dev(w0)
+    run_steps(b, r_b, w_b, range(5))
+    saved = (to_np_f32(r_b).copy(), to_np_f32(w_b).copy())
+    del b
+    c = GpuRunner(off, k, P)
+    r_c, w_c = to_dev(saved[0]), to_dev(saved[1])
+    run_steps(c, r_c, w_c, range(5, 10))
+    assert_bits_equal("residual", to_np_f32(r_c), to_np_f32(r_a))
+    assert_bits_equal("weights", to_np_f32(w_c), to_np_f32(w_a))
+    mi_a, mv_a = a.message()
+    mi_c, mv_c = c.message()
+    assert_bits_equal("last message idx", mi_c, mi_a)
+    assert_bits_equal("last message val", mv_c, mv_a)
