@@ -35,6 +35,10 @@
  *   - arguments are validated on the host before anything is launched; on a
  *     negative status nothing has been launched and nothing written;
  *   - device faults surface at the caller's next synchronisation (HIP rules);
+ *   - the first call on a device builds the layout's device tables (and the
+ *     first aggregate with a given P its chunk tables) with hipMalloc and a
+ *     synchronous copy; after that a call allocates nothing, copies nothing
+ *     and does not synchronise, so it can be captured into a HIP graph;
  *   - one workspace must not be used by two calls that may overlap in time,
  *     except range calls on disjoint layer ranges (see lags_sparsify_range).
  */

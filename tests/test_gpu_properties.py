@@ -111,3 +111,56 @@ def test_resume_equals_continuous_run():
     mi_c, mv_c = c.message()
     assert_bits_equal("last message idx", mi_c, mi_a)
     assert_bits_equal("last message val", mv_c, mv_a)
+
+
+def test_graph_capture_replays_match_eager():
+    """After a first call has built the device tables, a step makes no
+    allocation and no synchronisation, so it can be captured into a HIP graph.
+    Each of three replays, with eager work and synchronisations between them,
+    must equal the eager step from the same state."""
+    import torch
+    from layer_wise_top_amd import lags
+    wl = W.get("vgg16")
+    off = wl.offsets()
+    num, den = wl.ratios()
+    k = lags.k_table(off, num, den)
+    P = wl.P
+    run = GpuRunner(off, k, P)
+    run.set_others(*W.gen_messages(wl, 0, k))
+    g = to_dev(W.gen_grad(wl, 0))
+    w0 = to_dev(W.gen_weights(wl))
+    r = torch.zeros(wl.n, dtype=torch.float32, device="cuda")
+    w = w0.clone()
+    s = torch.cuda.Stream()
+
+    def step():
+        lags.lags_sparsify_layers(run.layout, g, r, run.msg_idx[0], run.msg_val[0], run.ws, 0, s)
+        lags.lags_aggregate_apply(run.layout, w, run.msg_idx, run.msg_val, P, wl.lr, run.ws, s)
+
+    with torch.cuda.stream(s):
+        step()                                  # builds the device tables
+    torch.cuda.synchronize()
+    r_start, w_start = r.clone(), w.clone()
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    want = [to_np_f32(r).copy(), to_np_f32(w).copy(), run.message()]
+    graph = torch.cuda.CUDAGraph()
+    r.copy_(r_start)
+    w.copy_(w_start)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    for rep in range(3):
+        r.copy_(r_start)
+        w.copy_(w_start)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"[graph] replay {rep}")
+        assert_bits_equal("residual", to_np_f32(r), want[0])
+        assert_bits_equal("weights", to_np_f32(w), want[1])
+        mi, mv = run.message()
+        assert_bits_equal("msg_idx", mi, want[2][0])
+        assert_bits_equal("msg_val", mv, want[2][1])
+        float(torch.ones(1000, device="cuda").sum())   # eager work between replays
