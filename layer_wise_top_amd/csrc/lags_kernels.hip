@@ -191,21 +191,25 @@ __device__ void block_find_rank(const uint32_t *hist, uint32_t nbins, uint32_t r
 
 // ---------------------------------------------------------------------------
 // Exact selection by one workgroup: MSD radix select of the rank-th largest
-// 32-bit value among the items with match(i) true, digits of 11/11/10 bits.
-// Returns the value and, in *eq_take, how many items equal to it are needed to
-// reach rank (the items strictly above it number rank - eq_take).
+// 32-bit value among the items with match(i) true, in digits of at most 11
+// bits.  The caller may state that every matching value has the bits of
+// `known` above bit vbits (1 <= vbits <= 32); only the bits below are then
+// resolved.  Returns the value; *eq_take = how many items equal to it are
+// needed to reach rank (the items strictly above it number rank - eq_take);
+// *eq_count (if given) = how many matching items equal it.
 template <class Val, class Match>
 __device__ uint32_t block_radix_select(const Val &val, const Match &match, uint32_t n, uint32_t rank,
-                                       uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t *eq_take)
+                                       uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t *eq_take,
+                                       uint32_t *eq_count = nullptr, uint32_t vbits = 32u,
+                                       uint32_t known = 0u)
 {
-    uint32_t prefix = 0;
-    const uint32_t shifts[3] = {21u, 10u, 0u};
-    const uint32_t widths[3] = {11u, 11u, 10u};
-    for (int lev = 0; lev < 3; ++lev) {
-        const uint32_t sh = shifts[lev];
-        const uint32_t nb = 1u << widths[lev];
-        const uint32_t top = sh + widths[lev];   // bits above this digit: [top, 32)
-        for (uint32_t b = threadIdx.x; b < nb; b += kBlock) hist[b] = 0;
+    uint32_t prefix = (vbits >= 32u) ? 0u : (known >> vbits) << vbits;
+    for (uint32_t top = vbits; top > 0u;) {   // this digit: bits [sh, top)
+        const uint32_t width = min(top, 11u);
+        const uint32_t sh = top - width;
+        const uint32_t nb = 1u << width;
+        const uint32_t nbins = max(nb, (uint32_t)kBlock);
+        for (uint32_t b = threadIdx.x; b < nbins; b += kBlock) hist[b] = 0;
         __syncthreads();
         // four items per thread per round: their loads are in flight together
         for (uint32_t i0 = threadIdx.x; i0 < n; i0 += 4u * kBlock) {
@@ -224,13 +228,23 @@ __device__ uint32_t block_radix_select(const Val &val, const Match &match, uint3
             }
         }
         __syncthreads();
-        block_find_rank(hist, nb < (uint32_t)kBlock ? (uint32_t)kBlock : nb, rank, res, tmp);
+        block_find_rank(hist, nbins, rank, res, tmp);
         prefix |= res[0] << sh;
         rank -= res[1];
+        // the last digit's bin holds exactly the items equal to the result
+        if (sh == 0u && eq_count) *eq_count = hist[res[0]];
         __syncthreads();
+        top = sh;
     }
     *eq_take = rank;
     return prefix;
+}
+
+// Bits that resolve a value known to lie in [lo, hi]: every such value has
+// lo's bits above the highest bit in which lo and hi differ.
+__device__ __forceinline__ uint32_t varying_bits(uint32_t lo, uint32_t hi)
+{
+    return max(32u - (uint32_t)__clz(lo ^ hi), 1u);
 }
 
 // Emit the selection of one layer from a value source, in index order: entries
@@ -344,11 +358,24 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     if (S.full_sample) {
         cnt = L.n;
         rank = L.k;
-        for (uint32_t i = threadIdx.x; i < cnt; i += NT) {
-            const uint32_t key = key_of(a.grad[L.off + i] + a.res[L.off + i]);
-            keys[i] = key;
-            m = max(m, key);
-            atomicAdd(&hist[key >> 19], 1u);
+        // the whole layer is requested at once (cnt <= kSampleMax entries)
+        constexpr int EPT = kSampleMax / NT;
+        float gv[EPT], rv[EPT];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const uint32_t i = threadIdx.x + u * NT;
+            gv[u] = (i < cnt) ? a.grad[L.off + i] : 0.0f;
+            rv[u] = (i < cnt) ? a.res[L.off + i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const uint32_t i = threadIdx.x + u * NT;
+            if (i < cnt) {
+                const uint32_t key = key_of(gv[u] + rv[u]);
+                keys[i] = key;
+                m = max(m, key);
+                atomicAdd(&hist[key >> 19], 1u);
+            }
         }
     } else {
         cnt = S.nchunk * kSampleChunk;
@@ -604,11 +631,25 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
     const LayerInfo L = a.linfo[w.layer];
     const uint32_t lo = L.off + w.tile * kDenseTile;
     const uint32_t hi = min(lo + kDenseTile, L.off + L.n);
-    for (uint32_t i = lo + threadIdx.x; i < hi; i += kBlock) {
-        const float x = a.grad[i] + a.res[i];
-        a.res[i] = 0.0f;
-        a.msg_idx[L.moff + (i - L.off)] = i;
-        a.msg_val[L.moff + (i - L.off)] = x;
+    // batches of EPT entries per thread, all loads of a batch in flight
+    // before its stores (a store to the residual may alias a later load)
+    constexpr int EPT = 16;
+    for (uint32_t i0 = lo + threadIdx.x; i0 < hi; i0 += EPT * kBlock) {
+        float x[EPT];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const uint32_t i = i0 + u * kBlock;
+            x[u] = (i < hi) ? a.grad[i] + a.res[i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const uint32_t i = i0 + u * kBlock;
+            if (i < hi) {
+                a.res[i] = 0.0f;
+                a.msg_idx[L.moff + (i - L.off)] = i;
+                a.msg_val[L.moff + (i - L.off)] = x[u];
+            }
+        }
     }
 }
 
@@ -900,18 +941,26 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
 // Exact threshold and tie cut among the h entries of the threshold bin (the
 // need-th largest key; among keys equal to it, the lowest indices first), and
 // the per-segment and per-workgroup counts of the bin's selected entries.
+// Every key of the bin lies in [klo, khi] and every index in the layer
+// [f.off, f.off + f.n), so only the bits that vary there are resolved.  When
+// all keys equal to the threshold are taken, the cut is the largest index.
 template <class KeyF, class IdxF>
 __device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t h, uint32_t need,
-                             const KeyF &key, const IdxF &idx, uint32_t *hist, uint32_t *tmp,
-                             uint32_t *res, uint32_t &T_out, uint32_t &cut_out)
+                             uint32_t klo, uint32_t khi, const KeyF &key, const IdxF &idx,
+                             uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t &T_out,
+                             uint32_t &cut_out)
 {
-    uint32_t e;
-    const uint32_t T = block_radix_select(key, [](uint32_t) { return true; }, h, need, hist, tmp, res, &e);
-    // e-th smallest index among keys == T  ==  e-th largest of ~index
-    uint32_t e2;
-    const uint32_t ncut = block_radix_select([&](uint32_t p) { return ~idx(p); },
-                                             [&](uint32_t p) { return key(p) == T; }, h, e, hist, tmp, res, &e2);
-    const uint32_t cut = ~ncut;
+    uint32_t e, eq;
+    const uint32_t T = block_radix_select(key, [](uint32_t) { return true; }, h, need, hist, tmp, res, &e,
+                                          &eq, varying_bits(klo, khi), klo);
+    uint32_t cut = 0xffffffffu;
+    if (e < eq) {
+        // e-th smallest index among keys == T  ==  e-th largest of ~index
+        const uint32_t nlo = ~(f.off + (f.n - 1u)), nhi = ~f.off;
+        uint32_t e2;
+        cut = ~block_radix_select([&](uint32_t p) { return ~idx(p); }, [&](uint32_t p) { return key(p) == T; },
+                                  h, e, hist, tmp, res, &e2, nullptr, varying_bits(nlo, nhi), nlo);
+    }
     for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
         const uint32_t kp = key(p), ip = idx(p);
         if (kp > T || (kp == T && ip <= cut)) {
@@ -942,8 +991,21 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
         // a small layer, start to finish: acc in LDS, exact radix select
         const LayerInfo L = a.linfo[a.small_layers[a.small_base + (blockIdx.x - a.nsampled)]];
         float *acc_s = reinterpret_cast<float *>(pool);
-        for (uint32_t i = threadIdx.x; i < L.n; i += kBlock)
-            acc_s[i] = a.grad[L.off + i] + a.res[L.off + i];
+        {
+            constexpr int EPT = kSmallMax / kBlock;   // the whole layer requested at once
+            float gv[EPT], rv[EPT];
+#pragma unroll
+            for (int u = 0; u < EPT; ++u) {
+                const uint32_t i = threadIdx.x + u * kBlock;
+                gv[u] = (i < L.n) ? a.grad[L.off + i] : 0.0f;
+                rv[u] = (i < L.n) ? a.res[L.off + i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < EPT; ++u) {
+                const uint32_t i = threadIdx.x + u * kBlock;
+                if (i < L.n) acc_s[i] = gv[u] + rv[u];
+            }
+        }
         __syncthreads();
         if (L.k == L.n) {
             for (uint32_t i = threadIdx.x; i < L.n; i += kBlock) {
@@ -1011,19 +1073,35 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     // otherwise straight from the workspace
     const uint32_t need = L.k - st->c_above;
     const uint2 *tb = a.tbin + (((uint64_t)S.slot_hi << 32) | S.slot_lo);
+    // the keys of bin bstar: (key - G) >> SH == bstar, or above for the last bin
+    const uint32_t bstar = st->bstar;
+    const uint64_t blo = (uint64_t)st->G + ((uint64_t)bstar << st->SH);
+    const uint32_t klo = (uint32_t)min(blo, (uint64_t)0x7fffffffu);
+    const uint32_t khi = (bstar + 1u >= kNBins) ? 0x7fffffffu
+                                                : (uint32_t)min(blo + (1ull << st->SH) - 1u, (uint64_t)0x7fffffffu);
     uint32_t T, idx_cut;
     if (h <= kTbinCap) {
-        for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
-            const uint2 c = tb[p];
-            ti[p] = c.x;
-            tk[p] = c.y & 0x7fffffffu;
+        constexpr int EPT = kTbinCap / kBlock;     // the whole bin requested at once
+        uint2 c[EPT];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const uint32_t p = threadIdx.x + u * kBlock;
+            c[u] = (p < h) ? tb[p] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const uint32_t p = threadIdx.x + u * kBlock;
+            if (p < h) {
+                ti[p] = c[u].x;
+                tk[p] = c[u].y & 0x7fffffffu;
+            }
         }
         __syncthreads();
-        resolve_tbin(a, f, h, need, [&](uint32_t p) { return tk[p]; }, [&](uint32_t p) { return ti[p]; },
-                     hist, tmp, res, T, idx_cut);
+        resolve_tbin(a, f, h, need, klo, khi, [&](uint32_t p) { return tk[p]; },
+                     [&](uint32_t p) { return ti[p]; }, hist, tmp, res, T, idx_cut);
     } else {
         if (threadIdx.x == 0) atomicAdd(&a.report[kRepWide], 1u);
-        resolve_tbin(a, f, h, need, [&](uint32_t p) { return tb[p].y & 0x7fffffffu; },
+        resolve_tbin(a, f, h, need, klo, khi, [&](uint32_t p) { return tb[p].y & 0x7fffffffu; },
                      [&](uint32_t p) { return tb[p].x; }, hist, tmp, res, T, idx_cut);
     }
     // the workgroup's own atomics above complete before the scan reads the totals
