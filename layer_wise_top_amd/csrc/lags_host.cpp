@@ -180,7 +180,10 @@ int build_plan(lags_layout *lo)
             }
             si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
             si.slot_hi = (uint32_t)(slot_base >> 32);
-            si.fin_nblocks = (si.nseg + kFinSegs - 1) / kFinSegs;
+            // finer finishing workgroups for smaller layers: more of them run
+            // at once, and the larger layers keep fewer reservation atomics
+            const uint32_t grain = si.nseg <= kFinSmallLayer ? kFinSegsSmall : kFinSegs;
+            si.fin_nblocks = (si.nseg + grain - 1) / grain;
             // every candidate the layer can store fits its threshold-bin list,
             // so a large bin (many equal keys) never forces the exact path
             si.tbin_cap = (uint32_t)std::min<uint64_t>((uint64_t)si.nseg * si.cap, 0xffffffffu);
@@ -211,7 +214,8 @@ int build_plan(lags_layout *lo)
             for (uint32_t b = 0; b < si.fin_nblocks; ++b) {
                 FinWork f{};
                 f.sid = li.sid;
-                f.seg0 = b * kFinSegs;
+                f.seg0 = b * grain;
+                f.grain = grain;
                 f.nseg = si.nseg;
                 f.seg_base = si.seg_base;
                 f.cap = si.cap;

@@ -24,7 +24,9 @@ constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
 constexpr uint32_t kHistMaxCopies = 64;  // copies of a layer's histogram, at most (spread atomics)
 constexpr uint32_t kTilesPerCopy = 128;  // streaming workgroups per histogram copy, about
 constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LDS (larger: global)
-constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup
+constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup (at most)
+constexpr uint32_t kFinSegsSmall = 16;   // ... in a layer of at most kFinSmallLayer segments
+constexpr uint32_t kFinSmallLayer = 1024;
 // aggregate
 constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
 constexpr uint32_t kAggCap = 1024;            // fast-path capacity (entries per chunk)
@@ -110,7 +112,8 @@ struct FinWork {
     uint32_t fin_first;   // first finishing workgroup of the layer
     uint32_t off, n;      // the layer's entries
     uint32_t moff, k;     // the layer's message
-    uint32_t tbin_cap, pad0;
+    uint32_t tbin_cap;
+    uint32_t grain;       // segments per finishing workgroup of the layer
     uint32_t a4;          // 4-aligned start of the layer's interior
     uint32_t pad;
 };

@@ -654,9 +654,9 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Finishing kernels.  fin_work lists, per sampled layer, workgroups of up to
-// kFinSegs consecutive segments; each wave of a workgroup takes every
-// kWaves-th.  Each entry carries everything static the workgroup needs, so
+// Finishing kernels.  fin_work lists, per sampled layer, workgroups of f.grain
+// (at most kFinSegs) consecutive segments; each wave of a workgroup takes
+// every kWaves-th.  Each entry carries everything static the workgroup needs, so
 // its first load is followed directly by the per-call loads.
 
 __device__ __forceinline__ uint32_t seg_of(const FinWork &f, uint32_t i)
@@ -806,7 +806,7 @@ struct WaveSegs {
     {
         s0 = f.seg0;
         wave = wv;
-        send = min(f.seg0 + kFinSegs, f.nseg);
+        send = min(f.seg0 + f.grain, f.nseg);
 #pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[f.seg_base + seg(i)] : 0u;
 #pragma unroll
@@ -966,7 +966,7 @@ __device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t h
         if (kp > T || (kp == T && ip <= cut)) {
             const uint32_t sg = seg_of(f, ip);
             atomicAdd(&a.seg_sel[f.seg_base + sg], 1u);
-            atomicAdd(&a.fin_total[f.fin_first + sg / kFinSegs], 1u);
+            atomicAdd(&a.fin_total[f.fin_first + sg / f.grain], 1u);
         }
     }
     T_out = T;
@@ -1195,7 +1195,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
     if (status != kStOk && status != kStZero) return;
     const bool zero = status == kStZero;
     static_assert(kFinSegs <= 64, "one wave scans the segment counts");
-    const uint32_t s_end = min(f.seg0 + kFinSegs, f.nseg);
+    const uint32_t s_end = min(f.seg0 + f.grain, f.nseg);
     if (threadIdx.x < 64) {
         const uint32_t s = f.seg0 + ln;
         const bool in = s < s_end;
