@@ -185,6 +185,7 @@ struct AggArgs {
     uint32_t j_lo, j_hi;
     uint32_t c_lo, c_hi;
     uint32_t npb;               // entries of pos_layer
+    uint32_t tl;                // start pass: LDS table entries (layers a block spans, plus 2)
 };
 
 // kernel ids for tracing

@@ -1266,14 +1266,16 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 // first and the one-past-last chunk of the range, so a call reads only its own
 // message entries and writes only the starts of chunks [c_lo, c_hi]; the
 // shared boundary start c_hi gets the same value from either neighbour.  A
-// workgroup covers kStartsBlock positions of one worker; the layers they span
-// (at most kStartsBlock + 2, since every layer sends at least one entry) are
-// staged in LDS.
+// workgroup covers kStartsBlock positions of one worker, all requested at
+// once; the layers they span are staged in LDS, in five tables of a.tl
+// entries (dynamic LDS, sized by the host for the layout's widest block: at
+// most kStartsBlock + 3, since every layer sends at least one entry).
 __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
 {
     constexpr int PPT = kStartsBlock / kBlock;      // positions per thread
-    constexpr uint32_t TL = kStartsBlock + 2;
-    __shared__ uint32_t t_off[TL], t_n[TL], t_moff[TL + 1], t_cb[TL], t_sh[TL];
+    extern __shared__ uint32_t tab[];
+    uint32_t *t_off = tab, *t_n = tab + a.tl, *t_moff = tab + 2u * a.tl, *t_cb = tab + 3u * a.tl,
+             *t_sh = tab + 4u * a.tl;
     __shared__ uint32_t lrange[2];
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) a.report[kRepBad + threadIdx.x] = 0;
     const uint32_t p = blockIdx.y;
@@ -1527,7 +1529,7 @@ hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t 
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
 {
     const uint32_t nx = a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u;
-    hipLaunchKernelGGL(k_agg_starts, dim3(nx, a.P), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_agg_starts, dim3(nx, a.P), dim3(kBlock), 5u * a.tl * sizeof(uint32_t), s, a);
     return hipGetLastError();
 }
 

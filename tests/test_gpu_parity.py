@@ -104,8 +104,12 @@ LAYOUT_CASES = [
     ("int", [300000, 12345], (1, 1000), "int", 8, 3),
     ("rand_k", [3000, 70000, 12000, 4200, 500000], "rand", "normal", 6, 2),
     ("many_layers", [97] * 300 + [5000] * 20 + [33333] * 5, (1, 100), "normal", 3, 2),
-    # one sent entry per layer: a block of 256 message positions spans 258 layers
+    # one sent entry per layer: the aggregate's start pass stages ~700 layers
+    # for one block of message positions
     ("tiny_layers", [5] * 700 + [20000], (1, 100), "normal", 4, 2),
+    # 6000 layers of 1-3 entries: every block of message positions spans as
+    # many layers as it has positions (the start pass's largest layer table)
+    ("tiny_layers_widest", [1, 2, 3] * 2000 + [9000], (1, 100), "normal", 3, 2),
 ]
 
 
