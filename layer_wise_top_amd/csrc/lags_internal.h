@@ -126,11 +126,16 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t bstar;       // histogram bin holding the k-th largest candidate
     uint32_t c_above;     // candidates in bins above bstar
     uint32_t reserved[2];
-    uint32_t tbin_n;      // entries of bin bstar collected
     uint32_t T;           // k-th largest key of the layer
     uint32_t idx_cut;     // largest global index taken among keys == T
-    uint32_t pad[5];
+    uint32_t pad0[22];
+    // on a cache line of its own: every finishing workgroup of the layer
+    // reads the fields above while the select pass adds to this one
+    uint32_t tbin_n;      // entries of bin bstar collected
+    uint32_t pad1[31];
 };
+static_assert(offsetof(SampledState, tbin_n) == 128 && sizeof(SampledState) == 256,
+              "the collection counter sits on its own 128-byte line");
 
 // report counters at the head of the workspace
 enum : uint32_t { kRepSampled = 0, kRepExact = 1, kRepBad = 2, kRepSlow = 3, kRepWide = 4, kRepWords = 64 };
