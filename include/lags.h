@@ -67,8 +67,12 @@ extern "C" {
 
 /* Flags for lags_sparsify_layers. */
 #define LAGS_SPARSIFY_EXACT 1u /* skip the sampled threshold estimate: every layer
-                                  above the small-layer size takes the exact
-                                  multi-pass selection (same results, slower) */
+                                  above the small-layer size finds its threshold
+                                  by a multi-workgroup radix select over all its
+                                  keys (three digit passes, then counting and
+                                  emission passes): the same results, about 28
+                                  bytes of memory traffic per entry instead of
+                                  about 12 */
 
 typedef struct lags_layout lags_layout; /* opaque; host object; see below */
 
@@ -270,8 +274,10 @@ int lags_adaptive_k(int32_t L, const int64_t *layer_off, const double *backward_
 
 /* What the last calls that used a workspace did. */
 typedef struct lags_report {
-    int32_t layers_sampled; /* layers on the sampled-threshold path in the last sparsify */
-    int32_t layers_exact;   /* of those, layers that fell back to the exact path */
+    int32_t layers_sampled; /* layers above the small-layer size with k < n in the last
+                               sparsify (the sampled-threshold path, or exact mode) */
+    int32_t layers_exact;   /* of those, layers selected exactly: all of them in exact
+                               mode, otherwise those whose sampled guess fell short */
     uint32_t bad_entries;   /* message entries the last aggregate skipped as invalid */
     uint32_t slow_chunks;   /* aggregate chunks above the fast-path capacity */
     int32_t layers_wide_bin; /* sampled layers whose threshold bin was resolved from the

@@ -401,6 +401,45 @@ int traced(lags_layout *lo, int32_t kid, hipStream_t s, F &&launch)
     return LAGS_OK;
 }
 
+// Exact mode: a multi-workgroup radix select of every sampled layer's
+// threshold (three digit passes, each followed by a per-layer pick), the
+// per-segment counts and tie cut, then the same emission as the sampled path;
+// small layers as always.  k_sample has cleared the layers' state and
+// histogram copies.
+int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t nmain,
+                   uint32_t nfin, hipStream_t s)
+{
+    int rc;
+    if (nmain) {
+        rc = traced(lo, kKXFirst, s, [&] { return launch_x_first(a, nmain, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    for (uint32_t level = 0; ns && level < 3; ++level) {
+        if (level > 0) {
+            rc = traced(lo, kKXPass, s, [&] { return launch_x_pass(a, nfin, level, s); });
+            if (rc != LAGS_OK) return rc;
+        }
+        rc = traced(lo, kKXPick, s, [&] { return launch_x_pick(a, ns, level, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    if (ns) {
+        rc = traced(lo, kKXCount, s, [&] { return launch_x_count(a, nfin, s); });
+        if (rc != LAGS_OK) return rc;
+        rc = traced(lo, kKXCut, s, [&] { return launch_x_cut(a, ns, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    if (a.nsmall) {
+        SparsifyArgs b = a;
+        b.nsampled = 0;           // every workgroup of the launch is a small layer
+        rc = traced(lo, kKFinResolve, s, [&] { return launch_fin_resolve(b, b.nsmall, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    if (ns) {
+        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    return LAGS_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -552,6 +591,7 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     // k_sample always runs: its first workgroup restarts the report counters
     rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
     if (rc != LAGS_OK) return rc;
+    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, nfin, s);
     if (nmain) {
         rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
         if (rc != LAGS_OK) return rc;
@@ -702,8 +742,10 @@ int32_t lags_num_kernels(void) { return kNumKernels; }
 
 const char *lags_kernel_name(int32_t id)
 {
-    static const char *names[kNumKernels] = {"k_sample", "k_main", "k_fin_bins", "k_fin_select",
-                                             "k_fin_resolve", "k_fin_emit", "k_agg_starts", "k_agg"};
+    static const char *names[kNumKernels] = {"k_sample",     "k_main",     "k_fin_bins",   "k_fin_select",
+                                             "k_fin_resolve", "k_fin_emit", "k_agg_starts", "k_agg",
+                                             "k_x_first",    "k_x_pass",   "k_x_pick",     "k_x_count",
+                                             "k_x_cut"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 

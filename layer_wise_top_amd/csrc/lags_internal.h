@@ -125,7 +125,8 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t spare;
     uint32_t bstar;       // histogram bin holding the k-th largest candidate
     uint32_t c_above;     // candidates in bins above bstar
-    uint32_t reserved[2];
+    uint32_t xprefix;     // exact mode: key bits found so far
+    uint32_t xrank;       // exact mode: rank still to find among keys with that prefix
     uint32_t T;           // k-th largest key of the layer
     uint32_t idx_cut;     // largest global index taken among keys == T
     uint32_t pad0[22];
@@ -196,7 +197,8 @@ struct AggArgs {
 // kernel ids for tracing
 enum : int32_t {
     kKSample = 0, kKMain = 1, kKFinBins = 2, kKFinSelect = 3, kKFinResolve = 4,
-    kKFinEmit = 5, kKAggStarts = 6, kKAgg = 7, kNumKernels = 8
+    kKFinEmit = 5, kKAggStarts = 6, kKAgg = 7, kKXFirst = 8, kKXPass = 9, kKXPick = 10,
+    kKXCount = 11, kKXCut = 12, kNumKernels = 13
 };
 
 // launchers (lags_kernels.hip)
@@ -206,6 +208,11 @@ hipError_t launch_fin_bins(const SparsifyArgs &a, uint32_t nblocks, hipStream_t 
 hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_resolve(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_x_first(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_x_pass(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s);
+hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s);
+hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_x_cut(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
 hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s);
 

@@ -348,10 +348,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
     __syncthreads();
     if (a.force_exact) {
-        if (threadIdx.x == 0) {
-            st->G = 0xffffffffu;   // no key reaches it: the layer takes the exact path
-            st->SH = 0;
-        }
+        // exact mode: the radix select starts from an empty prefix at rank k
+        if (threadIdx.x == 0) st->xrank = L.k;
         return;
     }
     uint32_t cnt, rank, m = 0;
@@ -610,6 +608,8 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
     if (ln == 0) a.seg_count[w.seg_base + seg] = cw.run;
 }
 
+__device__ void dense_tile(const SparsifyArgs &a, const MainWork &w);
+
 // Only the candidate staging buffers live in LDS; the launch sets residency.
 __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 {
@@ -627,7 +627,12 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
         return;
     }
 
-    // k == n layer: every entry is sent
+    dense_tile(a, w);
+}
+
+// A k == n layer: every entry of tile w.tile is sent.
+__device__ void dense_tile(const SparsifyArgs &a, const MainWork &w)
+{
     const LayerInfo L = a.linfo[w.layer];
     const uint32_t lo = L.off + w.tile * kDenseTile;
     const uint32_t hi = min(lo + kDenseTile, L.off + L.n);
@@ -1258,6 +1263,359 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Exact mode (LAGS_SPARSIFY_EXACT): the threshold of every sampled layer by a
+// multi-workgroup MSD radix select over the 31-bit keys of acc, digits of
+// 11, 11 and 9 bits (key bits 30..20, 19..9, 8..0).  Each digit level is one
+// pass over the layer that histograms, in LDS, the digit of the keys that
+// match the prefix found so far and adds the histogram to the layer's copies
+// in device memory, followed by one workgroup per layer that picks the digit
+// holding the remaining rank.  Then per segment the keys above and equal to
+// the threshold T are counted, one workgroup per layer finds the tie cut
+// (the index of the e-th key equal to T, index order) and the message
+// offsets, and k_fin_emit re-reads every segment and emits its selection.
+
+constexpr uint32_t kXShift0 = 20u, kXShift1 = 9u;   // digit k: key bits [shift_k, shift_{k-1})
+__device__ __forceinline__ uint32_t x_shift(uint32_t level)
+{
+    return level == 0u ? kXShift0 : (level == 1u ? kXShift1 : 0u);
+}
+__device__ __forceinline__ uint32_t x_bins(uint32_t level) { return level < 2u ? 2048u : 512u; }
+
+// Walk one segment like walk_segment, with R rows of 64 float4 requested at
+// once.  fn must not store to the residual buffer.
+template <int R, class F>
+__device__ void walk_segment_rows(const SparsifyArgs &a, const FinWork &f, uint32_t seg, F &&fn)
+{
+    const uint32_t ln = lane_id();
+    const uint32_t end = f.off + f.n, b4 = end & ~3u;
+    uint32_t idx[4];
+    float v[4];
+    if (seg == 0 && f.off < f.a4) {
+        const uint32_t i = f.off + ln;
+        const bool in = i < f.a4;
+        idx[0] = idx[1] = idx[2] = idx[3] = i;
+        v[0] = in ? a.res[i] : 0.0f;
+        v[1] = v[2] = v[3] = 0.0f;
+        fn(in ? 1u : 0u, idx, v);
+    }
+    const uint32_t lo = f.a4 + seg * kSeg;
+    const uint32_t q0 = lo / 4u;
+    const uint32_t q1 = (uint32_t)min((uint64_t)lo + kSeg, (uint64_t)b4) / 4u;
+    const v4f *r4 = reinterpret_cast<const v4f *>(a.res);
+    for (uint32_t qb = q0; qb < q1; qb += 64u * R) {
+        v4f x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t q = qb + (uint32_t)r * 64u + ln;
+            x[r] = (q < q1) ? r4[q] : (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t q = qb + (uint32_t)r * 64u + ln;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                idx[j] = 4u * q + j;
+                v[j] = x[r][j];
+            }
+            fn(q < q1 ? 0xfu : 0u, idx, v);
+        }
+    }
+    if (seg == f.nseg - 1u && b4 < end) {
+        const uint32_t i = b4 + ln;
+        const bool in = i < end;
+        idx[0] = idx[1] = idx[2] = idx[3] = i;
+        v[0] = in ? a.res[i] : 0.0f;
+        v[1] = v[2] = v[3] = 0.0f;
+        fn(in ? 1u : 0u, idx, v);
+    }
+}
+
+// Per-wave LDS histograms (kWaves x 2048 words) added into histogram copy c
+// of the layer in device memory; all threads of the workgroup call.
+__device__ void x_flush(const uint32_t *hl, uint32_t *gh)
+{
+    __syncthreads();
+    for (uint32_t b = threadIdx.x; b < 2048u; b += kBlock) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += hl[w * 2048 + b];
+        if (c) atomicAdd(&gh[b], c);
+    }
+}
+
+__device__ __forceinline__ void x_clear(uint32_t *hl)
+{
+    for (uint32_t b = threadIdx.x; b < (uint32_t)kWaves * 2048u; b += kBlock) hl[b] = 0;
+    __syncthreads();
+}
+
+// k_x_first: the streaming pass of exact mode over the main work list.  A
+// sampled tile computes acc = grad + residual, stores it, and histograms the
+// first digit of every key; a k == n tile is sent whole as in k_main.
+__global__ __launch_bounds__(kBlock) void k_x_first(SparsifyArgs a)
+{
+    __shared__ uint32_t hl[kWaves * 2048];
+    const MainWork w = a.main_work[a.main_base + blockIdx.x];
+    if (w.cls != kClsSampled) {
+        dense_tile(a, w);
+        return;
+    }
+    x_clear(hl);
+    const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
+    uint32_t *h = hl + (threadIdx.x >> 6) * 2048u;
+    if (seg < w.nseg) {
+        const uint32_t ln = lane_id();
+        if (seg == 0 && w.off < w.a4) {
+            const uint32_t i = w.off + ln;
+            if (i < w.a4) {
+                const float x = a.grad[i] + a.res[i];
+                a.res[i] = x;
+                atomicAdd(&h[key_of(x) >> kXShift0], 1u);
+            }
+        }
+        const uint32_t e0 = w.a4 + seg * kSeg;
+        const uint32_t q1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4) / 4u;
+        const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
+        v4f *r4 = reinterpret_cast<v4f *>(a.res);
+        constexpr int U = 4;
+        for (uint32_t qb = e0 / 4u; qb < q1; qb += 64u * U) {
+            v4f acc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t q = qb + (uint32_t)u * 64u + ln;
+                acc[u] = (q < q1) ? __builtin_nontemporal_load(g4 + q) + __builtin_nontemporal_load(r4 + q)
+                                  : (v4f){0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t q = qb + (uint32_t)u * 64u + ln;
+                if (q < q1) {
+                    __builtin_nontemporal_store(acc[u], r4 + q);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) atomicAdd(&h[key_of(acc[u][j]) >> kXShift0], 1u);
+                }
+            }
+        }
+        if (seg == w.nseg - 1u && w.b4 < w.end) {
+            const uint32_t i = w.b4 + ln;
+            if (i < w.end) {
+                const float x = a.grad[i] + a.res[i];
+                a.res[i] = x;
+                atomicAdd(&h[key_of(x) >> kXShift0], 1u);
+            }
+        }
+    }
+    x_flush(hl, a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins);
+}
+
+// k_x_pass: digit `level` (1 or 2) of the keys that match the layer's prefix
+// above it, per finishing workgroup's segments, from acc in the residual buffer.
+__global__ __launch_bounds__(kBlock) void k_x_pass(SparsifyArgs a, uint32_t level)
+{
+    __shared__ uint32_t hl[kWaves * 2048];
+    const uint32_t fb = a.fin_base + blockIdx.x;
+    const FinWork f = a.fin_work[fb];
+    const SampledInfo S = a.sinfo[f.sid];
+    const uint32_t prefix = a.state[f.sid].xprefix;
+    x_clear(hl);
+    const uint32_t top = x_shift(level - 1u), sh = x_shift(level), mask = x_bins(level) - 1u;
+    uint32_t *h = hl + (threadIdx.x >> 6) * 2048u;
+    const uint32_t send = min(f.seg0 + f.grain, f.nseg);
+    for (uint32_t s = f.seg0 + (threadIdx.x >> 6); s < send; s += kWaves) {
+        walk_segment_rows<4>(a, f, s, [&](uint32_t valid, const uint32_t *, const float *v) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_of(v[j]);
+                if ((valid & (1u << j)) && (key >> top) == (prefix >> top))
+                    atomicAdd(&h[(key >> sh) & mask], 1u);
+            }
+        });
+    }
+    x_flush(hl, a.hist + S.hist_off + ((fb - f.fin_first) & (S.hcopies - 1u)) * kNBins);
+}
+
+// k_x_pick: one 1024-thread workgroup per sampled layer sums the histogram
+// copies of digit `level`, finds the digit holding the remaining rank, and
+// clears the copies for the next level.  After the last digit the prefix is
+// the threshold T and the remaining rank the number e of keys equal to T to
+// send.
+__global__ __launch_bounds__(kBinsThreads) void k_x_pick(SparsifyArgs a, uint32_t level)
+{
+    constexpr int NT = kBinsThreads;
+    __shared__ uint32_t hist[kNBins];
+    __shared__ uint32_t tmp[NT / 64];
+    __shared__ uint32_t res[2];
+    const uint32_t sid = a.sample_base + blockIdx.x;
+    const SampledInfo S = a.sinfo[sid];
+    SampledState *st = a.state + sid;
+    uint32_t *lh = a.hist + S.hist_off;
+    const uint32_t nb = x_bins(level);
+    for (uint32_t b = threadIdx.x; b < kNBins; b += NT) {
+        uint32_t h = 0;
+        if (b < nb) {
+            for (uint32_t c0 = 0; c0 < S.hcopies; c0 += 8) {
+                uint32_t v[8];
+#pragma unroll
+                for (uint32_t u = 0; u < 8; ++u) v[u] = (c0 + u < S.hcopies) ? lh[(c0 + u) * kNBins + b] : 0u;
+#pragma unroll
+                for (uint32_t u = 0; u < 8; ++u) h += v[u];
+            }
+        }
+        hist[b] = h;
+    }
+    __syncthreads();
+    const uint32_t rank = st->xrank;
+    block_find_rank<NT>(hist, max(nb, (uint32_t)NT), rank, res, tmp);
+    for (uint32_t t = threadIdx.x; t < S.hcopies * kNBins; t += NT) lh[t] = 0;
+    if (threadIdx.x == 0) {
+        const uint32_t prefix = st->xprefix | (res[0] << x_shift(level));
+        st->xprefix = prefix;
+        st->xrank = rank - res[1];
+        if (level == 2u) st->T = prefix;
+    }
+}
+
+// k_x_count: per segment, keys above T (into seg_sel) and equal to T (into
+// the layer's threshold-bin area, one word per segment); per finishing
+// workgroup, both totals.
+__global__ __launch_bounds__(kBlock) void k_x_count(SparsifyArgs a)
+{
+    __shared__ uint32_t wgt[kWaves], weq[kWaves];
+    const uint32_t fb = a.fin_base + blockIdx.x;
+    const FinWork f = a.fin_work[fb];
+    const uint32_t T = a.state[f.sid].T;
+    uint32_t *segeq = reinterpret_cast<uint32_t *>(a.tbin + (((uint64_t)f.slot_hi << 32) | f.slot_lo));
+    const uint32_t ln = lane_id(), wv = threadIdx.x >> 6;
+    const uint32_t send = min(f.seg0 + f.grain, f.nseg);
+    uint32_t tg = 0, te = 0;
+    for (uint32_t s = f.seg0 + wv; s < send; s += kWaves) {
+        uint32_t gt = 0, eq = 0;
+        walk_segment_rows<4>(a, f, s, [&](uint32_t valid, const uint32_t *, const float *v) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_of(v[j]);
+                if (valid & (1u << j)) {
+                    gt += (key > T) ? 1u : 0u;
+                    eq += (key == T) ? 1u : 0u;
+                }
+            }
+        });
+        gt = wave_sum(gt);
+        eq = wave_sum(eq);
+        if (ln == 0) {
+            a.seg_sel[f.seg_base + s] = gt;
+            segeq[s] = eq;
+        }
+        tg += gt;
+        te += eq;
+    }
+    if (ln == 0) {
+        wgt[wv] = tg;
+        weq[wv] = te;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t g = 0, e = 0;
+        for (int i = 0; i < kWaves; ++i) {
+            g += wgt[i];
+            e += weq[i];
+        }
+        a.fin_total[fb] = g;
+        a.fin_eq[fb] = e;
+    }
+}
+
+// k_x_cut: one workgroup per sampled layer.  Finds the segment s* holding
+// the e-th key equal to T (index order) and, re-reading it, that key's index
+// (the cut); then per segment the selected count (keys above T, plus its
+// keys equal to T up to the cut) and per finishing workgroup the message
+// offset, and marks every segment for re-reading by k_fin_emit.
+__global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
+{
+    __shared__ uint32_t tmp[kWaves];
+    __shared__ uint32_t res[3];
+    const uint32_t sid = a.sample_base + blockIdx.x;
+    const SampledInfo S = a.sinfo[sid];
+    SampledState *st = a.state + sid;
+    const FinWork f = a.fin_work[S.fin_first];     // the layer's static fields
+    const uint32_t *segeq =
+        reinterpret_cast<const uint32_t *>(a.tbin + (((uint64_t)S.slot_hi << 32) | S.slot_lo));
+    const uint32_t T = st->T, e = st->xrank;       // 1 <= e <= keys equal to T
+    if (threadIdx.x == 0) {       // (kept if the counts disagreed: bounded, never out of range)
+        res[0] = 0;
+        res[1] = 0;
+        res[2] = 0xffffffffu;
+    }
+    // the finishing workgroup holding the e-th tie
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
+        const uint32_t b = base + threadIdx.x;
+        const uint32_t z = (b < S.fin_nblocks) ? a.fin_eq[S.fin_first + b] : 0u;
+        uint32_t tot;
+        const uint32_t ex = carry + block_excl_scan(z, tmp, tot);
+        if (b < S.fin_nblocks && ex < e && e <= ex + z) {
+            res[0] = b;
+            res[1] = ex;
+        }
+        carry += tot;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {       // its segment holding the tie (at most kFinSegs)
+        uint32_t s = res[0] * f.grain, before = res[1];
+        while (s + 1u < f.nseg && before + segeq[s] < e) before += segeq[s++];
+        res[0] = s;
+        res[1] = before;
+    }
+    __syncthreads();
+    const uint32_t sstar = res[0], need = e - res[1];   // the need-th tie of segment s*
+    if (threadIdx.x < 64) {
+        uint32_t run = 0;
+        walk_segment_rows<4>(a, f, sstar, [&](uint32_t valid, const uint32_t *idx, const float *v) {
+            uint32_t tm = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((valid & (1u << j)) && key_of(v[j]) == T) tm |= 1u << j;
+            uint32_t tot;
+            uint32_t r = run + wave_prefix3((uint32_t)__popc(tm), tot);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (tm & (1u << j)) {
+                    ++r;
+                    if (r == need) res[2] = idx[j];
+                }
+            }
+            run += tot;
+        });
+    }
+    __syncthreads();
+    const uint32_t cut = res[2];
+    // selected per segment; message offset of each finishing workgroup
+    carry = 0;
+    for (uint32_t base = 0; base < f.nseg; base += kBlock) {
+        const uint32_t s = base + threadIdx.x;
+        uint32_t v = 0;
+        if (s < f.nseg) {
+            const uint32_t eq = segeq[s];
+            v = a.seg_sel[f.seg_base + s] + (s < sstar ? eq : (s == sstar ? need : 0u));
+        }
+        uint32_t tot;
+        const uint32_t ex = carry + block_excl_scan(v, tmp, tot);
+        if (s < f.nseg) {
+            a.seg_sel[f.seg_base + s] = v;
+            a.seg_count[f.seg_base + s] = 0xffffffffu;   // re-read by k_fin_emit
+            if (s % f.grain == 0u) a.fin_total[S.fin_first + s / f.grain] = ex;
+        }
+        carry += tot;
+    }
+    if (threadIdx.x == 0) {
+        st->idx_cut = cut;
+        st->status = kStOk;
+        atomicAdd(&a.report[kRepSampled], 1u);
+        atomicAdd(&a.report[kRepExact], 1u);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // aggregate
 
 // k_agg_starts: for every worker p and message position j in [j_lo, j_hi]
@@ -1523,6 +1881,36 @@ hipError_t launch_fin_resolve(const SparsifyArgs &a, uint32_t nblocks, hipStream
 hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     hipLaunchKernelGGL(k_fin_emit, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_x_first(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_x_first, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_x_pass(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_x_pass, dim3(nblocks), dim3(kBlock), 0, s, a, level);
+    return hipGetLastError();
+}
+
+hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_x_pick, dim3(nblocks), dim3(kBinsThreads), 0, s, a, level);
+    return hipGetLastError();
+}
+
+hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_x_count, dim3(nblocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_x_cut(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_x_cut, dim3(nblocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 

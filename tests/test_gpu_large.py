@@ -23,6 +23,28 @@ def _say(msg):
     print(msg, flush=True)
 
 
+def _exact_mode_agrees(run, g_d, r_d, sampled, tag):
+    """Sparsify the same gradient again in exact mode (the multi-workgroup
+    radix select; it shares no selection step with the sampled path) from a
+    zero residual: messages and residual must equal the sampled path's bits."""
+    import torch
+    from layer_wise_top_amd import lags
+    _say(f"{tag}: exact mode")
+    K = run.layout.K
+    r2 = torch.zeros_like(r_d)
+    mi2 = torch.empty(K, dtype=torch.int32, device="cuda")
+    mv2 = torch.empty(K, dtype=torch.float32, device="cuda")
+    lags.lags_sparsify_layers(run.layout, g_d, r2, mi2, mv2, run.ws, lags.LAGS_SPARSIFY_EXACT)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["layers_exact"] == sampled and rep["bad_entries"] == 0, rep
+    assert bool(torch.equal(mi2, run.msg_idx[0, :K])), f"{tag}: exact-mode msg_idx differs"
+    assert bool(torch.equal(mv2.view(torch.int32), run.msg_val[0, :K].view(torch.int32))), \
+        f"{tag}: exact-mode msg_val differs"
+    assert bool(torch.equal(r2.view(torch.int32), r_d.view(torch.int32))), f"{tag}: exact-mode residual differs"
+    del r2, mi2, mv2
+
+
 @pytest.mark.timeout(1200)
 def test_tfm1p3b_full_size(oracle):
     import torch
@@ -73,6 +95,9 @@ def test_tfm1p3b_full_size(oracle):
         tied_unsent = torch.nonzero(~s_l & (ks == T)).flatten()
         if tied_unsent.numel():
             assert int(tied_sent.max()) < int(tied_unsent.min())
+
+    del sent, key_g
+    _exact_mode_agrees(run, g_d, r_d, rep["layers_sampled"], "tfm1p3b")
 
     # ---- untouched weights keep their bits (whole buffer)
     touched = torch.zeros(wl.n, dtype=torch.bool, device="cuda")
@@ -137,6 +162,7 @@ def test_slgs1p3b_full_size(oracle):
     torch.cuda.synchronize()
     rep = run.report()
     assert rep["layers_exact"] == 0 and rep["bad_entries"] == 0, rep
+    _exact_mode_agrees(run, g_d, r_d, rep["layers_sampled"], "slgs1p3b")
 
     _say("host selection (acc = grad: the residual starts at zero)")
     key_h = g.view(np.int32) & np.int32(0x7FFFFFFF)

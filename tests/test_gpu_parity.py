@@ -113,8 +113,7 @@ LAYOUT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", LAYOUT_CASES, ids=lambda c: c[0])
-def test_layouts(oracle, case):
+def _layout_case(oracle, case, flags):
     name, sizes, ratio, kind, P, steps = case
     off = np.zeros(len(sizes) + 1, np.int64)
     off[1:] = np.cumsum(sizes)
@@ -139,10 +138,23 @@ def test_layouts(oracle, case):
                 loc = np.sort(rng.choice(sizes[l], int(k[l]), replace=False))
                 oi[p, moff[l]:moff[l + 1]] = loc + off[l]
             ov[p] = W.adversarial_values(1000 * step + p, K, "normal")
-        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, tag=f"{name}/{step}")
-    rep = run.report()
-    if kind in ("normal", "bf16") and name != "rand_k":
+        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, flags, tag=f"{name}/{step}")
+    return run.report()
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=lambda c: c[0])
+def test_layouts(oracle, case):
+    rep = _layout_case(oracle, case, 0)
+    if case[3] in ("normal", "bf16") and case[0] != "rand_k":
         assert rep["layers_exact"] == 0, rep
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES, ids=lambda c: c[0])
+def test_layouts_exact_mode(oracle, case):
+    """The same layouts with LAGS_SPARSIFY_EXACT: the multi-workgroup radix
+    select instead of the sampled guess, bit for bit the same results."""
+    _progress(f"[{case[0]}] exact mode")
+    _layout_case(oracle, case, 1)
 
 
 def test_vgg16(oracle):
@@ -206,7 +218,7 @@ def test_determinism():
         assert np.array_equal(a, b)
 
 
-def _single_layer_case(oracle, n, num, den, values, P=4, steps=1):
+def _single_layer_case(oracle, n, num, den, values, P=4, steps=1, flags=0):
     import torch
     off = np.array([0, n], np.int64)
     k = _k(oracle, off, num, den)
@@ -218,7 +230,7 @@ def _single_layer_case(oracle, n, num, den, values, P=4, steps=1):
         g = values(step)
         oi = np.stack([np.sort(rng.choice(n, int(k[0]), replace=False)) for _ in range(P - 1)]).astype(np.uint32)
         ov = rng.standard_normal(oi.shape).astype(np.float32)
-        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, tag=f"single n={n}/{step}")
+        r, w = _check_step(oracle, run, off, k, g, r, w, oi, ov, 0.1, flags, tag=f"single n={n}/{step}")
     return run.report()
 
 
@@ -229,6 +241,17 @@ def test_single_layer_100m(oracle):
     rep = _single_layer_case(oracle, n, 1, 1000,
                              lambda s: np.random.default_rng(7 + s).standard_normal(n, dtype=np.float32))
     assert rep["layers_exact"] == 0, rep
+
+
+@pytest.mark.parametrize("kind", ["normal", "bf16"])
+def test_single_layer_20m_exact_mode(oracle, kind):
+    """Exact mode on one 20M-entry layer (1250 finishing workgroups, 64
+    histogram copies); bf16-valued entries put many keys at the threshold,
+    so the tie cut falls inside a segment."""
+    n = 20_000_001
+    rep = _single_layer_case(oracle, n, 1, 1000, lambda s: W.adversarial_values(31 + s, n, kind),
+                             P=3, steps=2, flags=1)
+    assert rep["layers_exact"] == 1, rep
 
 
 def test_large_threshold_bin(oracle):
