@@ -27,8 +27,8 @@
 //   k_fin_resolve one workgroup per sampled layer: resolves the exact
 //                 threshold key T and the tie cut (lowest indices first) and
 //                 scans segment counts into message offsets.  A layer whose
-//                 guess failed (too few candidates or a full segment) is done
-//                 here by the exact multi-pass path.  One more workgroup per
+//                 guess failed (fewer than k candidates above a nonzero G) is
+//                 done here by the exact multi-pass path.  One more workgroup per
 //                 small layer (<= 4096 entries) does that layer start to
 //                 finish (exact radix select in LDS).
 //   k_fin_emit    writes the selected candidates of each segment, in index
@@ -36,6 +36,12 @@
 //                 with fewer than k nonzero keys (G = 0, "zero mode") sends
 //                 every nonzero entry and its lowest-index zeros; segments
 //                 that send zeros are re-read from the residual buffer.
+//   k_x_first, k_x_pass, k_x_pick, k_x_count, k_x_cut
+//                 exact mode (chosen by the caller): the threshold of every
+//                 sampled layer by a multi-workgroup radix select over all its
+//                 keys (three digit passes, each followed by a per-layer
+//                 pick), then per-segment counts, the tie cut and message
+//                 offsets; k_fin_emit re-reads every segment to emit.
 //   k_agg_starts  for every worker, where each index chunk starts in its
 //                 message (messages ascend per layer).
 //   k_agg         one workgroup per index chunk: worker-ordered sums in an LDS
