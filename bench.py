@@ -11,12 +11,18 @@ transformer gradient (1,311,178,752 fp32 entries in 193 tensors, rho = 1/1000,
 P = 16), the largest layout that fits one GPU.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
-                  [--no-cpu-baseline] [--flush] [--pipeline]
+                  [--no-cpu-baseline] [--flush] [--pipeline] [--no-exact-mode]
 
 --pipeline adds a second measurement of the same step issued layer range by
 layer range (lags_sparsify_range / lags_aggregate_range, last layers first),
 with the ranges of the merged-message schedule (lags_merge_schedule) under a
 synthetic cost model stated in pipeline_model().
+
+Every line also carries "exact_mode": the sparsify call with
+LAGS_SPARSIFY_EXACT (multi-workgroup radix select) from the state after the
+timed steps, its median time over five calls and whether its output equals
+the sampled path's bit for bit.  It runs after the timed region;
+--no-exact-mode leaves it out (profiles of the step alone).
 """
 from __future__ import annotations
 
@@ -238,7 +244,43 @@ def stream_ceiling_gbs(n, reps=5):
     return round(12 * n / (ms * 1e-3) / 1e9, 1)
 
 
-def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
+def exact_mode(lay, g_d, r_d, msg_idx0, msg_val0, ws, stream, reps):
+    """Sparsify in exact mode (the multi-workgroup radix select) from the
+    current residual: equal bit for bit to the sampled path from the same
+    state, and its time per call (events around each call; the residual is
+    restored outside them).  Not part of the step."""
+    import torch
+    from layer_wise_top_amd import lags
+    r0 = r_d.clone()
+    outs = []
+    for flags in (0, lags.LAGS_SPARSIFY_EXACT):
+        r = r0.clone()
+        mi = torch.empty_like(msg_idx0)
+        mv = torch.empty_like(msg_val0)
+        lags.lags_sparsify_layers(lay, g_d, r, mi, mv, ws, flags, stream)
+        outs.append((mi, mv.view(torch.int32), r.view(torch.int32)))
+    torch.cuda.synchronize()
+    rep = lags.lags_workspace_report(lay, ws)
+    same = all(bool(torch.equal(a, b)) for a, b in zip(outs[0], outs[1]))
+    r = outs[1][2].view(torch.float32)
+    mi, mv = outs[1][0], outs[1][1].view(torch.float32)
+    times = []
+    for _ in range(reps):
+        r.copy_(r0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lags.lags_sparsify_layers(lay, g_d, r, mi, mv, ws, lags.LAGS_SPARSIFY_EXACT, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del outs, r0, r, mi, mv
+    torch.cuda.empty_cache()
+    return {"sparsify_ms_median": round(float(np.median(times)), 5), "calls": reps,
+            "same_as_sampled": same, "layers_exact": rep["layers_exact"]}
+
+
+def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True):
     import torch
     from layer_wise_top_amd import lags, workloads as W
 
@@ -358,6 +400,8 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False):
     if times:
         out["step_ms_min"] = round(min(times), 5)
         out["step_ms_median"] = round(float(np.median(times)), 5)
+    if exact:
+        out["exact_mode"] = exact_mode(lay, g_d, r_d, mi[0], mv[0], ws, stream, 5)
     if pipeline:
         backward, nbytes, alpha, beta = pipeline_model(wl, k)
         runs, finish = lags.lags_merge_schedule(backward, nbytes, alpha, beta)
@@ -445,6 +489,8 @@ def main():
                          "Infinity Cache; steps are then timed one by one")
     ap.add_argument("--pipeline", action="store_true",
                     help="also time the step issued per merged-message layer range")
+    ap.add_argument("--no-exact-mode", action="store_true",
+                    help="leave out the exact-mode sparsify measured after the timed steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -472,7 +518,7 @@ def main():
             sys.exit(2)
     for name in names:
         out = run_config(name, args.steps, args.warmup, not args.no_cpu_baseline, args.flush,
-                         args.pipeline)
+                         args.pipeline, not args.no_exact_mode)
         print(json.dumps(out), flush=True)
 
 
