@@ -21,7 +21,8 @@ def _say(msg):
 @pytest.mark.parametrize("seed", list(range(8)))
 def test_random_layouts(oracle, seed):
     """Random layer sizes (1 .. 400000), random k in [1, n], a random value
-    kind per step, random P: messages, residuals and weights bit-exact."""
+    kind per step, random P: messages, residuals and weights bit-exact, and
+    the sparsify again in exact mode from the same residual, also bit-exact."""
     import torch
     rng = np.random.default_rng(zlib.crc32(f"random layout {seed}".encode()))
     L = int(rng.integers(1, 40))
@@ -62,6 +63,16 @@ def test_random_layouts(oracle, seed):
         assert_bits_equal("msg_idx", mi_g, mi_o)
         assert_bits_equal("msg_val", mv_g, mv_o)
         assert_bits_equal("residual", to_np_f32(r_d), r_o)
+        # exact mode from the same residual: the same bits
+        from layer_wise_top_amd import lags
+        r2 = to_dev(r)
+        mi2 = torch.empty(max(K, 1), dtype=torch.int32, device="cuda")
+        mv2 = torch.empty(max(K, 1), dtype=torch.float32, device="cuda")
+        lags.lags_sparsify_layers(run.layout, g_d, r2, mi2[:K], mv2[:K], run.ws, lags.LAGS_SPARSIFY_EXACT)
+        torch.cuda.synchronize()
+        assert_bits_equal("exact-mode msg_idx", mi2[:K].cpu().numpy().view(np.uint32), mi_o)
+        assert_bits_equal("exact-mode msg_val", to_np_f32(mv2[:K]), mv_o)
+        assert_bits_equal("exact-mode residual", to_np_f32(r2), r_o)
         ai = np.concatenate([mi_o[None], oi], 0) if P > 1 else mi_o[None]
         av = np.concatenate([mv_o[None], ov], 0) if P > 1 else mv_o[None]
         w_o = oracle.aggregate(ai, av, w, 0.05)
