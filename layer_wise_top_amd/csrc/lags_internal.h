@@ -12,10 +12,10 @@ namespace lags {
 // ---- launch geometry ------------------------------------------------------
 constexpr int kBlock = 256;              // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr uint32_t kSeg = 4096;          // entries per segment (one wave's stripe)
-constexpr uint32_t kTileSegs = 4;        // segments per streaming workgroup
+constexpr uint32_t kSeg = 4096;          // entries per segment (one streaming workgroup)
+constexpr uint32_t kTileSegs = 4;        // segments per streaming work entry (one workgroup each)
 constexpr uint32_t kSmallMax = 4096;     // layers up to this size: one workgroup, exact
-constexpr uint32_t kDenseTile = 16384;   // entries per workgroup for k == n layers
+constexpr uint32_t kDenseTile = 16384;   // entries per streaming work entry of a k == n layer
 constexpr uint32_t kSampleMax = 16384;   // sampled keys per layer (LDS resident)
 constexpr uint32_t kSampleChunk = 64;    // contiguous entries per sample chunk
 constexpr uint32_t kCapMax = 1024;       // candidate slots per segment, at most (beyond:

@@ -454,203 +454,168 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
     return min((key - G) >> SH, kNBins - 1u);
 }
 
-// Candidates of one segment, in index order.  They are staged in the wave's
-// LDS buffer and written to the segment's slots in contiguous bursts: isolated
-// 8-byte stores would each cost a partial-line write in memory.  Every
-// candidate, stored or beyond the segment's slots, is also counted in the
-// layer's bin histogram (device atomics; a few per segment).
-constexpr uint32_t kStage = 256;   // per wave; one row holds at most 4 x 64 candidates
+// One workgroup streams one segment of a sampled layer in a single step: each
+// thread requests kRows float4 rows of grad and residual at once (a row is
+// kBlock consecutive float4, so the workgroup covers one 16 KiB range per
+// array), writes acc = grad + residual back to the residual buffer, and flags
+// the entries with key >= G.  Measured on gfx950: workgroups that each read
+// 16 KiB per array in one step stream at ~6.2 TB/s, workgroups that loop over
+// 64 KiB at ~5.5 TB/s (the fewer address ranges in flight at once, the more
+// each opened DRAM row is reused).  When the guess is G = 0 (most of the layer
+// may be zero), only nonzero keys are flagged; the segment's zeros are then its
+// length minus its candidates.
+//
+// Candidates are numbered in index order (the layer's unaligned head, the
+// rows, the unaligned tail) by wave ballots and one exchange of wave totals in
+// LDS, staged in LDS and written to the segment's slots in one burst.  Every
+// candidate, stored or beyond the segment's slots, is also counted in one of
+// the layer's histogram copies (device atomics).
+constexpr int kRows = kSeg / 4u / kBlock;   // float4 rows per thread
+static_assert(kRows * 4 * kBlock == (int)kSeg, "a segment is kRows rows of the workgroup");
+constexpr int kParts = kRows + 2;           // head, rows, tail
 
-struct CandWriter {
-    uint2 *slots;      // the segment's slots
-    uint2 *stage;      // the wave's LDS buffer
-    uint32_t *hist;    // the layer's kNBins bins above G (bin width 2^SH)
-    uint32_t G, SH;
-    uint32_t cap;      // slots of the segment
-    uint32_t run;      // candidates so far (may exceed cap)
-    uint32_t flushed;  // candidates written to slots so far
-    uint32_t ln;
-
-    __device__ void flush()
-    {
-        const uint32_t n = run - flushed;   // staged, <= kStage
-        // other lanes' LDS writes before these reads, and these reads before
-        // the next appends overwrite the buffer (one wave: program order)
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        for (uint32_t t = ln; t < n; t += 64) {
-            const uint32_t pos = flushed + t;
-            const uint2 c = stage[t];
-            if (pos < cap) slots[pos] = c;      // a full segment is re-read later
-            atomicAdd(&hist[cand_bin(c.y & 0x7fffffffu, G, SH)], 1u);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        flushed = run;
-    }
-
-    // Append the flagged entries of a lane group (up to 4 per lane, index
-    // order lane-major, then j).  Wave-uniform call.
-    __device__ void append(uint32_t cmask, const uint32_t *idx, const float *v)
-    {
-        uint32_t tot;
-        const uint32_t pre = wave_prefix3((uint32_t)__popc(cmask), tot);
-        if (run - flushed + tot > kStage) flush();
-        uint32_t pos = run - flushed + pre;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (cmask & (1u << j)) {
-                stage[pos] = make_uint2(idx[j], __float_as_uint(v[j]));
-                ++pos;
-            }
-        }
-        run += tot;
-    }
-};
-
-// One wave streams one segment of a sampled layer: acc = grad + residual is
-// written back to the residual buffer, and entries with key >= G are appended
-// in index order to the segment's candidate slots.  When the guess is G = 0
-// (most of the layer may be zero), only nonzero keys are stored: the
-// segment's zeros are then its length minus its candidates.  Rows of 2 x 64
-// float4 per iteration (measured fastest on gfx950 for this loop).
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
-                                SampledState *st, uint32_t *hist, uint2 *stage)
+                                const SampledState *st, uint32_t *hist, uint2 *stage,
+                                uint32_t (*wtot)[kWaves])
 {
-    constexpr int U = 2;
-    const uint32_t ln = lane_id();
+    const uint32_t t = threadIdx.x, ln = lane_id(), wv = t >> 6;
     const uint32_t e0 = w.a4 + seg * kSeg;
-    const uint32_t e1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4);
-    const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * w.cap;
+    const uint32_t q0 = e0 / 4u;
+    const uint32_t q1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4) / 4u;
     const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
     v4f *r4 = reinterpret_cast<v4f *>(a.res);
-    const uint32_t q1 = e1 / 4u;
-    uint32_t q0 = e0 / 4u;
-    // the first rows are requested before the guess arrives
-    v4f gv[U], rv[U];
+    // every row is requested at once: the loads are unconditional, at rows
+    // clamped into the segment (q1 > q0), so no branch separates them; rows
+    // past the segment's end are neither stored nor flagged
+    v4f acc[kRows];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t q = q0 + u * 64u + ln;
+    for (int u = 0; u < kRows; ++u) {
+        const uint32_t q = min(q0 + (uint32_t)u * kBlock + t, q1 - 1u);
+        acc[u] = __builtin_nontemporal_load(g4 + q) + __builtin_nontemporal_load(r4 + q);
+    }
+    // the layer's unaligned head (segment 0) and tail (last segment), < 4 each
+    const uint32_t nh = seg == 0 ? w.a4 - w.off : 0u;
+    const uint32_t ntl = seg == w.nseg - 1u ? w.end - w.b4 : 0u;
+    float hv = 0.0f, tv = 0.0f;
+    if (t < nh) hv = a.grad[w.off + t] + a.res[w.off + t];
+    if (t < ntl) tv = a.grad[w.b4 + t] + a.res[w.b4 + t];
+    const uint32_t G = st->G, SH = st->SH;
+    const uint32_t Gs = G ? G : 1u;   // flagged: key >= Gs
+
+    uint32_t fl = 0;   // bit 4u + j: entry j of row u
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+        const uint32_t q = q0 + (uint32_t)u * kBlock + t;
         if (q < q1) {
-            gv[u] = __builtin_nontemporal_load(g4 + q);
-            rv[u] = __builtin_nontemporal_load(r4 + q);
-        } else {
-            gv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-            rv[u] = gv[u];
+            __builtin_nontemporal_store(acc[u], r4 + q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (key_of(acc[u][j]) >= Gs) fl |= 1u << (4 * u + j);
         }
     }
-    const uint32_t G = st->G;
-    const uint32_t Gs = G ? G : 1u;           // stored candidates: key >= Gs
-    CandWriter cw{a.slots + slot0, stage, hist, G, st->SH, w.cap, 0u, 0u, ln};
-    uint32_t idx[4];
-    float v[4];
+    if (t < nh) a.res[w.off + t] = hv;
+    if (t < ntl) a.res[w.b4 + t] = tv;
+    uint32_t c[kParts];
+    c[0] = (t < nh && key_of(hv) >= Gs) ? 1u : 0u;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fl >> (4 * u)) & 15u);
+    c[kParts - 1] = (t < ntl && key_of(tv) >= Gs) ? 1u : 0u;
 
-    if (seg == 0 && w.off < w.a4) {          // unaligned head of the layer
-        const uint32_t i = w.off + ln;
-        uint32_t cm = 0;
-        v[0] = v[1] = v[2] = v[3] = 0.0f;
-        idx[0] = idx[1] = idx[2] = idx[3] = i;
-        if (i < w.a4) {
-            v[0] = a.grad[i] + a.res[i];
-            a.res[i] = v[0];
-            if (key_of(v[0]) >= Gs) cm = 1;
-        }
-        cw.append(cm, idx, v);
+    // position of each part's first candidate: parts in order, waves in order
+    // inside a part, lanes in order inside a wave
+    uint32_t pos[kParts];
+    const bool any = __ballot(fl != 0u || c[0] != 0u || c[kParts - 1] != 0u) != 0;
+#pragma unroll
+    for (int r = 0; r < kParts; ++r) {
+        uint32_t tot = 0;
+        pos[r] = any ? wave_prefix3(c[r], tot) : 0u;
+        if (ln == 0) wtot[r][wv] = tot;
     }
-
-    while (true) {
+    __syncthreads();
+    uint32_t total = 0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t q = q0 + u * 64u + ln;
-            const v4f acc = gv[u] + rv[u];
-            uint32_t cm = 0;
-            if (q < q1) {
-                __builtin_nontemporal_store(acc, r4 + q);
+    for (int r = 0; r < kParts; ++r) {
+        uint32_t before = 0, tot = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (key_of(acc[j]) >= Gs) cm |= 1u << j;
-            }
-            if (__ballot(cm != 0)) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    idx[j] = 4u * q + j;
-                    v[j] = acc[j];
-                }
-                cw.append(cm, idx, v);
-            }
+        for (int i = 0; i < kWaves; ++i) {
+            const uint32_t x = wtot[r][i];
+            before += i < (int)wv ? x : 0u;
+            tot += x;
         }
-        // let this iteration's stores drain before the next rows are
-        // requested: without the wait the pass measured ~3% slower (stores
-        // piling up behind the loads)
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt untouched
-        q0 += 64u * U;
-        if (q0 >= q1) break;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t q = q0 + u * 64u + ln;
-            if (q < q1) {
-                gv[u] = __builtin_nontemporal_load(g4 + q);
-                rv[u] = __builtin_nontemporal_load(r4 + q);
-            } else {
-                gv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-                rv[u] = gv[u];
-            }
-        }
+        pos[r] += total + before;
+        total += tot;
     }
 
-    if (seg == w.nseg - 1 && w.b4 < w.end) {   // unaligned tail of the layer
-        const uint32_t i = w.b4 + ln;
-        uint32_t cm = 0;
-        v[0] = v[1] = v[2] = v[3] = 0.0f;
-        idx[0] = idx[1] = idx[2] = idx[3] = i;
-        if (i < w.end) {
-            v[0] = a.grad[i] + a.res[i];
-            a.res[i] = v[0];
-            if (key_of(v[0]) >= Gs) cm = 1;
-        }
-        cw.append(cm, idx, v);
+    const uint32_t cap = w.cap;
+    const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * cap;
+    auto put = [&](uint32_t p, uint32_t idx, float v) {
+        const uint2 e = make_uint2(idx, __float_as_uint(v));
+        if (p < kCapMax) stage[p] = e;
+        else if (p < cap) a.slots[slot0 + p] = e;   // only layers of <= kSampleMax entries
+                                                     // have more than kCapMax slots
+        atomicAdd(&hist[cand_bin(key_of(v), G, SH)], 1u);
+    };
+    if (c[0]) put(pos[0], w.off + t, hv);
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+        uint32_t p = pos[1 + u];
+        const uint32_t q = q0 + (uint32_t)u * kBlock + t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * q + j, acc[u][j]);
     }
-    cw.flush();
-    // all candidates, also those beyond the slots: the finishing kernels
-    // re-read a segment whose count exceeds its slots
-    if (ln == 0) a.seg_count[w.seg_base + seg] = cw.run;
+    if (c[kParts - 1]) put(pos[kParts - 1], w.b4 + t, tv);
+    __syncthreads();
+    // a segment with more candidates than slots keeps only the first cap
+    // (the finishing kernels re-read it)
+    const uint32_t ns = min(total, min(cap, kCapMax));
+    for (uint32_t i = t; i < ns; i += kBlock) a.slots[slot0 + i] = stage[i];
+    if (t == 0) a.seg_count[w.seg_base + seg] = total;
 }
 
-__device__ void dense_tile(const SparsifyArgs &a, const MainWork &w);
+__device__ void dense_tile(const SparsifyArgs &a, const MainWork &w, uint32_t part, uint32_t nparts);
 
-// Only the candidate staging buffers live in LDS; the launch sets residency.
+// Grid: kTileSegs workgroups per work entry.  A sampled tile's workgroup
+// takes one segment; a k == n tile is split into kTileSegs equal parts.
 __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 {
-    __shared__ uint2 stage[kWaves][kStage];
+    __shared__ uint2 stage[kCapMax];
+    __shared__ uint32_t wtot[kParts][kWaves];
 
-    const MainWork w = a.main_work[a.main_base + blockIdx.x];
+    const uint32_t part = blockIdx.x % kTileSegs;
+    const MainWork w = a.main_work[a.main_base + blockIdx.x / kTileSegs];
 
-    if (w.cls == kClsSampled) {   // streaming tile w.tile: one segment per wave
-        const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
+    if (w.cls == kClsSampled) {
+        const uint32_t seg = w.tile * kTileSegs + part;
         // consecutive workgroups take consecutive histogram copies
         if (seg < w.nseg)
             sampled_segment(a, w, seg, a.state + w.sid,
-                            a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins,
-                            stage[threadIdx.x >> 6]);
+                            a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins, stage, wtot);
         return;
     }
 
-    dense_tile(a, w);
+    dense_tile(a, w, part, kTileSegs);
 }
 
-// A k == n layer: every entry of tile w.tile is sent.
-__device__ void dense_tile(const SparsifyArgs &a, const MainWork &w)
+// A k == n layer: every entry of part `part` (of nparts) of tile w.tile is sent.
+__device__ void dense_tile(const SparsifyArgs &a, const MainWork &w, uint32_t part, uint32_t nparts)
 {
     const LayerInfo L = a.linfo[w.layer];
-    const uint32_t lo = L.off + w.tile * kDenseTile;
-    const uint32_t hi = min(lo + kDenseTile, L.off + L.n);
+    const uint32_t width = kDenseTile / nparts;
+    const uint64_t end = (uint64_t)L.off + L.n;
+    const uint32_t lo = (uint32_t)min((uint64_t)L.off + (uint64_t)w.tile * kDenseTile + (uint64_t)part * width, end);
+    const uint32_t hi = (uint32_t)min((uint64_t)lo + width, end);
     // batches of EPT entries per thread, all loads of a batch in flight
-    // before its stores (a store to the residual may alias a later load)
+    // before its stores (a store to the residual may alias a later load);
+    // the loads are unconditional, at indices clamped into the range, so that
+    // no branch separates them
     constexpr int EPT = 16;
     for (uint32_t i0 = lo + threadIdx.x; i0 < hi; i0 += EPT * kBlock) {
         float x[EPT];
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
-            const uint32_t i = i0 + u * kBlock;
-            x[u] = (i < hi) ? a.grad[i] + a.res[i] : 0.0f;
+            const uint32_t i = min(i0 + u * kBlock, hi - 1u);
+            x[u] = a.grad[i] + a.res[i];
         }
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
@@ -1363,7 +1328,7 @@ __global__ __launch_bounds__(kBlock) void k_x_first(SparsifyArgs a)
     __shared__ uint32_t hl[kWaves * 2048];
     const MainWork w = a.main_work[a.main_base + blockIdx.x];
     if (w.cls != kClsSampled) {
-        dense_tile(a, w);
+        dense_tile(a, w, 0, 1);
         return;
     }
     x_clear(hl);
@@ -1708,6 +1673,15 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     __shared__ uint32_t tmp[kWaves];
 
     const uint32_t c = a.c_lo + blockIdx.x;
+    const uint32_t P = a.P;
+    // The chunk starts of the first kBlock workers do not depend on the
+    // chunk's layer: request them together with the layer lookup.
+    uint32_t s0f = 0, s1f = 0;
+    if (threadIdx.x < P) {
+        const uint32_t *srow = a.start + (uint64_t)threadIdx.x * (a.NC + 1);
+        s0f = srow[c];
+        s1f = srow[c + 1];
+    }
     const uint32_t l = a.chunk_layer[c];
     const LayerInfo L = a.linfo[l];
     const uint32_t sh = a.csh[l];
@@ -1715,7 +1689,6 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     const uint64_t hi64 = min(lo64 + (1ull << sh), (uint64_t)L.off + L.n);
     const uint32_t lo = (uint32_t)lo64, hi = (uint32_t)hi64;
     const uint32_t m0 = L.moff, m1 = L.moff + L.k;
-    const uint32_t P = a.P;
 
     uint32_t carry = 0;
     for (uint32_t base = 0; base < P; base += kBlock) {
@@ -1723,7 +1696,7 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
         uint32_t m = 0;
         if (p < P) {
             const uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
-            uint32_t s0 = srow[c], s1 = srow[c + 1];
+            uint32_t s0 = base == 0 ? s0f : srow[c], s1 = base == 0 ? s1f : srow[c + 1];
             s0 = min(max(s0, m0), m1);
             s1 = min(max(s1, s0), m1);
             ws0[p] = s0;
@@ -1796,14 +1769,24 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
                 if (slot[q] >= 0 && wk[q] == p) vals[slot[q]] = vals[slot[q]] + v[q];
             __syncthreads();
         }
-        // apply at every touched index
-        for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
-            const uint32_t key = keys[t];
-            if (key != 0xffffffffu) {
-                const uint32_t x = lo + key;
-                a.w[x] = __fsub_rn(a.w[x], __fmul_rn(s, vals[t]));
-            }
+        // apply at every touched index: every weight load of the thread is
+        // requested before the first store (a store may alias a later load as
+        // far as the compiler knows, so a plain loop waits one memory round
+        // trip per slot)
+        constexpr int TPT = kAggTable / kBlock;
+        uint32_t tk[TPT];
+        float tu[TPT], tw[TPT];
+#pragma unroll
+        for (int q = 0; q < TPT; ++q) {
+            tk[q] = keys[threadIdx.x + q * kBlock];
+            tu[q] = vals[threadIdx.x + q * kBlock];
         }
+#pragma unroll
+        for (int q = 0; q < TPT; ++q)
+            tw[q] = tk[q] != 0xffffffffu ? a.w[lo + tk[q]] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < TPT; ++q)
+            if (tk[q] != 0xffffffffu) a.w[lo + tk[q]] = __fsub_rn(tw[q], __fmul_rn(s, tu[q]));
     } else {
         // dense windows over the chunk's index range; every entry is visited
         // once per window, workers in order
@@ -1858,11 +1841,14 @@ hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    // Unused dynamic LDS caps residency at 5 workgroups (20 waves) per CU: the
-    // streaming pass measured about 5% faster so than at the full 32 waves
-    // (more concurrent streams cost more than the extra loads in flight gain).
-    constexpr size_t kResidencyPad = 24000;
-    hipLaunchKernelGGL(k_main, dim3(nblocks), dim3(kBlock), kResidencyPad, s, a);
+    // kTileSegs workgroups per work entry.  Unused dynamic LDS sets how many
+    // workgroups a CU holds (static LDS ~8.3 KB): 5 for large launches, 7 for
+    // smaller ones.  Measured: 1.31B entries (320K workgroups) 2.46 ms at 4-5
+    // per CU, 2.57 at 6, 2.63 at 7, 2.66 at 8, 2.77 at 3; 15M-66M entries
+    // (3.7K-16K workgroups) fastest at 7, 1-3% slower at 5.
+    const uint32_t ngroups = nblocks * kTileSegs;
+    const size_t pad = ngroups >= 65536u ? 24000 : 15000;
+    hipLaunchKernelGGL(k_main, dim3(ngroups), dim3(kBlock), pad, s, a);
     return hipGetLastError();
 }
 
