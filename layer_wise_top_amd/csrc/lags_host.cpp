@@ -181,9 +181,7 @@ int build_plan(lags_layout *lo)
             }
             si.slot_lo = (uint32_t)(slot_base & 0xffffffffu);
             si.slot_hi = (uint32_t)(slot_base >> 32);
-            // finer finishing workgroups for smaller layers: more of them run
-            // at once, and the larger layers keep fewer reservation atomics
-            const uint32_t grain = si.nseg <= kFinSmallLayer ? kFinSegsSmall : kFinSegs;
+            const uint32_t grain = fin_grain(si.nseg);
             si.fin_nblocks = (si.nseg + grain - 1) / grain;
             // every candidate the layer can store fits its threshold-bin list,
             // so a large bin (many equal keys) never forces the exact path
@@ -416,14 +414,14 @@ int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t
     }
     for (uint32_t level = 0; ns && level < 3; ++level) {
         if (level > 0) {
-            rc = traced(lo, kKXPass, s, [&] { return launch_x_pass(a, nfin, level, s); });
+            rc = traced(lo, kKXPass, s, [&] { return launch_x_pass(a, nmain, level, s); });
             if (rc != LAGS_OK) return rc;
         }
         rc = traced(lo, kKXPick, s, [&] { return launch_x_pick(a, ns, level, s); });
         if (rc != LAGS_OK) return rc;
     }
     if (ns) {
-        rc = traced(lo, kKXCount, s, [&] { return launch_x_count(a, nfin, s); });
+        rc = traced(lo, kKXCount, s, [&] { return launch_x_count(a, nmain, s); });
         if (rc != LAGS_OK) return rc;
         rc = traced(lo, kKXCut, s, [&] { return launch_x_cut(a, ns, s); });
         if (rc != LAGS_OK) return rc;
@@ -435,7 +433,7 @@ int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t
         if (rc != LAGS_OK) return rc;
     }
     if (ns) {
-        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
+        rc = traced(lo, kKXEmit, s, [&] { return launch_x_emit(a, nmain, s); });
         if (rc != LAGS_OK) return rc;
     }
     return LAGS_OK;
@@ -745,7 +743,7 @@ const char *lags_kernel_name(int32_t id)
     static const char *names[kNumKernels] = {"k_sample",     "k_main",     "k_fin_bins",   "k_fin_select",
                                              "k_fin_resolve", "k_fin_emit", "k_agg_starts", "k_agg",
                                              "k_x_first",    "k_x_pass",   "k_x_pick",     "k_x_count",
-                                             "k_x_cut"};
+                                             "k_x_cut",      "k_x_emit"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 

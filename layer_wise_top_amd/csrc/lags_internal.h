@@ -27,6 +27,13 @@ constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LD
 constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup (at most)
 constexpr uint32_t kFinSegsSmall = 16;   // ... in a layer of at most kFinSmallLayer segments
 constexpr uint32_t kFinSmallLayer = 1024;
+// segments per finishing workgroup of a layer of nseg segments: finer for
+// smaller layers (more of them run at once; the larger layers keep fewer
+// reservation atomics)
+__host__ __device__ inline uint32_t fin_grain(uint32_t nseg)
+{
+    return nseg <= kFinSmallLayer ? kFinSegsSmall : kFinSegs;
+}
 // aggregate
 constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
 constexpr uint32_t kAggCap = 1024;            // fast-path capacity (entries per chunk)
@@ -198,7 +205,7 @@ struct AggArgs {
 enum : int32_t {
     kKSample = 0, kKMain = 1, kKFinBins = 2, kKFinSelect = 3, kKFinResolve = 4,
     kKFinEmit = 5, kKAggStarts = 6, kKAgg = 7, kKXFirst = 8, kKXPass = 9, kKXPick = 10,
-    kKXCount = 11, kKXCut = 12, kNumKernels = 13
+    kKXCount = 11, kKXCut = 12, kKXEmit = 13, kNumKernels = 14
 };
 
 // launchers (lags_kernels.hip)
@@ -213,6 +220,7 @@ hipError_t launch_x_pass(const SparsifyArgs &a, uint32_t nblocks, uint32_t level
 hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s);
 hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_x_cut(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_x_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
 hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s);
 

@@ -447,88 +447,71 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// k_main: the streaming pass.
-
-__device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t SH)
-{
-    return min((key - G) >> SH, kNBins - 1u);
-}
-
-// One workgroup streams one segment of a sampled layer in a single step: each
-// thread requests kRows float4 rows of grad and residual at once (a row is
-// kBlock consecutive float4, so the workgroup covers one 16 KiB range per
-// array), writes acc = grad + residual back to the residual buffer, and flags
-// the entries with key >= G.  Measured on gfx950: workgroups that each read
-// 16 KiB per array in one step stream at ~6.2 TB/s, workgroups that loop over
-// 64 KiB at ~5.5 TB/s (the fewer address ranges in flight at once, the more
-// each opened DRAM row is reused).  When the guess is G = 0 (most of the layer
-// may be zero), only nonzero keys are flagged; the segment's zeros are then its
-// length minus its candidates.
-//
-// Candidates are numbered in index order (the layer's unaligned head, the
-// rows, the unaligned tail) by wave ballots and one exchange of wave totals in
-// LDS, staged in LDS and written to the segment's slots in one burst.  Every
-// candidate, stored or beyond the segment's slots, is also counted in one of
-// the layer's histogram copies (device atomics).
+// One segment per workgroup.  The streaming pass and the exact-mode passes
+// give each 4096-entry segment of a sampled layer one 256-thread workgroup
+// that requests all of the segment at once: thread t holds the float4 rows
+// q0 + u * kBlock + t (u < kRows) of the segment's aligned interior, and entry
+// t of the layer's unaligned head (segment 0) and tail (last segment), fewer
+// than 4 each.  Measured on gfx950: workgroups that each read 16 KiB per array
+// in one step stream at ~6.2 TB/s, workgroups that loop over 64 KiB at ~5.5
+// TB/s (the fewer address ranges in flight at once, the more each opened DRAM
+// row is reused).
 constexpr int kRows = kSeg / 4u / kBlock;   // float4 rows per thread
 static_assert(kRows * 4 * kBlock == (int)kSeg, "a segment is kRows rows of the workgroup");
-constexpr int kParts = kRows + 2;           // head, rows, tail
+constexpr int kParts = kRows + 2;           // head, rows, tail: index order
 
-__device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
-                                const SampledState *st, uint32_t *hist, uint2 *stage,
-                                uint32_t (*wtot)[kWaves])
+struct SegView {
+    uint32_t q0, q1;      // float4 rows [q0, q1) of the segment's aligned interior
+    uint32_t hlo, nh;     // head entries [hlo, hlo + nh)
+    uint32_t tlo, ntl;    // tail entries [tlo, tlo + ntl)
+    __device__ uint32_t row(int u) const { return q0 + (uint32_t)u * kBlock + threadIdx.x; }
+    __device__ bool row_in(int u) const { return row(u) < q1; }
+};
+
+__device__ __forceinline__ SegView seg_view(const MainWork &w, uint32_t seg)
 {
-    const uint32_t t = threadIdx.x, ln = lane_id(), wv = t >> 6;
+    SegView v;
     const uint32_t e0 = w.a4 + seg * kSeg;
-    const uint32_t q0 = e0 / 4u;
-    const uint32_t q1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4) / 4u;
-    const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
-    v4f *r4 = reinterpret_cast<v4f *>(a.res);
-    // every row is requested at once: the loads are unconditional, at rows
-    // clamped into the segment (q1 > q0), so no branch separates them; rows
-    // past the segment's end are neither stored nor flagged
-    v4f acc[kRows];
+    v.q0 = e0 / 4u;
+    v.q1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4) / 4u;
+    v.hlo = w.off;
+    v.nh = seg == 0 ? w.a4 - w.off : 0u;
+    v.tlo = w.b4;
+    v.ntl = seg == w.nseg - 1u ? w.end - w.b4 : 0u;
+    return v;
+}
+
+// Request every row of the thread at once: the loads are unconditional, at
+// rows clamped into the segment (q1 > q0), so no branch separates them.  Rows
+// past the segment's end (row_in false) hold a copy of its last row and must
+// not be used.
+template <bool NT>
+__device__ __forceinline__ void seg_rows(const float *p, const SegView &v, v4f (&x)[kRows])
+{
+    const v4f *p4 = reinterpret_cast<const v4f *>(p);
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
-        const uint32_t q = min(q0 + (uint32_t)u * kBlock + t, q1 - 1u);
-        acc[u] = __builtin_nontemporal_load(g4 + q) + __builtin_nontemporal_load(r4 + q);
+        const uint32_t q = min(v.row(u), v.q1 - 1u);
+        x[u] = NT ? __builtin_nontemporal_load(p4 + q) : p4[q];
     }
-    // the layer's unaligned head (segment 0) and tail (last segment), < 4 each
-    const uint32_t nh = seg == 0 ? w.a4 - w.off : 0u;
-    const uint32_t ntl = seg == w.nseg - 1u ? w.end - w.b4 : 0u;
-    float hv = 0.0f, tv = 0.0f;
-    if (t < nh) hv = a.grad[w.off + t] + a.res[w.off + t];
-    if (t < ntl) tv = a.grad[w.b4 + t] + a.res[w.b4 + t];
-    const uint32_t G = st->G, SH = st->SH;
-    const uint32_t Gs = G ? G : 1u;   // flagged: key >= Gs
+}
 
-    uint32_t fl = 0;   // bit 4u + j: entry j of row u
+// Positions, in index order over the workgroup, of the entries each thread
+// flags: c[r] (< 8) flagged entries of the thread in part r.  On return pos[r]
+// is the position of the first of them; returns the workgroup's total.  All
+// threads call; one barrier; wtot (LDS) may be reused only after another.
+__device__ uint32_t block_positions(const uint32_t (&c)[kParts], uint32_t (&pos)[kParts],
+                                    uint32_t (*wtot)[kWaves])
+{
+    const uint32_t ln = lane_id(), wv = threadIdx.x >> 6;
+    uint32_t any = 0;
 #pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-        const uint32_t q = q0 + (uint32_t)u * kBlock + t;
-        if (q < q1) {
-            __builtin_nontemporal_store(acc[u], r4 + q);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (key_of(acc[u][j]) >= Gs) fl |= 1u << (4 * u + j);
-        }
-    }
-    if (t < nh) a.res[w.off + t] = hv;
-    if (t < ntl) a.res[w.b4 + t] = tv;
-    uint32_t c[kParts];
-    c[0] = (t < nh && key_of(hv) >= Gs) ? 1u : 0u;
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fl >> (4 * u)) & 15u);
-    c[kParts - 1] = (t < ntl && key_of(tv) >= Gs) ? 1u : 0u;
-
-    // position of each part's first candidate: parts in order, waves in order
-    // inside a part, lanes in order inside a wave
-    uint32_t pos[kParts];
-    const bool any = __ballot(fl != 0u || c[0] != 0u || c[kParts - 1] != 0u) != 0;
+    for (int r = 0; r < kParts; ++r) any |= c[r];
+    const bool wany = __ballot(any != 0u) != 0;
 #pragma unroll
     for (int r = 0; r < kParts; ++r) {
         uint32_t tot = 0;
-        pos[r] = any ? wave_prefix3(c[r], tot) : 0u;
+        pos[r] = wany ? wave_prefix3(c[r], tot) : 0u;
         if (ln == 0) wtot[r][wv] = tot;
     }
     __syncthreads();
@@ -545,6 +528,59 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
         pos[r] += total + before;
         total += tot;
     }
+    return total;
+}
+
+// ---------------------------------------------------------------------------
+// k_main: the streaming pass.  One workgroup per segment of a sampled layer:
+// acc = grad + residual is written back to the residual buffer, and the
+// entries with key >= G are candidates.  When the guess is G = 0 (most of the
+// layer may be zero), only nonzero keys are candidates; the segment's zeros
+// are then its length minus its candidates.  Candidates are numbered in index
+// order, staged in LDS and written to the segment's slots in one burst; every
+// candidate, stored or beyond the segment's slots, is also counted in one of
+// the layer's histogram copies (device atomics).
+
+__device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t SH)
+{
+    return min((key - G) >> SH, kNBins - 1u);
+}
+
+__device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
+                                const SampledState *st, uint32_t *hist, uint2 *stage,
+                                uint32_t (*wtot)[kWaves])
+{
+    const uint32_t t = threadIdx.x;
+    const SegView sv = seg_view(w, seg);
+    v4f acc[kRows], rv[kRows];
+    seg_rows<true>(a.grad, sv, acc);
+    seg_rows<true>(a.res, sv, rv);
+    float hv = 0.0f, tv = 0.0f;
+    if (t < sv.nh) hv = a.grad[sv.hlo + t] + a.res[sv.hlo + t];
+    if (t < sv.ntl) tv = a.grad[sv.tlo + t] + a.res[sv.tlo + t];
+    const uint32_t G = st->G, SH = st->SH;
+    const uint32_t Gs = G ? G : 1u;   // candidates: key >= Gs
+
+    v4f *r4 = reinterpret_cast<v4f *>(a.res);
+    uint32_t fl = 0;   // bit 4u + j: entry j of row u
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+        acc[u] = acc[u] + rv[u];
+        if (sv.row_in(u)) {
+            __builtin_nontemporal_store(acc[u], r4 + sv.row(u));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (key_of(acc[u][j]) >= Gs) fl |= 1u << (4 * u + j);
+        }
+    }
+    if (t < sv.nh) a.res[sv.hlo + t] = hv;
+    if (t < sv.ntl) a.res[sv.tlo + t] = tv;
+    uint32_t c[kParts], pos[kParts];
+    c[0] = (t < sv.nh && key_of(hv) >= Gs) ? 1u : 0u;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fl >> (4 * u)) & 15u);
+    c[kParts - 1] = (t < sv.ntl && key_of(tv) >= Gs) ? 1u : 0u;
+    const uint32_t total = block_positions(c, pos, wtot);
 
     const uint32_t cap = w.cap;
     const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * cap;
@@ -555,16 +591,15 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
                                                      // have more than kCapMax slots
         atomicAdd(&hist[cand_bin(key_of(v), G, SH)], 1u);
     };
-    if (c[0]) put(pos[0], w.off + t, hv);
+    if (c[0]) put(pos[0], sv.hlo + t, hv);
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
         uint32_t p = pos[1 + u];
-        const uint32_t q = q0 + (uint32_t)u * kBlock + t;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * q + j, acc[u][j]);
+            if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * sv.row(u) + j, acc[u][j]);
     }
-    if (c[kParts - 1]) put(pos[kParts - 1], w.b4 + t, tv);
+    if (c[kParts - 1]) put(pos[kParts - 1], sv.tlo + t, tv);
     __syncthreads();
     // a segment with more candidates than slots keeps only the first cap
     // (the finishing kernels re-read it)
@@ -1301,108 +1336,124 @@ __device__ void walk_segment_rows(const SparsifyArgs &a, const FinWork &f, uint3
     }
 }
 
-// Per-wave LDS histograms (kWaves x 2048 words) added into histogram copy c
-// of the layer in device memory; all threads of the workgroup call.
+// The workgroup's LDS histogram (2048 words) added into histogram copy gh of
+// the layer in device memory, nonzero bins only; all threads call.
 __device__ void x_flush(const uint32_t *hl, uint32_t *gh)
 {
     __syncthreads();
-    for (uint32_t b = threadIdx.x; b < 2048u; b += kBlock) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += hl[w * 2048 + b];
-        if (c) atomicAdd(&gh[b], c);
-    }
+    for (uint32_t b = threadIdx.x; b < 2048u; b += kBlock)
+        if (hl[b]) atomicAdd(&gh[b], hl[b]);
 }
 
 __device__ __forceinline__ void x_clear(uint32_t *hl)
 {
-    for (uint32_t b = threadIdx.x; b < (uint32_t)kWaves * 2048u; b += kBlock) hl[b] = 0;
+    for (uint32_t b = threadIdx.x; b < 2048u; b += kBlock) hl[b] = 0;
     __syncthreads();
 }
 
-// k_x_first: the streaming pass of exact mode over the main work list.  A
-// sampled tile computes acc = grad + residual, stores it, and histograms the
-// first digit of every key; a k == n tile is sent whole as in k_main.
+// The exact-mode passes run, like k_main, one workgroup per segment over the
+// main work list (kTileSegs workgroups per entry); a workgroup whose entry is
+// not a sampled tile, or whose segment is past the layer's end, has nothing
+// to do (k_x_first sends the k == n tiles whole, as k_main does).
+__device__ __forceinline__ bool x_segment(const SparsifyArgs &a, MainWork &w, uint32_t &seg)
+{
+    w = a.main_work[a.main_base + blockIdx.x / kTileSegs];
+    seg = w.tile * kTileSegs + blockIdx.x % kTileSegs;
+    return w.cls == kClsSampled && seg < w.nseg;
+}
+
+// Acc of the segment from the residual buffer (after the first pass), with
+// the head and tail entries of the thread.
+struct XSeg {
+    SegView sv;
+    v4f x[kRows];
+    float hv, tv;
+    __device__ void load(const SparsifyArgs &a, const MainWork &w, uint32_t seg)
+    {
+        const uint32_t t = threadIdx.x;
+        sv = seg_view(w, seg);
+        seg_rows<false>(a.res, sv, x);
+        hv = t < sv.nh ? a.res[sv.hlo + t] : 0.0f;
+        tv = t < sv.ntl ? a.res[sv.tlo + t] : 0.0f;
+    }
+    // fn(index, value) for every entry the thread holds
+    template <class F>
+    __device__ void each(F &&fn) const
+    {
+        const uint32_t t = threadIdx.x;
+        if (t < sv.nh) fn(sv.hlo + t, hv);
+#pragma unroll
+        for (int u = 0; u < kRows; ++u)
+            if (sv.row_in(u)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) fn(4u * sv.row(u) + j, x[u][j]);
+            }
+        if (t < sv.ntl) fn(sv.tlo + t, tv);
+    }
+};
+
+// k_x_first: the streaming pass of exact mode.  A sampled segment computes
+// acc = grad + residual, stores it, and histograms the first digit of every
+// key; a k == n tile is sent whole as in k_main.
 __global__ __launch_bounds__(kBlock) void k_x_first(SparsifyArgs a)
 {
-    __shared__ uint32_t hl[kWaves * 2048];
-    const MainWork w = a.main_work[a.main_base + blockIdx.x];
-    if (w.cls != kClsSampled) {
-        dense_tile(a, w, 0, 1);
+    __shared__ uint32_t hl[2048];
+    MainWork w;
+    uint32_t seg;
+    if (!x_segment(a, w, seg)) {
+        if (w.cls != kClsSampled) dense_tile(a, w, blockIdx.x % kTileSegs, kTileSegs);
         return;
     }
     x_clear(hl);
-    const uint32_t seg = w.tile * kTileSegs + (threadIdx.x >> 6);
-    uint32_t *h = hl + (threadIdx.x >> 6) * 2048u;
-    if (seg < w.nseg) {
-        const uint32_t ln = lane_id();
-        if (seg == 0 && w.off < w.a4) {
-            const uint32_t i = w.off + ln;
-            if (i < w.a4) {
-                const float x = a.grad[i] + a.res[i];
-                a.res[i] = x;
-                atomicAdd(&h[key_of(x) >> kXShift0], 1u);
-            }
-        }
-        const uint32_t e0 = w.a4 + seg * kSeg;
-        const uint32_t q1 = (uint32_t)min((uint64_t)e0 + kSeg, (uint64_t)w.b4) / 4u;
-        const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
-        v4f *r4 = reinterpret_cast<v4f *>(a.res);
-        constexpr int U = 4;
-        for (uint32_t qb = e0 / 4u; qb < q1; qb += 64u * U) {
-            v4f acc[U];
+    const uint32_t t = threadIdx.x;
+    const SegView sv = seg_view(w, seg);
+    v4f acc[kRows], rv[kRows];
+    seg_rows<true>(a.grad, sv, acc);
+    seg_rows<true>(a.res, sv, rv);
+    float hv = 0.0f, tv = 0.0f;
+    if (t < sv.nh) hv = a.grad[sv.hlo + t] + a.res[sv.hlo + t];
+    if (t < sv.ntl) tv = a.grad[sv.tlo + t] + a.res[sv.tlo + t];
+    uint32_t *h = hl;
+    v4f *r4 = reinterpret_cast<v4f *>(a.res);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t q = qb + (uint32_t)u * 64u + ln;
-                acc[u] = (q < q1) ? __builtin_nontemporal_load(g4 + q) + __builtin_nontemporal_load(r4 + q)
-                                  : (v4f){0.f, 0.f, 0.f, 0.f};
-            }
+    for (int u = 0; u < kRows; ++u) {
+        acc[u] = acc[u] + rv[u];
+        if (sv.row_in(u)) {
+            __builtin_nontemporal_store(acc[u], r4 + sv.row(u));
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t q = qb + (uint32_t)u * 64u + ln;
-                if (q < q1) {
-                    __builtin_nontemporal_store(acc[u], r4 + q);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) atomicAdd(&h[key_of(acc[u][j]) >> kXShift0], 1u);
-                }
-            }
+            for (int j = 0; j < 4; ++j) atomicAdd(&h[key_of(acc[u][j]) >> kXShift0], 1u);
         }
-        if (seg == w.nseg - 1u && w.b4 < w.end) {
-            const uint32_t i = w.b4 + ln;
-            if (i < w.end) {
-                const float x = a.grad[i] + a.res[i];
-                a.res[i] = x;
-                atomicAdd(&h[key_of(x) >> kXShift0], 1u);
-            }
-        }
+    }
+    if (t < sv.nh) {
+        a.res[sv.hlo + t] = hv;
+        atomicAdd(&h[key_of(hv) >> kXShift0], 1u);
+    }
+    if (t < sv.ntl) {
+        a.res[sv.tlo + t] = tv;
+        atomicAdd(&h[key_of(tv) >> kXShift0], 1u);
     }
     x_flush(hl, a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins);
 }
 
-// k_x_pass: digit `level` (1 or 2) of the keys that match the layer's prefix
-// above it, per finishing workgroup's segments, from acc in the residual buffer.
+// k_x_pass: digit `level` (1 or 2) of the segment's keys that match the
+// layer's prefix above it, from acc in the residual buffer.
 __global__ __launch_bounds__(kBlock) void k_x_pass(SparsifyArgs a, uint32_t level)
 {
-    __shared__ uint32_t hl[kWaves * 2048];
-    const uint32_t fb = a.fin_base + blockIdx.x;
-    const FinWork f = a.fin_work[fb];
-    const SampledInfo S = a.sinfo[f.sid];
-    const uint32_t prefix = a.state[f.sid].xprefix;
+    __shared__ uint32_t hl[2048];
+    MainWork w;
+    uint32_t seg;
+    if (!x_segment(a, w, seg)) return;
     x_clear(hl);
+    XSeg xs;
+    xs.load(a, w, seg);
+    const uint32_t prefix = a.state[w.sid].xprefix;
     const uint32_t top = x_shift(level - 1u), sh = x_shift(level), mask = x_bins(level) - 1u;
-    uint32_t *h = hl + (threadIdx.x >> 6) * 2048u;
-    const uint32_t send = min(f.seg0 + f.grain, f.nseg);
-    for (uint32_t s = f.seg0 + (threadIdx.x >> 6); s < send; s += kWaves) {
-        walk_segment_rows<4>(a, f, s, [&](uint32_t valid, const uint32_t *, const float *v) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t key = key_of(v[j]);
-                if ((valid & (1u << j)) && (key >> top) == (prefix >> top))
-                    atomicAdd(&h[(key >> sh) & mask], 1u);
-            }
-        });
-    }
-    x_flush(hl, a.hist + S.hist_off + ((fb - f.fin_first) & (S.hcopies - 1u)) * kNBins);
+    uint32_t *h = hl;
+    xs.each([&](uint32_t, float v) {
+        const uint32_t key = key_of(v);
+        if ((key >> top) == (prefix >> top)) atomicAdd(&h[(key >> sh) & mask], 1u);
+    });
+    x_flush(hl, a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins);
 }
 
 // k_x_pick: one 1024-thread workgroup per sampled layer sums the histogram
@@ -1438,6 +1489,8 @@ __global__ __launch_bounds__(kBinsThreads) void k_x_pick(SparsifyArgs a, uint32_
     const uint32_t rank = st->xrank;
     block_find_rank<NT>(hist, max(nb, (uint32_t)NT), rank, res, tmp);
     for (uint32_t t = threadIdx.x; t < S.hcopies * kNBins; t += NT) lh[t] = 0;
+    if (level == 2u)   // k_x_count adds into the finishing workgroups' tie counts
+        for (uint32_t b = threadIdx.x; b < S.fin_nblocks; b += NT) a.fin_eq[S.fin_first + b] = 0;
     if (threadIdx.x == 0) {
         const uint32_t prefix = st->xprefix | (res[0] << x_shift(level));
         st->xprefix = prefix;
@@ -1447,42 +1500,31 @@ __global__ __launch_bounds__(kBinsThreads) void k_x_pick(SparsifyArgs a, uint32_
 }
 
 // k_x_count: per segment, keys above T (into seg_sel) and equal to T (into
-// the layer's threshold-bin area, one word per segment); per finishing
-// workgroup, both totals.
+// the layer's threshold-bin area, one word per segment); the keys equal to T
+// are also added to the tie count of the segment's finishing workgroup
+// (cleared by the last k_x_pick), which k_x_cut scans.
 __global__ __launch_bounds__(kBlock) void k_x_count(SparsifyArgs a)
 {
     __shared__ uint32_t wgt[kWaves], weq[kWaves];
-    const uint32_t fb = a.fin_base + blockIdx.x;
-    const FinWork f = a.fin_work[fb];
-    const uint32_t T = a.state[f.sid].T;
-    uint32_t *segeq = reinterpret_cast<uint32_t *>(a.tbin + (((uint64_t)f.slot_hi << 32) | f.slot_lo));
-    const uint32_t ln = lane_id(), wv = threadIdx.x >> 6;
-    const uint32_t send = min(f.seg0 + f.grain, f.nseg);
-    uint32_t tg = 0, te = 0;
-    for (uint32_t s = f.seg0 + wv; s < send; s += kWaves) {
-        uint32_t gt = 0, eq = 0;
-        walk_segment_rows<4>(a, f, s, [&](uint32_t valid, const uint32_t *, const float *v) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t key = key_of(v[j]);
-                if (valid & (1u << j)) {
-                    gt += (key > T) ? 1u : 0u;
-                    eq += (key == T) ? 1u : 0u;
-                }
-            }
-        });
-        gt = wave_sum(gt);
-        eq = wave_sum(eq);
-        if (ln == 0) {
-            a.seg_sel[f.seg_base + s] = gt;
-            segeq[s] = eq;
-        }
-        tg += gt;
-        te += eq;
-    }
-    if (ln == 0) {
-        wgt[wv] = tg;
-        weq[wv] = te;
+    MainWork w;
+    uint32_t seg;
+    if (!x_segment(a, w, seg)) return;
+    XSeg xs;
+    xs.load(a, w, seg);
+    const uint32_t T = a.state[w.sid].T;
+    const uint32_t fin_first = a.sinfo[w.sid].fin_first;
+    uint32_t gt = 0, eq = 0;
+    xs.each([&](uint32_t, float v) {
+        const uint32_t key = key_of(v);
+        gt += key > T ? 1u : 0u;
+        eq += key == T ? 1u : 0u;
+    });
+    gt = wave_sum(gt);
+    eq = wave_sum(eq);
+    const uint32_t wv = threadIdx.x >> 6;
+    if (lane_id() == 0) {
+        wgt[wv] = gt;
+        weq[wv] = eq;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1491,16 +1533,17 @@ __global__ __launch_bounds__(kBlock) void k_x_count(SparsifyArgs a)
             g += wgt[i];
             e += weq[i];
         }
-        a.fin_total[fb] = g;
-        a.fin_eq[fb] = e;
+        uint32_t *segeq = reinterpret_cast<uint32_t *>(a.tbin + (((uint64_t)w.slot_hi << 32) | w.slot_lo));
+        a.seg_sel[w.seg_base + seg] = g;
+        segeq[seg] = e;
+        if (e) atomicAdd(&a.fin_eq[fin_first + seg / fin_grain(w.nseg)], e);
     }
 }
 
 // k_x_cut: one workgroup per sampled layer.  Finds the segment s* holding
 // the e-th key equal to T (index order) and, re-reading it, that key's index
 // (the cut); then per segment the selected count (keys above T, plus its
-// keys equal to T up to the cut) and per finishing workgroup the message
-// offset, and marks every segment for re-reading by k_fin_emit.
+// keys equal to T up to the cut), scanned into the segment's message offset.
 __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
 {
     __shared__ uint32_t tmp[kWaves];
@@ -1560,7 +1603,8 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
     }
     __syncthreads();
     const uint32_t cut = res[2];
-    // selected per segment; message offset of each finishing workgroup
+    // selected per segment, scanned into each segment's message offset
+    // inside the layer (seg_sel, read by k_x_emit)
     carry = 0;
     for (uint32_t base = 0; base < f.nseg; base += kBlock) {
         const uint32_t s = base + threadIdx.x;
@@ -1571,11 +1615,7 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
         }
         uint32_t tot;
         const uint32_t ex = carry + block_excl_scan(v, tmp, tot);
-        if (s < f.nseg) {
-            a.seg_sel[f.seg_base + s] = v;
-            a.seg_count[f.seg_base + s] = 0xffffffffu;   // re-read by k_fin_emit
-            if (s % f.grain == 0u) a.fin_total[S.fin_first + s / f.grain] = ex;
-        }
+        if (s < f.nseg) a.seg_sel[f.seg_base + s] = ex;
         carry += tot;
     }
     if (threadIdx.x == 0) {
@@ -1584,6 +1624,60 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
         atomicAdd(&a.report[kRepSampled], 1u);
         atomicAdd(&a.report[kRepExact], 1u);
     }
+}
+
+// k_x_emit: one workgroup per segment re-reads acc and writes the segment's
+// selection (key > T, or key == T and index <= cut) in index order from the
+// layer's message offset plus the segment's (from k_x_cut); sent entries'
+// residual becomes +0.0.
+__global__ __launch_bounds__(kBlock) void k_x_emit(SparsifyArgs a)
+{
+    __shared__ uint32_t wtot[kParts][kWaves];
+    MainWork w;
+    uint32_t seg;
+    if (!x_segment(a, w, seg)) return;
+    XSeg xs;
+    xs.load(a, w, seg);
+    const SampledState *st = a.state + w.sid;
+    const LayerInfo L = a.linfo[w.layer];
+    const uint32_t base = L.moff + a.seg_sel[w.seg_base + seg];
+    if (st->status != kStOk) return;   // uniform; k_x_cut resolves every layer
+    const uint32_t T = st->T, cut = st->idx_cut;
+    const uint32_t t = threadIdx.x;
+    auto sel = [&](uint32_t idx, float v) {
+        const uint32_t key = key_of(v);
+        return key > T || (key == T && idx <= cut);
+    };
+    uint32_t fl = 0, c[kParts], pos[kParts];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u)
+        if (xs.sv.row_in(u)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (sel(4u * xs.sv.row(u) + j, xs.x[u][j])) fl |= 1u << (4 * u + j);
+        }
+    c[0] = (t < xs.sv.nh && sel(xs.sv.hlo + t, xs.hv)) ? 1u : 0u;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fl >> (4 * u)) & 15u);
+    c[kParts - 1] = (t < xs.sv.ntl && sel(xs.sv.tlo + t, xs.tv)) ? 1u : 0u;
+    block_positions(c, pos, wtot);
+    const uint32_t mend = L.moff + L.k;
+    auto put = [&](uint32_t p, uint32_t idx, float v) {
+        if (p < mend) {            // the layer's selection holds exactly k entries
+            a.msg_idx[p] = idx;
+            a.msg_val[p] = v;
+        }
+        a.res[idx] = 0.0f;
+    };
+    if (c[0]) put(base + pos[0], xs.sv.hlo + t, xs.hv);
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+        uint32_t p = base + pos[1 + u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * xs.sv.row(u) + j, xs.x[u][j]);
+    }
+    if (c[kParts - 1]) put(base + pos[kParts - 1], xs.sv.tlo + t, xs.tv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1833,6 +1927,19 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
 // ---------------------------------------------------------------------------
 // launchers
 
+// Unused dynamic LDS that sets how many one-segment workgroups a CU holds
+// (160 KiB of LDS per CU): a workgroup takes 36,000 B in launches of 64K
+// workgroups and more (4 per CU), 23,000 B below (6-7 per CU).  Measured on
+// the streaming pass, total LDS per workgroup: 1.31B entries (320K
+// workgroups) 2.44-2.46 ms at 32,288-36,000 B, 2.56-2.58 at 32,000, 2.59 at
+// 27,000, 2.65 at 23,000, 2.77 at 54,000 (3 per CU); 15M-66M entries
+// (3.7K-16K workgroups) fastest at 23,000 B, up to 6% slower at 32,288.
+size_t stream_lds_pad(uint32_t ngroups, size_t static_lds)
+{
+    const size_t total = ngroups >= 65536u ? 36000 : 23000;
+    return total > static_lds ? total - static_lds : 0;
+}
+
 hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     hipLaunchKernelGGL(k_sample, dim3(nblocks), dim3(kSampleThreads), 0, s, a);
@@ -1841,14 +1948,9 @@ hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    // kTileSegs workgroups per work entry.  Unused dynamic LDS sets how many
-    // workgroups a CU holds (static LDS ~8.3 KB): 5 for large launches, 7 for
-    // smaller ones.  Measured: 1.31B entries (320K workgroups) 2.46 ms at 4-5
-    // per CU, 2.57 at 6, 2.63 at 7, 2.66 at 8, 2.77 at 3; 15M-66M entries
-    // (3.7K-16K workgroups) fastest at 7, 1-3% slower at 5.
     const uint32_t ngroups = nblocks * kTileSegs;
-    const size_t pad = ngroups >= 65536u ? 24000 : 15000;
-    hipLaunchKernelGGL(k_main, dim3(ngroups), dim3(kBlock), pad, s, a);
+    hipLaunchKernelGGL(k_main, dim3(ngroups), dim3(kBlock),
+                       stream_lds_pad(ngroups, (kCapMax * 2 + kParts * kWaves) * 4), s, a);
     return hipGetLastError();
 }
 
@@ -1878,13 +1980,15 @@ hipError_t launch_fin_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t 
 
 hipError_t launch_x_first(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_x_first, dim3(nblocks), dim3(kBlock), 0, s, a);
+    const uint32_t ngroups = nblocks * kTileSegs;
+    hipLaunchKernelGGL(k_x_first, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, 2048 * 4), s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_x_pass(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_x_pass, dim3(nblocks), dim3(kBlock), 0, s, a, level);
+    const uint32_t ngroups = nblocks * kTileSegs;
+    hipLaunchKernelGGL(k_x_pass, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, 2048 * 4), s, a, level);
     return hipGetLastError();
 }
 
@@ -1896,7 +2000,16 @@ hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level
 
 hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_x_count, dim3(nblocks), dim3(kBlock), 0, s, a);
+    const uint32_t ngroups = nblocks * kTileSegs;
+    hipLaunchKernelGGL(k_x_count, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, 2 * kWaves * 4), s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_x_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+{
+    const uint32_t ngroups = nblocks * kTileSegs;
+    hipLaunchKernelGGL(k_x_emit, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, kParts * kWaves * 4),
+                       s, a);
     return hipGetLastError();
 }
 
