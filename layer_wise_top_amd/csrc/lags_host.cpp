@@ -46,7 +46,8 @@ struct lags_layout {
     std::vector<uint32_t> small_layers;
     std::vector<FinWork> fin_work;
     std::vector<uint32_t> pos_layer;
-    uint32_t starts_tl = 0;        // LDS table entries the start pass needs
+    uint32_t starts_tl = 0;        // LDS table entries the start pass needs (one block per workgroup)
+    uint32_t starts_tl4 = 0;       // ... four blocks per workgroup
     // per-layer prefix counts of the work lists, for layer-range launches:
     // small-layer work entries, streaming work entries, sampled layers and
     // finishing workgroups before layer l
@@ -253,11 +254,14 @@ int build_plan(lags_layout *lo)
     // before the block's first to the layer of the next block's first
     // position, and one more moff entry
     lo->starts_tl = 0;
+    lo->starts_tl4 = 0;
     for (uint64_t b = 0; b < npb; ++b) {
         const uint32_t l0 = lo->pos_layer[b];
-        const uint32_t l1 = (b + 1 < npb) ? lo->pos_layer[b + 1] : (uint32_t)L - 1;
         const uint32_t la = l0 > 0 ? l0 - 1 : 0;
+        const uint32_t l1 = (b + 1 < npb) ? lo->pos_layer[b + 1] : (uint32_t)L - 1;
+        const uint32_t l4 = (b + 4 < npb) ? lo->pos_layer[b + 4] : (uint32_t)L - 1;
         lo->starts_tl = std::max(lo->starts_tl, l1 - la + 2);
+        lo->starts_tl4 = std::max(lo->starts_tl4, l4 - la + 2);
     }
 
     const size_t ns = lo->sinfo.size();
@@ -670,7 +674,12 @@ int lags_aggregate_range(const lags_layout *clo, int32_t l0, int32_t l1, float *
     a.c_lo = t->h_cbase[l0];
     a.c_hi = t->h_cbase[l1];
     a.npb = (uint32_t)lo->pos_layer.size();
-    a.tl = lo->starts_tl;
+    // four position blocks per start-pass workgroup once the launch would
+    // take several rounds of workgroups (16K or more), else one
+    const uint64_t nblk = (uint64_t)(a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u) * (uint32_t)P;
+    const bool wide = nblk >= 16384 && 5ull * lo->starts_tl4 * 4 <= 32768;
+    a.bpw = wide ? 4u : 1u;
+    a.tl = wide ? lo->starts_tl4 : lo->starts_tl;
     rc = traced(lo, kKAggStarts, s, [&] { return launch_agg_starts(a, s); });
     if (rc != LAGS_OK) return rc;
     return traced(lo, kKAgg, s, [&] { return launch_agg(a, a.c_hi - a.c_lo, s); });

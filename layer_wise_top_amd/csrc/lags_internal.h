@@ -37,7 +37,7 @@ __host__ __device__ inline uint32_t fin_grain(uint32_t nseg)
 // aggregate
 constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
 constexpr uint32_t kAggCap = 1024;            // fast-path capacity (entries per chunk)
-constexpr uint32_t kStartsBlock = 1024;       // message positions per start-pass workgroup
+constexpr uint32_t kStartsBlock = 1024;       // message positions per start-pass block
 constexpr uint32_t kAggTableLog2 = 11;
 constexpr uint32_t kAggTable = 1u << kAggTableLog2;  // LDS hash slots (>= 2 * kAggCap);
                                                      // also the slow path's dense window
@@ -198,7 +198,8 @@ struct AggArgs {
     uint32_t j_lo, j_hi;
     uint32_t c_lo, c_hi;
     uint32_t npb;               // entries of pos_layer
-    uint32_t tl;                // start pass: LDS table entries (layers a block spans, plus 2)
+    uint32_t tl;                // start pass: LDS table entries (layers a workgroup spans, plus 2)
+    uint32_t bpw;               // start pass: position blocks per workgroup (1 or 4)
 };
 
 // kernel ids for tracing

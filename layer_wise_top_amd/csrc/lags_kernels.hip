@@ -1689,33 +1689,38 @@ __global__ __launch_bounds__(kBlock) void k_x_emit(SparsifyArgs a)
 // first and the one-past-last chunk of the range, so a call reads only its own
 // message entries and writes only the starts of chunks [c_lo, c_hi]; the
 // shared boundary start c_hi gets the same value from either neighbour.  A
-// workgroup covers kStartsBlock positions of one worker, all requested at
-// once; the layers they span are staged in LDS, in five tables of a.tl
-// entries (dynamic LDS, sized by the host for the layout's widest block: at
-// most kStartsBlock + 3, since every layer sends at least one entry).
+// workgroup covers BPW blocks of kStartsBlock positions of one worker (4 in
+// large launches, so that fewer rounds of workgroups wait on the two memory
+// round trips below; 1 in small ones, which would not fill the GPU), all
+// requested at once; the layers they span are staged in LDS, in five tables of
+// a.tl entries (dynamic LDS, sized by the host for the layout's widest span).
+template <int BPW>
 __global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
 {
-    constexpr int PPT = kStartsBlock / kBlock;      // positions per thread
+    constexpr int PPT = BPW * kStartsBlock / kBlock;   // positions per thread
     extern __shared__ uint32_t tab[];
     uint32_t *t_off = tab, *t_n = tab + a.tl, *t_moff = tab + 2u * a.tl, *t_cb = tab + 3u * a.tl,
              *t_sh = tab + 4u * a.tl;
     __shared__ uint32_t lrange[2];
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) a.report[kRepBad + threadIdx.x] = 0;
     const uint32_t p = blockIdx.y;
-    const uint32_t bb = a.j_lo / kStartsBlock + blockIdx.x;   // absolute position block
+    const uint32_t bb = a.j_lo / kStartsBlock + blockIdx.x * BPW;   // first absolute position block
     const uint32_t j0 = bb * kStartsBlock;
     const uint32_t *row = a.msg_idx + (uint64_t)p * a.K;
-    // message entries first: they do not depend on the layer lookup
+    // message entries first: they do not depend on the layer lookup.  The
+    // loads are unconditional, at positions clamped into [j_lo, j_hi) (not
+    // empty), so that none waits for another; positions outside it are not
+    // used below.
     uint32_t x[PPT], xp[PPT];
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const uint32_t j = j0 + threadIdx.x + q * kBlock;
-        x[q] = (j >= a.j_lo && j < a.j_hi) ? row[j] : 0u;
-        xp[q] = (j > a.j_lo && j <= a.j_hi) ? row[j - 1] : 0u;
+        x[q] = row[min(max(j, a.j_lo), a.j_hi - 1u)];
+        xp[q] = row[min(max(j, a.j_lo + 1u), a.j_hi) - 1u];
     }
     if (threadIdx.x == 0) {
         const uint32_t l0 = a.pos_layer[bb];
-        const uint32_t l1 = (bb + 1 < a.npb) ? a.pos_layer[bb + 1] : a.L - 1;
+        const uint32_t l1 = (bb + BPW < a.npb) ? a.pos_layer[bb + BPW] : a.L - 1;
         lrange[0] = l0 > 0 ? l0 - 1 : 0;   // the layer of position j0 - 1 may precede l0
         lrange[1] = l1;
     }
@@ -2021,8 +2026,14 @@ hipError_t launch_x_cut(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
 {
-    const uint32_t nx = a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u;
-    hipLaunchKernelGGL(k_agg_starts, dim3(nx, a.P), dim3(kBlock), 5u * a.tl * sizeof(uint32_t), s, a);
+    const uint32_t nb = a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u;
+    const size_t lds = 5u * a.tl * sizeof(uint32_t);
+    if (a.bpw == 4)
+        hipLaunchKernelGGL(k_agg_starts<4>, dim3((nb + 3u) / 4u, a.P), dim3(kBlock), lds, s, a);
+    else if (a.bpw == 1)
+        hipLaunchKernelGGL(k_agg_starts<1>, dim3(nb, a.P), dim3(kBlock), lds, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -197,6 +197,58 @@ def test_aggregate_concentrated_chunk(oracle):
     assert run.report()["slow_chunks"] > 0
 
 
+def _stratified_messages(rng, off, k, P):
+    """Per worker and layer, k_l distinct ascending indices (one uniform draw
+    in each of k_l equal strata of the layer) and normal values."""
+    rows_i, rows_v = [], []
+    for _ in range(P):
+        parts = []
+        for l in range(len(k)):
+            n_l, k_l = int(off[l + 1] - off[l]), int(k[l])
+            lo = (np.arange(k_l, dtype=np.int64) * n_l) // k_l
+            hi = (np.arange(1, k_l + 1, dtype=np.int64) * n_l) // k_l
+            parts.append(off[l] + lo + (rng.random(k_l) * (hi - lo)).astype(np.int64))
+        rows_i.append(np.concatenate(parts).astype(np.uint32))
+        rows_v.append(rng.standard_normal(int(k.sum())).astype(np.float32))
+    return np.stack(rows_i), np.stack(rows_v)
+
+
+def test_aggregate_wide_start_pass(oracle):
+    """Enough workers and message positions that the chunk-start pass takes
+    four position blocks per workgroup (16K blocks and more per launch), in
+    one call and in three layer ranges whose message ranges start at
+    unaligned positions."""
+    import torch
+    from layer_wise_top_amd import lags
+    sizes = [5000, 3_000_000, 12_345, 7_000_000, 999, 4_500_001, 2_000_000, 3_456_789, 77]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    k = np.array([(n + 63) // 64 for n in sizes], np.int64)
+    P = 128
+    assert (int(k.sum()) // 1024 + 1) * P >= 16384
+    assert (int(k[3:7].sum()) // 1024) * P >= 16384   # the middle range is wide on its own
+    rng = np.random.default_rng(21)
+    idx, val = _stratified_messages(rng, off, k, P)
+    w = W.adversarial_values(14, int(off[-1]), "normal")
+    _progress("[wide starts] oracle")
+    w_o = oracle.aggregate(idx, val, w, 0.1)
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(idx))
+    run.msg_val.copy_(to_dev(val))
+    _progress("[wide starts] one call")
+    w_d = to_dev(w)
+    run.aggregate(w_d, 0.1)
+    torch.cuda.synchronize()
+    assert_bits_equal("weights (one call)", to_np_f32(w_d), w_o)
+    _progress("[wide starts] three ranges")
+    w_d = to_dev(w)
+    for l0, l1 in [(7, 9), (0, 3), (3, 7)]:
+        lags.lags_aggregate_range(run.layout, l0, l1, w_d, run.msg_idx, run.msg_val, P, 0.1, run.ws)
+    torch.cuda.synchronize()
+    assert_bits_equal("weights (ranges)", to_np_f32(w_d), w_o)
+    rep = run.report()
+    assert rep["bad_entries"] == 0
+
+
 def test_determinism():
     """Two runs from the same inputs give identical bytes."""
     import torch
