@@ -13,12 +13,13 @@
 //                 sample as a threshold guess G that at least k entries of the
 //                 layer exceed with overwhelming probability; also clears the
 //                 layer's per-call state.
-//   k_main        the streaming pass: acc = grad + residual is written back
-//                 to the residual buffer; entries with |acc| key >= G (>= 1
-//                 when G = 0: zeros are not stored) are compacted, in index
-//                 order, into per-segment candidate slots, and counted in the
-//                 layer's histogram of bins above G.  k == n layers are sent
-//                 whole.
+//   k_main        the streaming pass, one workgroup per 4096-entry segment
+//                 requesting all of it at once: acc = grad + residual is
+//                 written back to the residual buffer; entries with |acc| key
+//                 >= G (>= 1 when G = 0: zeros are not stored) are compacted,
+//                 in index order, into per-segment candidate slots, and
+//                 counted in the layer's histogram of bins above G.  k == n
+//                 layers are sent whole.
 //   k_fin_bins    one workgroup per sampled layer: sums the layer's
 //                 histogram copies and finds the bin holding the k-th largest
 //                 candidate.
@@ -36,12 +37,14 @@
 //                 with fewer than k nonzero keys (G = 0, "zero mode") sends
 //                 every nonzero entry and its lowest-index zeros; segments
 //                 that send zeros are re-read from the residual buffer.
-//   k_x_first, k_x_pass, k_x_pick, k_x_count, k_x_cut
+//   k_x_first, k_x_pass, k_x_pick, k_x_count, k_x_cut, k_x_emit
 //                 exact mode (chosen by the caller): the threshold of every
 //                 sampled layer by a multi-workgroup radix select over all its
 //                 keys (three digit passes, each followed by a per-layer
 //                 pick), then per-segment counts, the tie cut and message
-//                 offsets; k_fin_emit re-reads every segment to emit.
+//                 offsets; k_x_emit re-reads every segment to emit.  The
+//                 passes over a layer take k_main's one-workgroup-per-segment
+//                 shape.
 //   k_agg_starts  for every worker, where each index chunk starts in its
 //                 message (messages ascend per layer).
 //   k_agg         one workgroup per index chunk: worker-ordered sums in an LDS
