@@ -160,6 +160,39 @@ __device__ uint32_t block_excl_small(uint32_t c, uint32_t *tmp, uint32_t &total)
     return before + pre;
 }
 
+// Exclusive scan, in item order, of the counts of n items (n may be large):
+// rounds of kBlock * E items, thread t taking the E consecutive items from
+// base + t * E, all requested at once (val is called at indices clamped into
+// [0, n) and must only read).  out(i, excl, count) receives each item's
+// exclusive prefix; it may overwrite what val reads for the same round.
+// Returns the total.  All threads of a kBlock workgroup call.
+template <int E, class Val, class Out>
+__device__ uint32_t block_scan_items(uint32_t n, uint32_t *tmp, const Val &val, const Out &out)
+{
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < n; base += kBlock * E) {
+        const uint32_t i0 = base + threadIdx.x * E;
+        uint32_t x[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = val(min(i0 + e, n - 1u));
+        uint32_t sum = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (i0 + e >= n) x[e] = 0;
+            sum += x[e];
+        }
+        uint32_t tot;
+        uint32_t run = carry + block_excl_scan(sum, tmp, tot);   // its barriers end the round's reads
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (i0 + e < n) out(i0 + e, run, x[e]);
+            run += x[e];
+        }
+        carry += tot;
+    }
+    return carry;
+}
+
 template <int NT = kBlock>
 __device__ uint32_t block_max(uint32_t v, uint32_t *tmp)
 {
@@ -1122,15 +1155,9 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     wait_mem_done();
     __syncthreads();
     // per-workgroup totals -> exclusive message offsets (in place)
-    uint32_t carry = 0;
-    for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
-        const uint32_t b = base + threadIdx.x;
-        const uint32_t v = (b < S.fin_nblocks) ? ld_coherent(&a.fin_total[S.fin_first + b]) : 0u;
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan(v, tmp, tot);
-        if (b < S.fin_nblocks) a.fin_total[S.fin_first + b] = carry + ex;
-        carry += tot;
-    }
+    block_scan_items<16>(
+        S.fin_nblocks, tmp, [&](uint32_t b) { return ld_coherent(&a.fin_total[S.fin_first + b]); },
+        [&](uint32_t b, uint32_t ex, uint32_t) { a.fin_total[S.fin_first + b] = ex; });
     if (threadIdx.x == 0) {
         st->T = T;
         st->idx_cut = idx_cut;
@@ -1564,18 +1591,13 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
         res[2] = 0xffffffffu;
     }
     // the finishing workgroup holding the e-th tie
-    uint32_t carry = 0;
-    for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
-        const uint32_t b = base + threadIdx.x;
-        const uint32_t z = (b < S.fin_nblocks) ? a.fin_eq[S.fin_first + b] : 0u;
-        uint32_t tot;
-        const uint32_t ex = carry + block_excl_scan(z, tmp, tot);
-        if (b < S.fin_nblocks && ex < e && e <= ex + z) {
-            res[0] = b;
-            res[1] = ex;
-        }
-        carry += tot;
-    }
+    block_scan_items<16>(S.fin_nblocks, tmp, [&](uint32_t b) { return a.fin_eq[S.fin_first + b]; },
+                         [&](uint32_t b, uint32_t ex, uint32_t z) {
+                             if (ex < e && e <= ex + z) {
+                                 res[0] = b;
+                                 res[1] = ex;
+                             }
+                         });
     __syncthreads();
     if (threadIdx.x == 0) {       // its segment holding the tie (at most kFinSegs)
         uint32_t s = res[0] * f.grain, before = res[1];
@@ -1608,19 +1630,13 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
     const uint32_t cut = res[2];
     // selected per segment, scanned into each segment's message offset
     // inside the layer (seg_sel, read by k_x_emit)
-    carry = 0;
-    for (uint32_t base = 0; base < f.nseg; base += kBlock) {
-        const uint32_t s = base + threadIdx.x;
-        uint32_t v = 0;
-        if (s < f.nseg) {
+    block_scan_items<16>(
+        f.nseg, tmp,
+        [&](uint32_t s) {
             const uint32_t eq = segeq[s];
-            v = a.seg_sel[f.seg_base + s] + (s < sstar ? eq : (s == sstar ? need : 0u));
-        }
-        uint32_t tot;
-        const uint32_t ex = carry + block_excl_scan(v, tmp, tot);
-        if (s < f.nseg) a.seg_sel[f.seg_base + s] = ex;
-        carry += tot;
-    }
+            return a.seg_sel[f.seg_base + s] + (s < sstar ? eq : (s == sstar ? need : 0u));
+        },
+        [&](uint32_t s, uint32_t ex, uint32_t) { a.seg_sel[f.seg_base + s] = ex; });
     if (threadIdx.x == 0) {
         st->idx_cut = cut;
         st->status = kStOk;
