@@ -96,6 +96,10 @@ LAYOUT_CASES = [
     ("unaligned", [7, 50001, 3, 70001, 9, 65536], (1, 1000), "normal", 5, 3),
     ("dense_big", [20000, 5001, 40000], (1, 1), "normal", 3, 2),
     ("big_ratio", [30000, 60001], (3, 10), "normal", 2, 2),
+    # full-sample layers (<= 16384 entries: one slot per entry) whose
+    # segments hold more than 1024 candidates
+    ("full_sample_many", [16384, 12000], (1, 2), "normal", 3, 2),
+    ("full_sample_equal", [16000, 9000], (1, 3), "equal", 2, 2),
     ("ties", [100000, 30000, 5000], (1, 100), "ties", 4, 2),
     ("bf16", [200000, 6000, 150000], (1, 1000), "bf16", 4, 2),
     ("zeros", [50000, 4097], (1, 100), "zeros", 2, 2),
