@@ -840,7 +840,7 @@ struct WaveSegs {
     uint32_t wave;
     uint32_t send;                    // end of the workgroup's segments
     uint32_t raw[kSegsPerWave];       // candidates of the segment (may exceed its slots)
-    uint32_t cnt[kSegsPerWave];       // of those, stored
+    uint32_t cap;                     // slots per segment
     uint2 first[kSegsPerWave];
     __device__ uint32_t seg(int i) const { return s0 + wave + (uint32_t)i * kWaves; }
     __device__ bool valid(int i) const { return seg(i) < send; }
@@ -848,18 +848,19 @@ struct WaveSegs {
     {
         return a.slots + (((uint64_t)f.slot_hi << 32) | f.slot_lo) + (uint64_t)seg(i) * f.cap;
     }
-    __device__ bool full(int i) const { return raw[i] > cnt[i]; }   // re-read from acc
+    __device__ uint32_t cnt(int i) const { return min(raw[i], cap); }   // stored candidates
+    __device__ bool full(int i) const { return raw[i] > cap; }          // re-read from acc
     __device__ void load(const SparsifyArgs &a, const FinWork &f, uint32_t wv, uint32_t ln)
     {
         s0 = f.seg0;
         wave = wv;
         send = min(f.seg0 + f.grain, f.nseg);
+        cap = f.cap;
 #pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[f.seg_base + seg(i)] : 0u;
 #pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) {
-            cnt[i] = min(raw[i], f.cap);
-            first[i] = (ln < cnt[i]) ? slots(a, f, i)[ln] : make_uint2(0, 0);
+            first[i] = (ln < min(raw[i], f.cap)) ? slots(a, f, i)[ln] : make_uint2(0, 0);
         }
     }
 };
@@ -867,7 +868,9 @@ struct WaveSegs {
 // k_fin_select: per segment, the count of candidates above the threshold bin;
 // the threshold bin's candidates are gathered into the layer's list (one
 // reservation per wave).  Per workgroup, the total above the bin.
-__global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
+// At most 64 VGPRs (8 waves per SIMD; 12 bytes spill): this latency-bound pass
+// measured 62 us at 74 VGPRs, 58 at 66 and 55 at 64 on the 1.31B-entry layout.
+__global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
 {
     __shared__ uint32_t wtot[kWaves];
     __shared__ uint32_t wzero[kWaves];
@@ -928,7 +931,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
                 }
             });
         } else {
-            const uint32_t cnt = ws.cnt[i];
+            const uint32_t cnt = ws.cnt(i);
             const uint2 *slots = ws.slots(a, f, i);
             for (uint32_t p = ln; p < cnt; p += 64) {
                 const uint2 c = (p < 64) ? ws.first[i] : slots[p];
@@ -965,7 +968,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_select(SparsifyArgs a)
                 });
                 continue;
             }
-            const uint32_t cnt = ws.cnt[i];
+            const uint32_t cnt = ws.cnt(i);
             const uint2 *slots = ws.slots(a, f, i);
             for (uint32_t p = ln; p < cnt; p += 64) {
                 const uint2 c = (p < 64) ? ws.first[i] : slots[p];
@@ -1265,7 +1268,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
         if (!ws.valid(i)) continue;
         const uint32_t base = sbase[ws.seg(i) - f.seg0];
         if (redo[ws.seg(i) - f.seg0]) continue;   // re-read below
-        const uint32_t cnt = ws.cnt[i];
+        const uint32_t cnt = ws.cnt(i);
         const uint2 *slots = ws.slots(a, f, i);
         uint32_t run = 0;
         for (uint32_t p0 = 0; p0 < cnt; p0 += 64) {
