@@ -1717,7 +1717,7 @@ __global__ __launch_bounds__(kBlock) void k_x_emit(SparsifyArgs a)
 // requested at once; the layers they span are staged in LDS, in five tables of
 // a.tl entries (dynamic LDS, sized by the host for the layout's widest span).
 template <int BPW>
-__global__ __launch_bounds__(kBlock) void k_agg_starts(AggArgs a)
+__global__ __launch_bounds__(kBlock, 8) void k_agg_starts(AggArgs a)
 {
     constexpr int PPT = BPW * kStartsBlock / kBlock;   // positions per thread
     extern __shared__ uint32_t tab[];
