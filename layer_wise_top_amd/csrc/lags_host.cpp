@@ -26,7 +26,7 @@ struct AggTables {
     void *dev = nullptr;
     uint32_t *cbase = nullptr;   // [L+1]
     uint32_t *csh = nullptr;     // [L]
-    uint32_t *chunk_layer = nullptr;  // [NC]
+    uint4 *chunk_info = nullptr;      // [NC]
 };
 
 struct TraceRec {
@@ -359,15 +359,24 @@ int ensure_agg(lags_layout *lo, int32_t P, AggTables **out)
     std::vector<uint32_t> cb, cs;
     uint32_t NC;
     plan_agg(lo, P, cb, cs, NC);
-    std::vector<uint32_t> cl(std::max<uint32_t>(NC, 1), 0);
-    for (int32_t l = 0; l < lo->L; ++l)
-        for (uint32_t c = cb[l]; c < cb[l + 1]; ++c) cl[c] = (uint32_t)l;
+    // per chunk: its index range inside its layer and the layer's message
+    // range, so that an aggregate workgroup needs one load to start
+    std::vector<uint4> ci(std::max<uint32_t>(NC, 1), uint4{0, 0, 0, 0});
+    for (int32_t l = 0; l < lo->L; ++l) {
+        const uint64_t off = lo->off[l], end = lo->off[l + 1];
+        for (uint32_t c = cb[l]; c < cb[l + 1]; ++c) {
+            const uint64_t clo = off + ((uint64_t)(c - cb[l]) << cs[l]);
+            const uint64_t chi = std::min<uint64_t>(clo + ((uint64_t)1 << cs[l]), end);
+            ci[c] = uint4{(uint32_t)clo, (uint32_t)chi, (uint32_t)lo->moff[l],
+                          (uint32_t)(lo->moff[l] + lo->k[l])};
+        }
+    }
     const size_t b0 = align_up(cb.size() * 4, kAlign), b1 = align_up(cs.size() * 4, kAlign),
-                 b2 = align_up(cl.size() * 4, kAlign);
+                 b2 = align_up(ci.size() * sizeof(uint4), kAlign);
     std::vector<unsigned char> host(b0 + b1 + b2, 0);
     std::memcpy(host.data(), cb.data(), cb.size() * 4);
     std::memcpy(host.data() + b0, cs.data(), cs.size() * 4);
-    std::memcpy(host.data() + b0 + b1, cl.data(), cl.size() * 4);
+    std::memcpy(host.data() + b0 + b1, ci.data(), ci.size() * sizeof(uint4));
     void *d = nullptr;
     if (hipMalloc(&d, host.size()) != hipSuccess) return LAGS_ENOMEM;
     if (hipMemcpy(d, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
@@ -380,7 +389,7 @@ int ensure_agg(lags_layout *lo, int32_t P, AggTables **out)
     t.dev = d;
     t.cbase = (uint32_t *)d;
     t.csh = (uint32_t *)((unsigned char *)d + b0);
-    t.chunk_layer = (uint32_t *)((unsigned char *)d + b0 + b1);
+    t.chunk_info = (uint4 *)((unsigned char *)d + b0 + b1);
     auto res = lo->agg.emplace(P, t);
     *out = &res.first->second;
     return LAGS_OK;
@@ -661,7 +670,7 @@ int lags_aggregate_range(const lags_layout *clo, int32_t l0, int32_t l1, float *
     a.pos_layer = lo->d_poslayer;
     a.cbase = t->cbase;
     a.csh = t->csh;
-    a.chunk_layer = t->chunk_layer;
+    a.chunk_info = t->chunk_info;
     a.start = (uint32_t *)(w + lo->ws_agg);
     a.report = (uint32_t *)(w + lo->ws_report);
     a.L = (uint32_t)lo->L;

@@ -186,7 +186,8 @@ struct AggArgs {
     const uint32_t *pos_layer;  // [ceil((K+1)/kStartsBlock)] layer of position b*kStartsBlock
     const uint32_t *cbase;      // [L+1] first chunk of each layer
     const uint32_t *csh;        // [L] log2 chunk width
-    const uint32_t *chunk_layer;// [NC]
+    const uint4 *chunk_info;    // [NC] per chunk: first index, end index, and the
+                                // message range [moff, moff + k) of its layer
     uint32_t *start;            // [P][NC+1]
     uint32_t *report;
     uint32_t L;

@@ -1803,13 +1803,9 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
         s0f = srow[c];
         s1f = srow[c + 1];
     }
-    const uint32_t l = a.chunk_layer[c];
-    const LayerInfo L = a.linfo[l];
-    const uint32_t sh = a.csh[l];
-    const uint64_t lo64 = (uint64_t)L.off + ((uint64_t)(c - a.cbase[l]) << sh);
-    const uint64_t hi64 = min(lo64 + (1ull << sh), (uint64_t)L.off + L.n);
-    const uint32_t lo = (uint32_t)lo64, hi = (uint32_t)hi64;
-    const uint32_t m0 = L.moff, m1 = L.moff + L.k;
+    const uint4 ci = a.chunk_info[c];
+    const uint32_t lo = ci.x, hi = ci.y;     // the chunk's indices
+    const uint32_t m0 = ci.z, m1 = ci.w;     // its layer's message range
 
     uint32_t carry = 0;
     for (uint32_t base = 0; base < P; base += kBlock) {
