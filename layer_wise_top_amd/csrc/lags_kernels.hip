@@ -1951,15 +1951,16 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
 // launchers
 
 // Unused dynamic LDS that sets how many one-segment workgroups a CU holds
-// (160 KiB of LDS per CU): a workgroup takes 36,000 B in launches of 64K
+// (160 KiB of LDS per CU): a workgroup takes 36,000 B in launches of 12K
 // workgroups and more (4 per CU), 23,000 B below (6-7 per CU).  Measured on
 // the streaming pass, total LDS per workgroup: 1.31B entries (320K
 // workgroups) 2.44-2.46 ms at 32,288-36,000 B, 2.56-2.58 at 32,000, 2.59 at
-// 27,000, 2.65 at 23,000, 2.77 at 54,000 (3 per CU); 15M-66M entries
-// (3.7K-16K workgroups) fastest at 23,000 B, up to 6% slower at 32,288.
+// 27,000, 2.65 at 23,000, 2.77 at 54,000 (3 per CU); 66M entries (16K
+// workgroups) 1.4% faster at 36,000 B than at 23,000; 15M-26M entries
+// (3.7K-6.2K workgroups) fastest at 23,000 B, up to 6% slower at 32,288.
 size_t stream_lds_pad(uint32_t ngroups, size_t static_lds)
 {
-    const size_t total = ngroups >= 65536u ? 36000 : 23000;
+    const size_t total = ngroups >= 12288u ? 36000 : 23000;
     return total > static_lds ? total - static_lds : 0;
 }
 
