@@ -414,11 +414,11 @@ int traced(lags_layout *lo, int32_t kid, hipStream_t s, F &&launch)
 
 // Exact mode: a multi-workgroup radix select of every sampled layer's
 // threshold (three digit passes, each followed by a per-layer pick), the
-// per-segment counts and tie cut, then the same emission as the sampled path;
-// small layers as always.  k_sample has cleared the layers' state and
-// histogram copies.
-int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t nmain,
-                   uint32_t nfin, hipStream_t s)
+// per-segment counts, tie cut and message offsets, then one emission
+// workgroup per segment; every pass over a layer runs on the main work list
+// (one workgroup per segment).  Small layers as always.  k_sample has cleared
+// the layers' state and histogram copies.
+int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t nmain, hipStream_t s)
 {
     int rc;
     if (nmain) {
@@ -602,7 +602,7 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     // k_sample always runs: its first workgroup restarts the report counters
     rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
     if (rc != LAGS_OK) return rc;
-    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, nfin, s);
+    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, s);
     if (nmain) {
         rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
         if (rc != LAGS_OK) return rc;
