@@ -414,11 +414,13 @@ int traced(lags_layout *lo, int32_t kid, hipStream_t s, F &&launch)
 
 // Exact mode: a multi-workgroup radix select of every sampled layer's
 // threshold (three digit passes, each followed by a per-layer pick), the
-// per-segment counts, tie cut and message offsets, then one emission
-// workgroup per segment; every pass over a layer runs on the main work list
-// (one workgroup per segment).  Small layers as always.  k_sample has cleared
-// the layers' state and histogram copies.
-int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t nmain, hipStream_t s)
+// per-segment counts, tie cut and message offsets, then the sampled path's
+// emission (from the entries >= T that k_x_count kept in the slots); every
+// pass over a layer runs on the main work list (one workgroup per segment).
+// Small layers as always.  k_sample has cleared the layers' state and
+// histogram copies.
+int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t nmain, uint32_t nfin,
+                   hipStream_t s)
 {
     int rc;
     if (nmain) {
@@ -446,7 +448,7 @@ int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t
         if (rc != LAGS_OK) return rc;
     }
     if (ns) {
-        rc = traced(lo, kKXEmit, s, [&] { return launch_x_emit(a, nmain, s); });
+        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
     }
     return LAGS_OK;
@@ -602,7 +604,7 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     // k_sample always runs: its first workgroup restarts the report counters
     rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
     if (rc != LAGS_OK) return rc;
-    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, s);
+    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, nfin, s);
     if (nmain) {
         rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
         if (rc != LAGS_OK) return rc;
@@ -761,7 +763,7 @@ const char *lags_kernel_name(int32_t id)
     static const char *names[kNumKernels] = {"k_sample",     "k_main",     "k_fin_bins",   "k_fin_select",
                                              "k_fin_resolve", "k_fin_emit", "k_agg_starts", "k_agg",
                                              "k_x_first",    "k_x_pass",   "k_x_pick",     "k_x_count",
-                                             "k_x_cut",      "k_x_emit"};
+                                             "k_x_cut"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "unknown";
 }
 

@@ -207,7 +207,7 @@ struct AggArgs {
 enum : int32_t {
     kKSample = 0, kKMain = 1, kKFinBins = 2, kKFinSelect = 3, kKFinResolve = 4,
     kKFinEmit = 5, kKAggStarts = 6, kKAgg = 7, kKXFirst = 8, kKXPass = 9, kKXPick = 10,
-    kKXCount = 11, kKXCut = 12, kKXEmit = 13, kNumKernels = 14
+    kKXCount = 11, kKXCut = 12, kNumKernels = 13
 };
 
 // launchers (lags_kernels.hip)
@@ -222,7 +222,6 @@ hipError_t launch_x_pass(const SparsifyArgs &a, uint32_t nblocks, uint32_t level
 hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s);
 hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_x_cut(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
-hipError_t launch_x_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
 hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s);
 

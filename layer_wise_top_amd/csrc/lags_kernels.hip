@@ -37,14 +37,14 @@
 //                 with fewer than k nonzero keys (G = 0, "zero mode") sends
 //                 every nonzero entry and its lowest-index zeros; segments
 //                 that send zeros are re-read from the residual buffer.
-//   k_x_first, k_x_pass, k_x_pick, k_x_count, k_x_cut, k_x_emit
+//   k_x_first, k_x_pass, k_x_pick, k_x_count, k_x_cut
 //                 exact mode (chosen by the caller): the threshold of every
 //                 sampled layer by a multi-workgroup radix select over all its
 //                 keys (three digit passes, each followed by a per-layer
 //                 pick), then per-segment counts, the tie cut and message
-//                 offsets; k_x_emit re-reads every segment to emit.  The
-//                 passes over a layer take k_main's one-workgroup-per-segment
-//                 shape.
+//                 offsets; k_x_count keeps each segment's keys >= T in its
+//                 slots and k_fin_emit emits from them.  The passes over a
+//                 layer take k_main's one-workgroup-per-segment shape.
 //   k_agg_starts  for every worker, where each index chunk starts in its
 //                 message (messages ascend per layer).
 //   k_agg         one workgroup per index chunk: worker-ordered sums in an LDS
@@ -1535,10 +1535,14 @@ __global__ __launch_bounds__(kBinsThreads) void k_x_pick(SparsifyArgs a, uint32_
 // k_x_count: per segment, keys above T (into seg_sel) and equal to T (into
 // the layer's threshold-bin area, one word per segment); the keys equal to T
 // are also added to the tie count of the segment's finishing workgroup
-// (cleared by the last k_x_pick), which k_x_cut scans.
+// (cleared by the last k_x_pick), which k_x_cut scans.  The segment's entries
+// with key >= T (the only ones that can be sent) are kept, in index order, in
+// its candidate slots when they fit, and their number in seg_count, which is
+// what k_fin_emit reads (more than the slots: the segment is re-read).
 __global__ __launch_bounds__(kBlock) void k_x_count(SparsifyArgs a)
 {
-    __shared__ uint32_t wgt[kWaves], weq[kWaves];
+    __shared__ uint32_t wtot[kParts][kWaves];
+    __shared__ uint32_t wgt[kWaves];
     MainWork w;
     uint32_t seg;
     if (!x_segment(a, w, seg)) return;
@@ -1546,28 +1550,50 @@ __global__ __launch_bounds__(kBlock) void k_x_count(SparsifyArgs a)
     xs.load(a, w, seg);
     const uint32_t T = a.state[w.sid].T;
     const uint32_t fin_first = a.sinfo[w.sid].fin_first;
-    uint32_t gt = 0, eq = 0;
-    xs.each([&](uint32_t, float v) {
-        const uint32_t key = key_of(v);
-        gt += key > T ? 1u : 0u;
-        eq += key == T ? 1u : 0u;
-    });
+    const uint32_t t = threadIdx.x;
+    const SegView &sv = xs.sv;
+    uint32_t fl = 0, gt = 0;   // fl bit 4u + j: entry j of row u has key >= T
+#pragma unroll
+    for (int u = 0; u < kRows; ++u)
+        if (sv.row_in(u)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t key = key_of(xs.x[u][j]);
+                if (key >= T) fl |= 1u << (4 * u + j);
+                gt += key > T ? 1u : 0u;
+            }
+        }
+    uint32_t c[kParts], pos[kParts];
+    c[0] = (t < sv.nh && key_of(xs.hv) >= T) ? 1u : 0u;
+    gt += (t < sv.nh && key_of(xs.hv) > T) ? 1u : 0u;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fl >> (4 * u)) & 15u);
+    c[kParts - 1] = (t < sv.ntl && key_of(xs.tv) >= T) ? 1u : 0u;
+    gt += (t < sv.ntl && key_of(xs.tv) > T) ? 1u : 0u;
+    const uint32_t total = block_positions(c, pos, wtot);   // keys >= T in the segment
     gt = wave_sum(gt);
-    eq = wave_sum(eq);
-    const uint32_t wv = threadIdx.x >> 6;
-    if (lane_id() == 0) {
-        wgt[wv] = gt;
-        weq[wv] = eq;
+    if (lane_id() == 0) wgt[t >> 6] = gt;
+    if (total <= w.cap) {
+        uint2 *slots = a.slots + (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * w.cap;
+        if (c[0]) slots[pos[0]] = make_uint2(sv.hlo + t, __float_as_uint(xs.hv));
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            uint32_t p = pos[1 + u];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((fl >> (4 * u + j)) & 1u)
+                    slots[p++] = make_uint2(4u * sv.row(u) + j, __float_as_uint(xs.x[u][j]));
+        }
+        if (c[kParts - 1]) slots[pos[kParts - 1]] = make_uint2(sv.tlo + t, __float_as_uint(xs.tv));
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t g = 0, e = 0;
-        for (int i = 0; i < kWaves; ++i) {
-            g += wgt[i];
-            e += weq[i];
-        }
+    if (t == 0) {
+        uint32_t g = 0;
+        for (int i = 0; i < kWaves; ++i) g += wgt[i];
+        const uint32_t e = total - g;
         uint32_t *segeq = reinterpret_cast<uint32_t *>(a.tbin + (((uint64_t)w.slot_hi << 32) | w.slot_lo));
         a.seg_sel[w.seg_base + seg] = g;
+        a.seg_count[w.seg_base + seg] = total;
         segeq[seg] = e;
         if (e) atomicAdd(&a.fin_eq[fin_first + seg / fin_grain(w.nseg)], e);
     }
@@ -1576,7 +1602,9 @@ __global__ __launch_bounds__(kBlock) void k_x_count(SparsifyArgs a)
 // k_x_cut: one workgroup per sampled layer.  Finds the segment s* holding
 // the e-th key equal to T (index order) and, re-reading it, that key's index
 // (the cut); then per segment the selected count (keys above T, plus its
-// keys equal to T up to the cut), scanned into the segment's message offset.
+// keys equal to T up to the cut) and per finishing workgroup the message
+// offset.  k_fin_emit then emits each segment from the entries k_x_count kept
+// in its slots, or re-reads a segment whose entries did not fit.
 __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
 {
     __shared__ uint32_t tmp[kWaves];
@@ -1631,75 +1659,24 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
     }
     __syncthreads();
     const uint32_t cut = res[2];
-    // selected per segment, scanned into each segment's message offset
-    // inside the layer (seg_sel, read by k_x_emit)
+    // selected per segment (seg_sel) and each finishing workgroup's message
+    // offset (fin_total), which k_fin_emit reads as in the sampled path
     block_scan_items<16>(
         f.nseg, tmp,
         [&](uint32_t s) {
             const uint32_t eq = segeq[s];
             return a.seg_sel[f.seg_base + s] + (s < sstar ? eq : (s == sstar ? need : 0u));
         },
-        [&](uint32_t s, uint32_t ex, uint32_t) { a.seg_sel[f.seg_base + s] = ex; });
+        [&](uint32_t s, uint32_t ex, uint32_t v) {
+            a.seg_sel[f.seg_base + s] = v;
+            if (s % f.grain == 0u) a.fin_total[S.fin_first + s / f.grain] = ex;
+        });
     if (threadIdx.x == 0) {
         st->idx_cut = cut;
         st->status = kStOk;
         atomicAdd(&a.report[kRepSampled], 1u);
         atomicAdd(&a.report[kRepExact], 1u);
     }
-}
-
-// k_x_emit: one workgroup per segment re-reads acc and writes the segment's
-// selection (key > T, or key == T and index <= cut) in index order from the
-// layer's message offset plus the segment's (from k_x_cut); sent entries'
-// residual becomes +0.0.
-__global__ __launch_bounds__(kBlock) void k_x_emit(SparsifyArgs a)
-{
-    __shared__ uint32_t wtot[kParts][kWaves];
-    MainWork w;
-    uint32_t seg;
-    if (!x_segment(a, w, seg)) return;
-    XSeg xs;
-    xs.load(a, w, seg);
-    const SampledState *st = a.state + w.sid;
-    const LayerInfo L = a.linfo[w.layer];
-    const uint32_t base = L.moff + a.seg_sel[w.seg_base + seg];
-    if (st->status != kStOk) return;   // uniform; k_x_cut resolves every layer
-    const uint32_t T = st->T, cut = st->idx_cut;
-    const uint32_t t = threadIdx.x;
-    auto sel = [&](uint32_t idx, float v) {
-        const uint32_t key = key_of(v);
-        return key > T || (key == T && idx <= cut);
-    };
-    uint32_t fl = 0, c[kParts], pos[kParts];
-#pragma unroll
-    for (int u = 0; u < kRows; ++u)
-        if (xs.sv.row_in(u)) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (sel(4u * xs.sv.row(u) + j, xs.x[u][j])) fl |= 1u << (4 * u + j);
-        }
-    c[0] = (t < xs.sv.nh && sel(xs.sv.hlo + t, xs.hv)) ? 1u : 0u;
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fl >> (4 * u)) & 15u);
-    c[kParts - 1] = (t < xs.sv.ntl && sel(xs.sv.tlo + t, xs.tv)) ? 1u : 0u;
-    block_positions(c, pos, wtot);
-    const uint32_t mend = L.moff + L.k;
-    auto put = [&](uint32_t p, uint32_t idx, float v) {
-        if (p < mend) {            // the layer's selection holds exactly k entries
-            a.msg_idx[p] = idx;
-            a.msg_val[p] = v;
-        }
-        a.res[idx] = 0.0f;
-    };
-    if (c[0]) put(base + pos[0], xs.sv.hlo + t, xs.hv);
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-        uint32_t p = base + pos[1 + u];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * xs.sv.row(u) + j, xs.x[u][j]);
-    }
-    if (c[kParts - 1]) put(base + pos[kParts - 1], xs.sv.tlo + t, xs.tv);
 }
 
 // ---------------------------------------------------------------------------
@@ -2025,14 +2002,7 @@ hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level
 hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     const uint32_t ngroups = nblocks * kTileSegs;
-    hipLaunchKernelGGL(k_x_count, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, 2 * kWaves * 4), s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_x_emit(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
-{
-    const uint32_t ngroups = nblocks * kTileSegs;
-    hipLaunchKernelGGL(k_x_emit, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, kParts * kWaves * 4),
+    hipLaunchKernelGGL(k_x_count, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, (kParts + 1) * kWaves * 4),
                        s, a);
     return hipGetLastError();
 }
