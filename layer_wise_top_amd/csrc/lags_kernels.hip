@@ -1935,6 +1935,13 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
 // 27,000, 2.65 at 23,000, 2.77 at 54,000 (3 per CU); 66M entries (16K
 // workgroups) 1.4% faster at 36,000 B than at 23,000; 15M-26M entries
 // (3.7K-6.2K workgroups) fastest at 23,000 B, up to 6% slower at 32,288.
+// The exact-mode passes that only read the layer (k_x_pass, k_x_count) run
+// 6-7 workgroups per CU at every size: their per-workgroup work (histogram,
+// ordering of the keys >= T) needs more workgroups in flight than the
+// streaming pass.  Same-box A/B of the exact call at 1.31B entries: 5.54 ms
+// with the streaming pass's rule, 5.26 at 23,000 B, 5.30 with no pad.
+constexpr size_t kReadPassLds = 23000;
+
 size_t stream_lds_pad(uint32_t ngroups, size_t static_lds)
 {
     const size_t total = ngroups >= 12288u ? 36000 : 23000;
@@ -1989,7 +1996,7 @@ hipError_t launch_x_first(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s
 hipError_t launch_x_pass(const SparsifyArgs &a, uint32_t nblocks, uint32_t level, hipStream_t s)
 {
     const uint32_t ngroups = nblocks * kTileSegs;
-    hipLaunchKernelGGL(k_x_pass, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, 2048 * 4), s, a, level);
+    hipLaunchKernelGGL(k_x_pass, dim3(ngroups), dim3(kBlock), kReadPassLds - 2048 * 4, s, a, level);
     return hipGetLastError();
 }
 
@@ -2002,8 +2009,7 @@ hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level
 hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     const uint32_t ngroups = nblocks * kTileSegs;
-    hipLaunchKernelGGL(k_x_count, dim3(ngroups), dim3(kBlock), stream_lds_pad(ngroups, (kParts + 1) * kWaves * 4),
-                       s, a);
+    hipLaunchKernelGGL(k_x_count, dim3(ngroups), dim3(kBlock), kReadPassLds - (kParts + 1) * kWaves * 4, s, a);
     return hipGetLastError();
 }
 
