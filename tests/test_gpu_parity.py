@@ -100,6 +100,8 @@ LAYOUT_CASES = [
     # segments hold more than 1024 candidates
     ("full_sample_many", [16384, 12000], (1, 2), "normal", 3, 2),
     ("full_sample_equal", [16000, 9000], (1, 3), "equal", 2, 2),
+    # one worker: the aggregate applies the own message alone (s = lr)
+    ("single_worker", [50000, 7000, 300], (1, 100), "normal", 1, 2),
     ("ties", [100000, 30000, 5000], (1, 100), "ties", 4, 2),
     ("bf16", [200000, 6000, 150000], (1, 1000), "bf16", 4, 2),
     ("zeros", [50000, 4097], (1, 100), "zeros", 2, 2),
