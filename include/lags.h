@@ -24,21 +24,22 @@
  * definitions (round to nearest even, no flush to zero, no FMA contraction).
  *
  * Conventions for every entry point:
- *   - pointers named grad/residual/weights/msg_* are DEVICE pointers on the
- *     device that was current when the layout was first used; tables passed
- *     to lags_layout_create are HOST pointers and are copied;
- *   - device buffers are owned by the caller; the library keeps no pointer
- *     to them after a call returns;
+ *   - pointers named grad, residual, weights, msg_idx, msg_val and ws are
+ *     DEVICE pointers on the device that was current when the workspace was
+ *     initialised; tables passed to lags_layout_create are HOST pointers and
+ *     are copied;
+ *   - device buffers are owned by the caller; the library never allocates
+ *     device memory and keeps no pointer to the caller's buffers after a call
+ *     returns, except the workspace addresses lags_workspace_init records;
+ *   - the layout's device tables live at the head of the caller's workspace:
+ *     lags_workspace_init copies them there once (asynchronously, on its
+ *     stream); the sparsify and aggregate calls only read them;
  *   - calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *     stream): no host synchronisation, no device-to-host copy, except where
- *     a function says it synchronises;
+ *     stream): no host synchronisation, no copy, no allocation, except where
+ *     a function says so, so they can be captured into a HIP graph;
  *   - arguments are validated on the host before anything is launched; on a
  *     negative status nothing has been launched and nothing written;
  *   - device faults surface at the caller's next synchronisation (HIP rules);
- *   - the first call on a device builds the layout's device tables (and the
- *     first aggregate with a given P its chunk tables) with hipMalloc and a
- *     synchronous copy; after that a call allocates nothing, copies nothing
- *     and does not synchronise, so it can be captured into a HIP graph;
  *   - one workspace must not be used by two calls that may overlap in time,
  *     except range calls on disjoint layer ranges (see lags_sparsify_range).
  */
@@ -55,11 +56,12 @@ extern "C" {
 /* Status codes (negative = error). */
 #define LAGS_OK 0
 #define LAGS_EINVAL (-1)     /* invalid argument: null/misaligned pointer, bad table, overlap */
-#define LAGS_ERANGE (-2)     /* size outside the supported range (n or K >= 2^32, P, L) */
+#define LAGS_ERANGE (-2)     /* size outside the supported range (n or K above 2^32 - 2, P, L) */
 #define LAGS_EWORKSPACE (-3) /* workspace null, misaligned or smaller than required */
 #define LAGS_EHIP (-4)       /* a HIP runtime call failed (no device, launch error, ...) */
-#define LAGS_EDEVICE (-5)    /* current device differs from the layout's device */
-#define LAGS_ENOMEM (-6)     /* host or device allocation failed */
+#define LAGS_EDEVICE (-5)    /* current device differs from the workspace's device */
+#define LAGS_ENOMEM (-6)     /* host allocation failed */
+#define LAGS_ENOTINIT (-7)   /* workspace not initialised for this layout (lags_workspace_init) */
 
 /* Limits. */
 #define LAGS_MAX_LAYERS 65536
@@ -93,22 +95,25 @@ int64_t lags_k_for_ratio(int64_t n, int64_t num, int64_t den);
  * the per-layer count k[l] of entries each worker sends (abstract: the set's
  * size is chosen per layer).
  *   layer_off: host int64[L+1], layer_off[0] == 0, strictly increasing,
- *              layer_off[L] < 2^32;
+ *              layer_off[L] <= 2^32 - 2 (indices are uint32; 0xffffffff is
+ *              kept free as a marker);
  *   k:         host int64[L], 1 <= k[l] <= layer_off[l+1] - layer_off[l],
- *              sum(k) < 2^32;
+ *              sum(k) <= 2^32 - 2;
  *   out:       receives the new layout (destroy with lags_layout_destroy).
- * Pure host work: no HIP call is made here.  Device copies of the tables are
- * made on first use, on the device current at that time.  The layout is
- * immutable after creation and may be shared by concurrent calls (its lazily
- * built device tables are guarded by a lock).
+ * Pure host work: no HIP call is made here; the device tables are built on
+ * the host and copied into a workspace by lags_workspace_init.  The layout
+ * is immutable after creation and may be shared by concurrent calls (its
+ * per-worker-count chunk plans and its record of initialised workspaces are
+ * guarded by a lock).
  * Returns LAGS_OK, LAGS_EINVAL (bad table / null pointer), LAGS_ERANGE
- * (L < 1 or L > LAGS_MAX_LAYERS, n or sum(k) >= 2^32), LAGS_ENOMEM.
+ * (L < 1 or L > LAGS_MAX_LAYERS, n or sum(k) above 2^32 - 2), LAGS_ENOMEM.
  */
 int lags_layout_create(int32_t L, const int64_t *layer_off, const int64_t *k,
                        lags_layout **out);
 
-/* Free the layout and its device tables.  NULL is accepted.  The caller must
- * make sure no call using it is still running on the device. */
+/* Free the layout (host memory only).  NULL is accepted.  The caller must
+ * make sure no call using it, and no copy issued by lags_workspace_init, is
+ * still running on the device. */
 void lags_layout_destroy(lags_layout *layout);
 
 /* n (entries), K = sum(k) (message length per worker), L. -1 on NULL. */
@@ -121,12 +126,38 @@ int64_t lags_layout_msg_offset(const lags_layout *layout, int32_t l);
 
 /*
  * Bytes of device workspace that lags_sparsify_layers and
- * lags_aggregate_apply (with up to P workers) need.  The workspace is scratch
- * space only: its contents on entry are never read before being written, so
- * results do not depend on them.  Returns 0 for a NULL layout or P outside
+ * lags_aggregate_apply (with up to P workers) need: the layout's tables, the
+ * aggregate's chunk tables for P workers, and scratch space.  The scratch
+ * part's contents on entry are never read before being written, so results
+ * do not depend on them.  Returns 0 for a NULL layout or P outside
  * [1, LAGS_MAX_WORKERS].
  */
 size_t lags_workspace_bytes(const lags_layout *layout, int32_t P);
+
+/*
+ * Prepare a workspace for a layout and up to P workers: copies the layer
+ * tables and the chunk tables for P workers (host images the layout built)
+ * into the head and tail of ws with hipMemcpyAsync on `stream`, and records
+ * (ws, P, current device) in the layout.  The sparsify and aggregate calls
+ * of this layout accept only a workspace so recorded (else LAGS_ENOTINIT),
+ * read the tables from it, and allocate and copy nothing themselves.
+ * Initialising the same ws again replaces its record.  The tables must stay
+ * intact: anything else that writes the workspace (another layout's calls,
+ * a free and reallocation at the same address) requires a new
+ * lags_workspace_init before the next call.  The copies read the layout's
+ * host images, so the layout must outlive them (as it must outlive every
+ * call that uses it).
+ *   ws:       device memory of ws_bytes >= lags_workspace_bytes(layout, P),
+ *             16-byte aligned, on the current device;
+ *   P:        1..LAGS_MAX_WORKERS: the largest worker count the aggregate
+ *             calls will pass with this workspace;
+ *   stream:   hipStream_t of the copies; calls on other streams must be
+ *             ordered after them by the caller.
+ * Returns LAGS_OK, LAGS_EINVAL (null layout), LAGS_ERANGE (P),
+ * LAGS_EWORKSPACE (null, misaligned or small ws), LAGS_EHIP, LAGS_ENOMEM.
+ */
+int lags_workspace_init(const lags_layout *layout, void *ws, size_t ws_bytes, int32_t P,
+                        void *stream);
 
 /*
  * Sparsify worker 0's gradient (abstract; proposed method, bullets 1 and 4).
@@ -136,14 +167,16 @@ size_t lags_workspace_bytes(const lags_layout *layout, int32_t P);
  *             order, ascending inside each layer (layer l at
  *             lags_layout_msg_offset(l));
  *   msg_val:  device fp32[K], out: the matching acc values, bit for bit;
- *   ws:       device workspace of ws_bytes >= lags_workspace_bytes(layout, 1);
+ *   ws:       device workspace initialised for this layout by
+ *             lags_workspace_init (any P), ws_bytes its size;
  *   flags:    0 or LAGS_SPARSIFY_EXACT;
  *   stream:   hipStream_t.
  * The message buffers are exactly row 0 of the [P][K] layout that
  * lags_aggregate_apply reads.  grad, residual, msg_idx, msg_val and ws must
  * be 16-byte aligned and must not overlap.
- * Returns LAGS_OK, LAGS_EINVAL, LAGS_EWORKSPACE, LAGS_EDEVICE, LAGS_EHIP,
- * LAGS_ENOMEM (first use: device tables).
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_EWORKSPACE, LAGS_ENOTINIT, LAGS_EDEVICE
+ * (current device is not the one the workspace was initialised on),
+ * LAGS_EHIP.
  */
 int lags_sparsify_layers(const lags_layout *layout, const float *grad,
                          float *residual, uint32_t *msg_idx, float *msg_val,
@@ -158,7 +191,8 @@ int lags_sparsify_layers(const lags_layout *layout, const float *grad,
  *            distinct indices of that layer, ascending);
  *   msg_val: device fp32[P][K];
  *   P:       1..LAGS_MAX_WORKERS;  lr: learning rate (s = lr / P in fp32);
- *   ws:      device workspace of ws_bytes >= lags_workspace_bytes(layout, P).
+ *   ws:      device workspace initialised for this layout by
+ *            lags_workspace_init with at least P workers, ws_bytes its size.
  * Messages that break the layout (an index outside its layer, indices not
  * strictly ascending) never cause an out-of-bounds access and never change
  * the weights of another layer: an entry found outside the index chunk it
@@ -166,8 +200,9 @@ int lags_sparsify_layers(const lags_layout *layout, const float *grad,
  * land outside their chunk) is skipped and counted in
  * lags_report.bad_entries; the weights of a layer with malformed entries are
  * otherwise unspecified (e.g. for a repeated index).
- * Returns LAGS_OK, LAGS_EINVAL, LAGS_ERANGE (P), LAGS_EWORKSPACE,
- * LAGS_EDEVICE, LAGS_EHIP, LAGS_ENOMEM (first use with this P: device tables).
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_ERANGE (P), LAGS_EWORKSPACE (also: P
+ * above the workspace's initialised worker count), LAGS_ENOTINIT,
+ * LAGS_EDEVICE, LAGS_EHIP.
  */
 int lags_aggregate_apply(const lags_layout *layout, float *weights,
                          const uint32_t *msg_idx, const float *msg_val,
@@ -282,6 +317,9 @@ typedef struct lags_report {
     uint32_t slow_chunks;   /* aggregate chunks above the fast-path capacity */
     int32_t layers_wide_bin; /* sampled layers whose threshold bin was resolved from the
                                 workspace rather than LDS (last sparsify) */
+    uint32_t fix_timeouts;  /* barrier waits of the guess-failure fallback that gave up
+                               (bounded waits; 0 unless its workgroups could not all
+                               run at once, and then the layer's output is wrong) */
 } lags_report;
 
 /* Synchronise `stream` and read the report kept in the workspace.  Only

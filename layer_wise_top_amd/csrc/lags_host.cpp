@@ -20,13 +20,22 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-struct AggTables {
+// The aggregate's chunk plan for up to P workers: chunk widths per layer and
+// the host image of its device tables (copied into a workspace by
+// lags_workspace_init).
+struct AggPlan {
     uint32_t NC = 0;
-    std::vector<uint32_t> h_cbase;    // [L+1], host copy
-    void *dev = nullptr;
-    uint32_t *cbase = nullptr;   // [L+1]
-    uint32_t *csh = nullptr;     // [L]
-    uint4 *chunk_info = nullptr;      // [NC]
+    std::vector<uint32_t> h_cbase;    // [L+1]
+    size_t b_cbase = 0, b_csh = 0, b_info = 0;   // byte offsets inside the image
+    std::vector<unsigned char> image; // cbase[L+1], csh[L], chunk_info[NC]
+};
+
+// A workspace that lags_workspace_init prepared for this layout.
+struct WsRec {
+    const void *ws;
+    size_t bytes;
+    int32_t P;
+    int device;
 };
 
 struct TraceRec {
@@ -55,21 +64,17 @@ struct lags_layout {
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
     uint64_t hist_words = 0;
-    // workspace plan (byte offsets)
+    // host image of the layer tables (the head of every workspace) and the
+    // byte offsets of its parts
+    std::vector<unsigned char> tables;
+    size_t tb_linfo = 0, tb_sinfo = 0, tb_main = 0, tb_fin = 0, tb_moff = 0, tb_pos = 0,
+           tb_small = 0;
+    // workspace plan (byte offsets; the P-dependent part starts at ws_agg)
     size_t ws_report = 0, ws_state = 0, ws_hist = 0, ws_segcount = 0, ws_segsel = 0,
-           ws_slots = 0, ws_tbin = 0, ws_fintot = 0, ws_fineq = 0, ws_agg = 0;
-    // device tables, built on first use
+           ws_slots = 0, ws_tbin = 0, ws_fintot = 0, ws_fineq = 0, ws_fb = 0, ws_agg = 0;
     std::mutex mu;
-    int device = -1;
-    void *dev = nullptr;
-    LayerInfo *d_linfo = nullptr;
-    SampledInfo *d_sinfo = nullptr;
-    MainWork *d_main = nullptr;
-    FinWork *d_fin = nullptr;
-    uint32_t *d_moff = nullptr;
-    uint32_t *d_poslayer = nullptr;
-    uint32_t *d_small = nullptr;
-    std::map<int32_t, AggTables> agg;
+    std::map<int32_t, AggPlan> agg;     // chunk plans by worker count
+    std::vector<WsRec> wss;             // initialised workspaces
     // tracing
     bool trace = false;
     std::vector<TraceRec> recs;
@@ -264,8 +269,36 @@ int build_plan(lags_layout *lo)
         lo->starts_tl4 = std::max(lo->starts_tl4, l4 - la + 2);
     }
 
-    const size_t ns = lo->sinfo.size();
+    // the layer tables: a host image, copied to the head of a workspace by
+    // lags_workspace_init
     size_t at = 0;
+    auto part = [&](size_t bytes) {
+        const size_t o = at;
+        at = align_up(at + std::max<size_t>(bytes, 4), kAlign);
+        return o;
+    };
+    lo->tb_linfo = part(lo->linfo.size() * sizeof(LayerInfo));
+    lo->tb_sinfo = part(lo->sinfo.size() * sizeof(SampledInfo));
+    lo->tb_main = part(lo->main_work.size() * sizeof(MainWork));
+    lo->tb_fin = part(lo->fin_work.size() * sizeof(FinWork));
+    lo->tb_moff = part(lo->moff.size() * 4);
+    lo->tb_pos = part(lo->pos_layer.size() * 4);
+    lo->tb_small = part(lo->small_layers.size() * 4);
+    lo->tables.assign(at, 0);
+    unsigned char *h = lo->tables.data();
+    auto put = [&](size_t o, const void *src, size_t bytes) {
+        if (bytes) std::memcpy(h + o, src, bytes);
+    };
+    put(lo->tb_linfo, lo->linfo.data(), lo->linfo.size() * sizeof(LayerInfo));
+    put(lo->tb_sinfo, lo->sinfo.data(), lo->sinfo.size() * sizeof(SampledInfo));
+    put(lo->tb_main, lo->main_work.data(), lo->main_work.size() * sizeof(MainWork));
+    put(lo->tb_fin, lo->fin_work.data(), lo->fin_work.size() * sizeof(FinWork));
+    put(lo->tb_moff, lo->moff.data(), lo->moff.size() * 4);
+    put(lo->tb_pos, lo->pos_layer.data(), lo->pos_layer.size() * 4);
+    put(lo->tb_small, lo->small_layers.data(), lo->small_layers.size() * 4);
+
+    // scratch: never read before being written in a call
+    const size_t ns = lo->sinfo.size();
     lo->ws_report = at;
     at = align_up(at + kRepWords * 4, kAlign);
     lo->ws_state = at;
@@ -284,16 +317,49 @@ int build_plan(lags_layout *lo)
     at = align_up(at + lo->fin_work.size() * 4, kAlign);
     lo->ws_fineq = at;
     at = align_up(at + lo->fin_work.size() * 4, kAlign);
+    lo->ws_fb = at;
+    at = align_up(at + ns * (size_t)kFbWords * 4, kAlign);
     lo->ws_agg = at;
     return LAGS_OK;
 }
 
-size_t agg_bytes(const lags_layout *lo, int32_t P)
+// The chunk plan for up to P workers (caller holds lo->mu, or the layout is
+// not shared yet).  The image holds cbase, csh and, per chunk, its index range
+// and its layer's message range, so that an aggregate workgroup needs one load
+// to start.
+const AggPlan &agg_plan(lags_layout *lo, int32_t P)
 {
+    auto it = lo->agg.find(P);
+    if (it != lo->agg.end()) return it->second;
+    AggPlan t;
     std::vector<uint32_t> cb, cs;
-    uint32_t NC;
-    plan_agg(lo, P, cb, cs, NC);
-    return align_up((size_t)P * ((size_t)NC + 1) * 4, kAlign);
+    plan_agg(lo, P, cb, cs, t.NC);
+    std::vector<uint4> ci(std::max<uint32_t>(t.NC, 1), uint4{0, 0, 0, 0});
+    for (int32_t l = 0; l < lo->L; ++l) {
+        const uint64_t off = lo->off[l], end = lo->off[l + 1];
+        for (uint32_t c = cb[l]; c < cb[l + 1]; ++c) {
+            const uint64_t clo = off + ((uint64_t)(c - cb[l]) << cs[l]);
+            const uint64_t chi = std::min<uint64_t>(clo + ((uint64_t)1 << cs[l]), end);
+            ci[c] = uint4{(uint32_t)clo, (uint32_t)chi, (uint32_t)lo->moff[l],
+                          (uint32_t)(lo->moff[l] + lo->k[l])};
+        }
+    }
+    t.b_cbase = 0;
+    t.b_csh = align_up(cb.size() * 4, kAlign);
+    t.b_info = t.b_csh + align_up(cs.size() * 4, kAlign);
+    t.image.assign(t.b_info + align_up(ci.size() * sizeof(uint4), kAlign), 0);
+    std::memcpy(t.image.data() + t.b_cbase, cb.data(), cb.size() * 4);
+    std::memcpy(t.image.data() + t.b_csh, cs.data(), cs.size() * 4);
+    std::memcpy(t.image.data() + t.b_info, ci.data(), ci.size() * sizeof(uint4));
+    t.h_cbase = std::move(cb);
+    return lo->agg.emplace(P, std::move(t)).first->second;
+}
+
+// Bytes of the P-dependent tail of a workspace: the chunk-start table
+// [P][NC+1], then the chunk tables.
+size_t agg_tail_bytes(const AggPlan &t, int32_t P)
+{
+    return align_up((size_t)P * ((size_t)t.NC + 1) * 4, kAlign) + t.image.size();
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -304,95 +370,12 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Device tables for the layout on the current device (caller holds lo->mu).
-int ensure_device(lags_layout *lo)
+// The record of an initialised workspace, or null (caller holds lo->mu).
+const WsRec *find_ws(const lags_layout *lo, const void *ws)
 {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return LAGS_EHIP;
-    if (lo->dev) return dev == lo->device ? LAGS_OK : LAGS_EDEVICE;
-    const size_t b_l = align_up(lo->linfo.size() * sizeof(LayerInfo), kAlign);
-    const size_t b_s = align_up(std::max<size_t>(1, lo->sinfo.size()) * sizeof(SampledInfo), kAlign);
-    const size_t b_m = align_up(std::max<size_t>(1, lo->main_work.size()) * sizeof(MainWork), kAlign);
-    const size_t b_f = align_up(std::max<size_t>(1, lo->fin_work.size()) * sizeof(FinWork), kAlign);
-    const size_t b_o = align_up(lo->moff.size() * 4, kAlign);
-    const size_t b_p = align_up(lo->pos_layer.size() * 4, kAlign);
-    const size_t b_sm = align_up(std::max<size_t>(1, lo->small_layers.size()) * 4, kAlign);
-    const size_t total = b_l + b_s + b_m + b_f + b_o + b_p + b_sm;
-    std::vector<unsigned char> host(total, 0);
-    std::memcpy(host.data(), lo->linfo.data(), lo->linfo.size() * sizeof(LayerInfo));
-    if (!lo->sinfo.empty())
-        std::memcpy(host.data() + b_l, lo->sinfo.data(), lo->sinfo.size() * sizeof(SampledInfo));
-    std::memcpy(host.data() + b_l + b_s, lo->main_work.data(), lo->main_work.size() * sizeof(MainWork));
-    if (!lo->fin_work.empty())
-        std::memcpy(host.data() + b_l + b_s + b_m, lo->fin_work.data(), lo->fin_work.size() * sizeof(FinWork));
-    std::memcpy(host.data() + b_l + b_s + b_m + b_f, lo->moff.data(), lo->moff.size() * 4);
-    std::memcpy(host.data() + b_l + b_s + b_m + b_f + b_o, lo->pos_layer.data(), lo->pos_layer.size() * 4);
-    if (!lo->small_layers.empty())
-        std::memcpy(host.data() + b_l + b_s + b_m + b_f + b_o + b_p, lo->small_layers.data(),
-                    lo->small_layers.size() * 4);
-    void *d = nullptr;
-    if (hipMalloc(&d, total) != hipSuccess) return LAGS_ENOMEM;
-    if (hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipFree(d);
-        return LAGS_EHIP;
-    }
-    unsigned char *p = (unsigned char *)d;
-    lo->dev = d;
-    lo->device = dev;
-    lo->d_linfo = (LayerInfo *)p;
-    lo->d_sinfo = (SampledInfo *)(p + b_l);
-    lo->d_main = (MainWork *)(p + b_l + b_s);
-    lo->d_fin = (FinWork *)(p + b_l + b_s + b_m);
-    lo->d_moff = (uint32_t *)(p + b_l + b_s + b_m + b_f);
-    lo->d_poslayer = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o);
-    lo->d_small = (uint32_t *)(p + b_l + b_s + b_m + b_f + b_o + b_p);
-    return LAGS_OK;
-}
-
-int ensure_agg(lags_layout *lo, int32_t P, AggTables **out)
-{
-    auto it = lo->agg.find(P);
-    if (it != lo->agg.end()) {
-        *out = &it->second;
-        return LAGS_OK;
-    }
-    std::vector<uint32_t> cb, cs;
-    uint32_t NC;
-    plan_agg(lo, P, cb, cs, NC);
-    // per chunk: its index range inside its layer and the layer's message
-    // range, so that an aggregate workgroup needs one load to start
-    std::vector<uint4> ci(std::max<uint32_t>(NC, 1), uint4{0, 0, 0, 0});
-    for (int32_t l = 0; l < lo->L; ++l) {
-        const uint64_t off = lo->off[l], end = lo->off[l + 1];
-        for (uint32_t c = cb[l]; c < cb[l + 1]; ++c) {
-            const uint64_t clo = off + ((uint64_t)(c - cb[l]) << cs[l]);
-            const uint64_t chi = std::min<uint64_t>(clo + ((uint64_t)1 << cs[l]), end);
-            ci[c] = uint4{(uint32_t)clo, (uint32_t)chi, (uint32_t)lo->moff[l],
-                          (uint32_t)(lo->moff[l] + lo->k[l])};
-        }
-    }
-    const size_t b0 = align_up(cb.size() * 4, kAlign), b1 = align_up(cs.size() * 4, kAlign),
-                 b2 = align_up(ci.size() * sizeof(uint4), kAlign);
-    std::vector<unsigned char> host(b0 + b1 + b2, 0);
-    std::memcpy(host.data(), cb.data(), cb.size() * 4);
-    std::memcpy(host.data() + b0, cs.data(), cs.size() * 4);
-    std::memcpy(host.data() + b0 + b1, ci.data(), ci.size() * sizeof(uint4));
-    void *d = nullptr;
-    if (hipMalloc(&d, host.size()) != hipSuccess) return LAGS_ENOMEM;
-    if (hipMemcpy(d, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipFree(d);
-        return LAGS_EHIP;
-    }
-    AggTables t;
-    t.NC = NC;
-    t.h_cbase = cb;
-    t.dev = d;
-    t.cbase = (uint32_t *)d;
-    t.csh = (uint32_t *)((unsigned char *)d + b0);
-    t.chunk_info = (uint4 *)((unsigned char *)d + b0 + b1);
-    auto res = lo->agg.emplace(P, t);
-    *out = &res.first->second;
-    return LAGS_OK;
+    for (const WsRec &r : lo->wss)
+        if (r.ws == ws) return &r;
+    return nullptr;
 }
 
 // Launch with optional tracing events around it.
@@ -448,10 +431,123 @@ int sparsify_exact(lags_layout *lo, const SparsifyArgs &a, uint32_t ns, uint32_t
         if (rc != LAGS_OK) return rc;
     }
     if (ns) {
-        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
+        SparsifyArgs b = a;
+        b.fix_groups = 0;         // exact mode marks no layer for the fallback
+        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(b, nfin, s); });
         if (rc != LAGS_OK) return rc;
     }
     return LAGS_OK;
+}
+
+// Launch the sparsify kernels for layers [l0, l1) on a workspace whose head
+// holds the layout tables (caller holds lo->mu and has validated everything).
+int sparsify_launch(lags_layout *lo, int32_t l0, int32_t l1, const float *grad, float *residual,
+                    uint32_t *msg_idx, float *msg_val, unsigned char *w, uint32_t flags, hipStream_t s)
+{
+    SparsifyArgs a{};
+    a.grad = grad;
+    a.res = residual;
+    a.msg_idx = msg_idx;
+    a.msg_val = msg_val;
+    a.linfo = (const LayerInfo *)(w + lo->tb_linfo);
+    a.sinfo = (const SampledInfo *)(w + lo->tb_sinfo);
+    a.main_work = (const MainWork *)(w + lo->tb_main);
+    a.fin_work = (const FinWork *)(w + lo->tb_fin);
+    a.small_layers = (const uint32_t *)(w + lo->tb_small);
+    a.report = (uint32_t *)(w + lo->ws_report);
+    a.state = (SampledState *)(w + lo->ws_state);
+    a.hist = (uint32_t *)(w + lo->ws_hist);
+    a.seg_count = (uint32_t *)(w + lo->ws_segcount);
+    a.seg_sel = (uint32_t *)(w + lo->ws_segsel);
+    a.slots = (uint2 *)(w + lo->ws_slots);
+    a.tbin = (uint2 *)(w + lo->ws_tbin);
+    a.fin_total = (uint32_t *)(w + lo->ws_fintot);
+    a.fin_eq = (uint32_t *)(w + lo->ws_fineq);
+    a.fb = (uint32_t *)(w + lo->ws_fb);
+    a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
+    a.sample_base = lo->sid_pre[l0];
+    a.nsampled = lo->sid_pre[l1] - lo->sid_pre[l0];
+    a.main_base = lo->stream_pre[l0];
+    a.fin_base = lo->fin_pre[l0];
+    a.small_base = lo->small_pre[l0];
+    a.nsmall = lo->small_pre[l1] - lo->small_pre[l0];
+    const uint32_t ns = a.nsampled;
+    const uint32_t nmain = lo->stream_pre[l1] - lo->stream_pre[l0];
+    const uint32_t nfin = lo->fin_pre[l1] - lo->fin_pre[l0];
+    // the fallback's workgroups: about one per 8 segments of the range's
+    // sampled layers, at least the finishing workgroups, at most kFixGroups
+    // (k_fin_emit is launched with max(nfin, fix_groups) workgroups)
+    const uint32_t sid0 = lo->sid_pre[l0], sid1 = lo->sid_pre[l1];
+    const uint32_t nseg_range =
+        ns ? (sid1 < lo->sinfo.size() ? lo->sinfo[sid1].seg_base : lo->nseg_total) - lo->sinfo[sid0].seg_base
+           : 0u;
+    a.nfin = nfin;
+    a.fix_groups = std::min(kFixGroups, std::max(nfin, (nseg_range + 7u) / 8u));
+    int rc;
+    // k_sample always runs: its first workgroup restarts the report counters
+    rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
+    if (rc != LAGS_OK) return rc;
+    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, nfin, s);
+    if (nmain) {
+        rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    if (ns) {
+        rc = traced(lo, kKFinBins, s, [&] { return launch_fin_bins(a, ns, s); });
+        if (rc != LAGS_OK) return rc;
+        rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, nfin, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    if (ns + a.nsmall) {
+        rc = traced(lo, kKFinResolve, s, [&] { return launch_fin_resolve(a, ns + a.nsmall, s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    if (ns) {
+        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, std::max(nfin, a.fix_groups), s); });
+        if (rc != LAGS_OK) return rc;
+    }
+    return LAGS_OK;
+}
+
+// Launch the aggregate kernels for layers [l0, l1) with P workers on a
+// workspace initialised for Pw >= P workers (caller holds lo->mu).
+int aggregate_launch(lags_layout *lo, int32_t l0, int32_t l1, float *weights, const uint32_t *msg_idx,
+                     const float *msg_val, int32_t P, int32_t Pw, float lr, unsigned char *w,
+                     hipStream_t s)
+{
+    const AggPlan &t = agg_plan(lo, Pw);     // built when the workspace was initialised
+    unsigned char *tab = w + lo->ws_agg + align_up((size_t)Pw * ((size_t)t.NC + 1) * 4, kAlign);
+    AggArgs a{};
+    a.w = weights;
+    a.msg_idx = msg_idx;
+    a.msg_val = msg_val;
+    a.linfo = (const LayerInfo *)(w + lo->tb_linfo);
+    a.moff = (const uint32_t *)(w + lo->tb_moff);
+    a.pos_layer = (const uint32_t *)(w + lo->tb_pos);
+    a.cbase = (const uint32_t *)(tab + t.b_cbase);
+    a.csh = (const uint32_t *)(tab + t.b_csh);
+    a.chunk_info = (const uint4 *)(tab + t.b_info);
+    a.start = (uint32_t *)(w + lo->ws_agg);
+    a.report = (uint32_t *)(w + lo->ws_report);
+    a.L = (uint32_t)lo->L;
+    a.P = (uint32_t)P;
+    a.K = (uint32_t)lo->K;
+    a.NC = t.NC;
+    a.s = lr / (float)P;
+    a.j_lo = lo->moff[l0];
+    a.j_hi = lo->moff[l1];
+    a.c_lo = t.h_cbase[l0];
+    a.c_hi = t.h_cbase[l1];
+    a.npb = (uint32_t)lo->pos_layer.size();
+    // four position blocks per start-pass workgroup once the launch would
+    // take several rounds of workgroups (16K or more), else one
+    const uint64_t nblk = (uint64_t)(a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u) * (uint32_t)P;
+    const bool wide = nblk >= 16384 && 5ull * lo->starts_tl4 * 4 <= 32768;
+    a.bpw = wide ? 4u : 1u;
+    a.tl = wide ? lo->starts_tl4 : lo->starts_tl;
+    int rc = traced(lo, kKAggStarts, s, [&] { return launch_agg_starts(a, s); });
+    if (rc != LAGS_OK) return rc;
+    return traced(lo, kKAgg, s, [&] { return launch_agg(a, a.c_hi - a.c_lo, s); });
 }
 }  // namespace
 
@@ -465,8 +561,9 @@ const char *lags_strerror(int status)
     case LAGS_ERANGE: return "size out of the supported range";
     case LAGS_EWORKSPACE: return "workspace missing, misaligned or too small";
     case LAGS_EHIP: return "HIP runtime error";
-    case LAGS_EDEVICE: return "current device differs from the layout's device";
+    case LAGS_EDEVICE: return "current device differs from the workspace's device";
     case LAGS_ENOMEM: return "out of memory";
+    case LAGS_ENOTINIT: return "workspace not initialised for this layout (lags_workspace_init)";
     default: return "unknown status";
     }
 }
@@ -527,8 +624,6 @@ void lags_layout_destroy(lags_layout *lo)
         (void)hipEventDestroy(r.a);
         (void)hipEventDestroy(r.b);
     }
-    for (auto &kv : lo->agg) (void)hipFree(kv.second.dev);
-    if (lo->dev) (void)hipFree(lo->dev);
     delete lo;
 }
 
@@ -542,10 +637,54 @@ int64_t lags_layout_msg_offset(const lags_layout *lo, int32_t l)
     return (int64_t)lo->moff[l];
 }
 
-size_t lags_workspace_bytes(const lags_layout *lo, int32_t P)
+size_t lags_workspace_bytes(const lags_layout *clo, int32_t P)
 {
+    lags_layout *lo = const_cast<lags_layout *>(clo);
     if (!lo || P < 1 || P > LAGS_MAX_WORKERS) return 0;
-    return lo->ws_agg + agg_bytes(lo, P);
+    std::lock_guard<std::mutex> g(lo->mu);
+    try {
+        return lo->ws_agg + agg_tail_bytes(agg_plan(lo, P), P);
+    } catch (...) {
+        return 0;
+    }
+}
+
+int lags_workspace_init(const lags_layout *clo, void *ws, size_t ws_bytes, int32_t P, void *stream)
+{
+    lags_layout *lo = const_cast<lags_layout *>(clo);
+    if (!lo) return LAGS_EINVAL;
+    if (P < 1 || P > LAGS_MAX_WORKERS) return LAGS_ERANGE;
+    std::lock_guard<std::mutex> g(lo->mu);
+    const AggPlan *t;
+    try {
+        t = &agg_plan(lo, P);
+    } catch (...) {
+        return LAGS_ENOMEM;
+    }
+    const size_t need = lo->ws_agg + agg_tail_bytes(*t, P);
+    if (!ws || !aligned16(ws) || ws_bytes < need) return LAGS_EWORKSPACE;
+    WsRec rec{ws, need, P, -1};
+    if (hipGetDevice(&rec.device) != hipSuccess) return LAGS_EHIP;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char *w = (unsigned char *)ws;
+    // both images live in the layout until it is destroyed, so the copies
+    // may complete after this call returns
+    if (hipMemcpyAsync(w, lo->tables.data(), lo->tables.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+        return LAGS_EHIP;
+    const size_t tail = lo->ws_agg + align_up((size_t)P * ((size_t)t->NC + 1) * 4, kAlign);
+    if (hipMemcpyAsync(w + tail, t->image.data(), t->image.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+        return LAGS_EHIP;
+    for (WsRec &r : lo->wss)
+        if (r.ws == ws) {
+            r = rec;
+            return LAGS_OK;
+        }
+    try {
+        lo->wss.push_back(rec);
+    } catch (...) {
+        return LAGS_ENOMEM;
+    }
+    return LAGS_OK;
 }
 
 int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const float *grad,
@@ -565,65 +704,16 @@ int lags_sparsify_range(const lags_layout *clo, int32_t l0, int32_t l1, const fl
     for (int i = 0; i < 5; ++i)
         for (int j = i + 1; j < 5; ++j)
             if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
-    if (l0 == l1) return LAGS_OK;
 
     std::lock_guard<std::mutex> g(lo->mu);
-    int rc = ensure_device(lo);
-    if (rc != LAGS_OK) return rc;
-    hipStream_t s = (hipStream_t)stream;
-    unsigned char *w = (unsigned char *)ws;
-    SparsifyArgs a{};
-    a.grad = grad;
-    a.res = residual;
-    a.msg_idx = msg_idx;
-    a.msg_val = msg_val;
-    a.linfo = lo->d_linfo;
-    a.sinfo = lo->d_sinfo;
-    a.main_work = lo->d_main;
-    a.fin_work = lo->d_fin;
-    a.report = (uint32_t *)(w + lo->ws_report);
-    a.state = (SampledState *)(w + lo->ws_state);
-    a.hist = (uint32_t *)(w + lo->ws_hist);
-    a.seg_count = (uint32_t *)(w + lo->ws_segcount);
-    a.seg_sel = (uint32_t *)(w + lo->ws_segsel);
-    a.slots = (uint2 *)(w + lo->ws_slots);
-    a.tbin = (uint2 *)(w + lo->ws_tbin);
-    a.fin_total = (uint32_t *)(w + lo->ws_fintot);
-    a.fin_eq = (uint32_t *)(w + lo->ws_fineq);
-    a.force_exact = (flags & LAGS_SPARSIFY_EXACT) ? 1u : 0u;
-    a.sample_base = lo->sid_pre[l0];
-    a.nsampled = lo->sid_pre[l1] - lo->sid_pre[l0];
-    a.main_base = lo->stream_pre[l0];
-    a.fin_base = lo->fin_pre[l0];
-    a.small_layers = lo->d_small;
-    a.small_base = lo->small_pre[l0];
-    a.nsmall = lo->small_pre[l1] - lo->small_pre[l0];
-    const uint32_t ns = a.nsampled;
-    const uint32_t nmain = lo->stream_pre[l1] - lo->stream_pre[l0];
-    const uint32_t nfin = lo->fin_pre[l1] - lo->fin_pre[l0];
-    // k_sample always runs: its first workgroup restarts the report counters
-    rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });
-    if (rc != LAGS_OK) return rc;
-    if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, nfin, s);
-    if (nmain) {
-        rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
-        if (rc != LAGS_OK) return rc;
-    }
-    if (ns) {
-        rc = traced(lo, kKFinBins, s, [&] { return launch_fin_bins(a, ns, s); });
-        if (rc != LAGS_OK) return rc;
-        rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, nfin, s); });
-        if (rc != LAGS_OK) return rc;
-    }
-    if (ns + a.nsmall) {
-        rc = traced(lo, kKFinResolve, s, [&] { return launch_fin_resolve(a, ns + a.nsmall, s); });
-        if (rc != LAGS_OK) return rc;
-    }
-    if (ns) {
-        rc = traced(lo, kKFinEmit, s, [&] { return launch_fin_emit(a, nfin, s); });
-        if (rc != LAGS_OK) return rc;
-    }
-    return LAGS_OK;
+    const WsRec *rec = find_ws(lo, ws);
+    if (!rec) return LAGS_ENOTINIT;
+    if (l0 == l1) return LAGS_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LAGS_EHIP;
+    if (dev != rec->device) return LAGS_EDEVICE;
+    return sparsify_launch(lo, l0, l1, grad, residual, msg_idx, msg_val, (unsigned char *)ws, flags,
+                           (hipStream_t)stream);
 }
 
 int lags_sparsify_layers(const lags_layout *lo, const float *grad, float *residual,
@@ -645,55 +735,28 @@ int lags_aggregate_range(const lags_layout *clo, int32_t l0, int32_t l1, float *
     if (P < 1 || P > LAGS_MAX_WORKERS) return LAGS_ERANGE;
     if ((uint64_t)P * lo->K >= (1ull << 40)) return LAGS_ERANGE;
     if (!aligned16(weights) || !aligned16(msg_idx) || !aligned16(msg_val)) return LAGS_EINVAL;
-    const size_t need = lo->ws_agg + agg_bytes(lo, P);
-    if (!ws || !aligned16(ws) || ws_bytes < need) return LAGS_EWORKSPACE;
+    if (!ws || !aligned16(ws)) return LAGS_EWORKSPACE;
     const size_t nb = lo->n * 4, mb = (size_t)P * lo->K * 4;
     const void *bufs[4] = {weights, msg_idx, msg_val, ws};
-    const size_t lens[4] = {nb, mb, mb, need};
-    for (int i = 0; i < 4; ++i)
-        for (int j = i + 1; j < 4; ++j)
+    size_t lens[4] = {nb, mb, mb, 0};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
             if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
-    if (l0 == l1) return LAGS_OK;
 
     std::lock_guard<std::mutex> g(lo->mu);
-    int rc = ensure_device(lo);
-    if (rc != LAGS_OK) return rc;
-    AggTables *t = nullptr;
-    rc = ensure_agg(lo, P, &t);
-    if (rc != LAGS_OK) return rc;
-    hipStream_t s = (hipStream_t)stream;
-    unsigned char *w = (unsigned char *)ws;
-    AggArgs a{};
-    a.w = weights;
-    a.msg_idx = msg_idx;
-    a.msg_val = msg_val;
-    a.linfo = lo->d_linfo;
-    a.moff = lo->d_moff;
-    a.pos_layer = lo->d_poslayer;
-    a.cbase = t->cbase;
-    a.csh = t->csh;
-    a.chunk_info = t->chunk_info;
-    a.start = (uint32_t *)(w + lo->ws_agg);
-    a.report = (uint32_t *)(w + lo->ws_report);
-    a.L = (uint32_t)lo->L;
-    a.P = (uint32_t)P;
-    a.K = (uint32_t)lo->K;
-    a.NC = t->NC;
-    a.s = lr / (float)P;
-    a.j_lo = lo->moff[l0];
-    a.j_hi = lo->moff[l1];
-    a.c_lo = t->h_cbase[l0];
-    a.c_hi = t->h_cbase[l1];
-    a.npb = (uint32_t)lo->pos_layer.size();
-    // four position blocks per start-pass workgroup once the launch would
-    // take several rounds of workgroups (16K or more), else one
-    const uint64_t nblk = (uint64_t)(a.j_hi / kStartsBlock - a.j_lo / kStartsBlock + 1u) * (uint32_t)P;
-    const bool wide = nblk >= 16384 && 5ull * lo->starts_tl4 * 4 <= 32768;
-    a.bpw = wide ? 4u : 1u;
-    a.tl = wide ? lo->starts_tl4 : lo->starts_tl;
-    rc = traced(lo, kKAggStarts, s, [&] { return launch_agg_starts(a, s); });
-    if (rc != LAGS_OK) return rc;
-    return traced(lo, kKAgg, s, [&] { return launch_agg(a, a.c_hi - a.c_lo, s); });
+    const WsRec *rec = find_ws(lo, ws);
+    if (!rec) return LAGS_ENOTINIT;
+    if (P > rec->P) return LAGS_EWORKSPACE;        // initialised for fewer workers
+    if (ws_bytes < rec->bytes) return LAGS_EWORKSPACE;
+    lens[3] = rec->bytes;
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(bufs[i], lens[i], bufs[3], lens[3])) return LAGS_EINVAL;
+    if (l0 == l1) return LAGS_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LAGS_EHIP;
+    if (dev != rec->device) return LAGS_EDEVICE;
+    return aggregate_launch(lo, l0, l1, weights, msg_idx, msg_val, P, rec->P, lr, (unsigned char *)ws,
+                            (hipStream_t)stream);
 }
 
 int lags_aggregate_apply(const lags_layout *lo, float *weights, const uint32_t *msg_idx,
@@ -709,9 +772,9 @@ int lags_workspace_report(const lags_layout *lo, const void *ws, size_t ws_bytes
                           lags_report *out)
 {
     if (!lo || !ws || !out) return LAGS_EINVAL;
-    if (ws_bytes < lo->ws_report + 20) return LAGS_EWORKSPACE;
+    if (ws_bytes < lo->ws_report + kRepWords * 4) return LAGS_EWORKSPACE;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LAGS_EHIP;
-    uint32_t h[5];
+    uint32_t h[6];
     if (hipMemcpy(h, (const unsigned char *)ws + lo->ws_report, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess)
         return LAGS_EHIP;
     out->layers_sampled = (int32_t)h[kRepSampled];
@@ -719,6 +782,7 @@ int lags_workspace_report(const lags_layout *lo, const void *ws, size_t ws_bytes
     out->bad_entries = h[kRepBad];
     out->slow_chunks = h[kRepSlow];
     out->layers_wide_bin = (int32_t)h[kRepWide];
+    out->fix_timeouts = h[kRepFixTimeout];
     return LAGS_OK;
 }
 

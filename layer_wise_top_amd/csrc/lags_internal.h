@@ -42,6 +42,14 @@ constexpr uint32_t kAggTableLog2 = 11;
 constexpr uint32_t kAggTable = 1u << kAggTableLog2;  // LDS hash slots (>= 2 * kAggCap);
                                                      // also the slow path's dense window
 constexpr uint32_t kAggMaxWidthLog2 = 30;     // chunk width cap (entries)
+// guess-failure fallback (inside k_fin_emit): the first kFixGroups workgroups
+// of the launch select every failed layer together, by a radix select over all
+// of its keys, meeting at barriers between the passes
+constexpr uint32_t kFixGroups = 512;
+// per sampled layer: histograms of the three key digits (11, 11 and 9 bits),
+// then per fallback workgroup its count of keys above and equal to the threshold
+constexpr uint32_t kFbHist0 = 0, kFbHist1 = 2048, kFbHist2 = 4096, kFbCount = 4608;
+constexpr uint32_t kFbWords = kFbCount + 2 * kFixGroups;
 
 // ---- layer classes --------------------------------------------------------
 enum : uint32_t {
@@ -57,6 +65,9 @@ enum : uint32_t {
     kStExact = 2,     // the exact multi-pass path handled the layer
     kStZero = 3,      // guess G = 0 and fewer than k nonzero keys: T = 0, all nonzero
                       // entries plus the lowest-index zeros are sent
+    kStFix = 4,       // the guess failed (fewer than k candidates above a nonzero G, or a
+                      // threshold bin larger than its list): k_fin_emit's fallback
+                      // workgroups select the layer from all of its keys
 };
 
 struct LayerInfo {        // one per layer, device table
@@ -136,7 +147,10 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t xrank;       // exact mode: rank still to find among keys with that prefix
     uint32_t T;           // k-th largest key of the layer
     uint32_t idx_cut;     // largest global index taken among keys == T
-    uint32_t pad0[22];
+    uint32_t fix_bar;     // fallback: arrivals at the barriers between its passes
+    uint32_t nfail;       // (first sampled layer of a launched range only) layers of the
+                          // range that need the fallback
+    uint32_t pad0[20];
     // on a cache line of its own: every finishing workgroup of the layer
     // reads the fields above while the select pass adds to this one
     uint32_t tbin_n;      // entries of bin bstar collected
@@ -146,7 +160,10 @@ static_assert(offsetof(SampledState, tbin_n) == 128 && sizeof(SampledState) == 2
               "the collection counter sits on its own 128-byte line");
 
 // report counters at the head of the workspace
-enum : uint32_t { kRepSampled = 0, kRepExact = 1, kRepBad = 2, kRepSlow = 3, kRepWide = 4, kRepWords = 64 };
+enum : uint32_t {
+    kRepSampled = 0, kRepExact = 1, kRepBad = 2, kRepSlow = 3, kRepWide = 4, kRepFixTimeout = 5,
+    kRepWords = 64
+};
 
 struct SparsifyArgs {
     const float *grad;
@@ -166,6 +183,10 @@ struct SparsifyArgs {
     uint2 *tbin;
     uint32_t *fin_total;      // per finishing workgroup: count, then message offset
     uint32_t *fin_eq;         // per finishing workgroup (zero mode): zeros, then zeros before it
+    uint32_t *fb;             // per sampled layer kFbWords words: the fallback's histograms, counts
+    uint32_t fix_groups;      // workgroups of the k_fin_emit launch that run the fallback
+    uint32_t nfin;            // finishing workgroups of the launched range (k_fin_emit may
+                              // launch more: the extra ones only run the fallback)
     uint32_t nsampled;        // sampled layers in the launched range
     uint32_t force_exact;
     // the launched layer range, as offsets into the layout's work lists

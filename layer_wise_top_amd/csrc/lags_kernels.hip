@@ -378,6 +378,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 
     if (blockIdx.x == 0 && threadIdx.x < 2) a.report[kRepSampled + threadIdx.x] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 2) a.report[kRepWide] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 3) a.report[kRepFixTimeout] = 0;
     if (blockIdx.x >= a.nsampled) return;
     const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
@@ -582,6 +583,22 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
     return min((key - G) >> SH, kNBins - 1u);
 }
 
+// Add the active lanes' bins to a device histogram with one atomic per
+// distinct bin of the wave.  All lanes of the wave call.
+__device__ __forceinline__ void wave_bin_add(uint32_t *hist, uint32_t bin, bool active)
+{
+    uint64_t todo = __ballot(active);
+    while (todo) {
+        const uint32_t leader = (uint32_t)__ffsll((unsigned long long)todo) - 1u;
+        const uint32_t b = __shfl(bin, leader, 64);
+        const uint64_t same = __ballot(active && bin == b);
+        if (lane_id() == leader) atomicAdd(&hist[b], (uint32_t)__popcll(same));
+        todo &= ~same;
+    }
+}
+
+constexpr uint32_t kHeavySeg = 256;   // candidates of a segment counted per wave beyond this
+
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
                                 const SampledState *st, uint32_t *hist, uint2 *stage,
                                 uint32_t (*wtot)[kWaves])
@@ -620,12 +637,16 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
 
     const uint32_t cap = w.cap;
     const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * cap;
+    // a segment with many candidates (equal keys, clustered large values)
+    // counts them with one atomic per distinct bin of each wave instead of one
+    // per candidate: thousands of device atomics on one address serialise
+    const bool heavy = total > kHeavySeg;   // uniform over the workgroup
     auto put = [&](uint32_t p, uint32_t idx, float v) {
         const uint2 e = make_uint2(idx, __float_as_uint(v));
         if (p < kCapMax) stage[p] = e;
         else if (p < cap) a.slots[slot0 + p] = e;   // only layers of <= kSampleMax entries
                                                      // have more than kCapMax slots
-        atomicAdd(&hist[cand_bin(key_of(v), G, SH)], 1u);
+        if (!heavy) atomicAdd(&hist[cand_bin(key_of(v), G, SH)], 1u);
     };
     if (c[0]) put(pos[0], sv.hlo + t, hv);
 #pragma unroll
@@ -636,6 +657,15 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
             if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * sv.row(u) + j, acc[u][j]);
     }
     if (c[kParts - 1]) put(pos[kParts - 1], sv.tlo + t, tv);
+    if (heavy) {
+        wave_bin_add(hist, cand_bin(key_of(hv), G, SH), c[0] != 0u);
+#pragma unroll
+        for (int u = 0; u < kRows; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wave_bin_add(hist, cand_bin(key_of(acc[u][j]), G, SH), ((fl >> (4 * u + j)) & 1u) != 0u);
+        wave_bin_add(hist, cand_bin(key_of(tv), G, SH), c[kParts - 1] != 0u);
+    }
     __syncthreads();
     // a segment with more candidates than slots keeps only the first cap
     // (the finishing kernels re-read it)
@@ -724,6 +754,21 @@ __device__ __forceinline__ uint32_t seg_len(const FinWork &f, uint32_t s)
     return len;
 }
 
+// Hand a sampled layer whose guess failed to the fallback of k_fin_emit:
+// status kStFix, one more failed layer in the range's count, the layer's
+// fallback histograms cleared.  All NT threads of the workgroup call.
+template <int NT>
+__device__ void mark_for_fix(const SparsifyArgs &a, uint32_t sid)
+{
+    uint32_t *fb = a.fb + (uint64_t)sid * kFbWords;
+    for (uint32_t t = threadIdx.x; t < kFbCount; t += NT) fb[t] = 0;
+    if (threadIdx.x == 0) {
+        a.state[sid].status = kStFix;
+        atomicAdd(&a.state[a.sample_base].nfail, 1u);
+        atomicAdd(&a.report[kRepExact], 1u);
+    }
+}
+
 // k_fin_bins: one 1024-thread workgroup per sampled layer, after the
 // streaming pass has filled the layer's histogram copies.  Sums the copies
 // (eight loads in flight per thread), then locates the candidate bin that
@@ -759,11 +804,8 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     uint32_t C;
     block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above
     if (C < L.k && st->G != 0) {
-        if (threadIdx.x == 0) {
-            st->status = kStExact;
-            atomicAdd(&a.report[kRepSampled], 1u);
-            atomicAdd(&a.report[kRepExact], 1u);
-        }
+        mark_for_fix<NT>(a, sid);
+        if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
         return;
     }
     if (C < L.k) {
@@ -778,6 +820,13 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
         return;
     }
     block_find_rank<NT>(hist, kNBins, L.k, res, tmp);
+    if (hist[res[0]] > S.tbin_cap) {
+        // the threshold bin holds more candidates than the layer's list (many
+        // equal keys): the fallback selects the layer
+        mark_for_fix<NT>(a, sid);
+        if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
+        return;
+    }
     if (threadIdx.x == 0) {
         st->bstar = res[0];
         st->c_above = res[1];
@@ -1107,15 +1156,11 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
         return;
     }
 
-    if (status != kStOk || h > S.tbin_cap) {
-        // the residual buffer holds acc for every entry of the layer
-        if (threadIdx.x == 0) {
-            if (status == kStOk) atomicAdd(&a.report[kRepExact], 1u);
-            st->status = kStExact;
-        }
-        const float *accp = a.res + L.off;
-        exact_layer<false>([&](uint32_t i) { return accp[i]; }, L.n, L.k, L.off, L.moff,
-                           a.res + L.off, a.msg_idx, a.msg_val, hist, tmp, res);
+    if (status != kStOk) return;       // kStFix: the fallback takes the layer
+    if (h > S.tbin_cap) {
+        // more threshold-bin entries than the list holds (many equal keys in
+        // segments re-read from acc): the fallback selects the layer
+        mark_for_fix<kBlock>(a, sid);
         return;
     }
 
@@ -1221,14 +1266,25 @@ __device__ void emit_rescan(const SparsifyArgs &a, const FinWork &f, uint32_t se
     });
 }
 
-// k_fin_emit: write the selected candidates of each segment, in index order,
-// and zero their residual.  Segments with more candidates than slots, and in
-// zero mode segments that send zeros, are re-read whole instead.
-__global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
+// Shared memory of the guess-failure fallback (fix_layers, below).
+struct FixLds {
+    uint32_t hl[2048];            // this workgroup's histogram of the current digit
+    uint32_t hp[2048];            // the layer's histogram of the current digit
+    uint32_t flag[kBlock];        // failed layers among the next kBlock sampled layers
+    uint32_t wtot[kParts][kWaves];
+    uint32_t tmp[kWaves];
+    uint32_t res[2];
+    uint32_t run[2];
+};
+__device__ void fix_layers(const SparsifyArgs &a, FixLds &x);
+
+// Emission of one finishing workgroup's segments (the body of k_fin_emit).
+__device__ void emit_segments(const SparsifyArgs &a)
 {
     __shared__ uint32_t sbase[kFinSegs];
     __shared__ uint32_t ztake[kFinSegs];
     __shared__ uint32_t redo[kFinSegs];
+    if (blockIdx.x >= a.nfin) return;        // a workgroup launched for the fallback only
     const uint32_t fb = a.fin_base + blockIdx.x;
     const FinWork f = a.fin_work[fb];
     const SampledState *st = a.state + f.sid;
@@ -1299,6 +1355,17 @@ __global__ __launch_bounds__(kBlock) void k_fin_emit(SparsifyArgs a)
         if (zero) emit_rescan<true>(a, f, s, sbase[s - f.seg0], ztake[s - f.seg0], 0u, 0u);
         else emit_rescan<false>(a, f, s, sbase[s - f.seg0], 0u, T, cut);
     }
+}
+
+// k_fin_emit: write the selected candidates of each segment, in index order,
+// and zero their residual.  Segments with more candidates than slots, and in
+// zero mode segments that send zeros, are re-read whole instead.  Then the
+// first a.fix_groups workgroups select the layers whose guess failed, if any.
+__global__ __launch_bounds__(kBlock, 8) void k_fin_emit(SparsifyArgs a)
+{
+    __shared__ FixLds x;
+    emit_segments(a);
+    if (blockIdx.x < a.fix_groups) fix_layers(a, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1676,6 +1743,219 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
         st->status = kStOk;
         atomicAdd(&a.report[kRepSampled], 1u);
         atomicAdd(&a.report[kRepExact], 1u);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Guess-failure fallback.  A sampled layer whose guess failed (fewer than k
+// candidates above a nonzero G, or a threshold bin beyond its list) is marked
+// kStFix and selected here from all of its keys, which the residual buffer
+// holds (acc) after the streaming pass.  The first a.fix_groups workgroups of
+// the k_fin_emit launch (at most kFixGroups, dispatched first and all resident
+// at once) split the layer's segments into contiguous ranges and run the
+// exact-mode radix select over them: three digit passes (11, 11 and 9 key
+// bits), each adding the workgroup's LDS histogram of the keys that match the
+// prefix found so far into the layer's histogram of that digit, then meeting
+// at a barrier after which every workgroup reads that histogram and picks the
+// same digit.  The last pass also counts, per workgroup, the keys whose top 22
+// bits exceed the prefix; with the workgroup's own last-digit histogram that
+// gives its keys above and equal to the threshold T.  After one more barrier
+// every workgroup scans those counts for its ties before it (only the first e
+// keys equal to T, in index order, are sent) and its message position, and
+// emits its segments in index order.  Four passes of 4 bytes per entry, all
+// workgroups streaming.  Every wait is bounded: a barrier that is not reached
+// in time is counted in the report and passed (the layer's output is then
+// wrong; stores stay inside the layer and its message range).
+
+constexpr uint32_t kFixSpin = 1u << 22;   // sleeps of ~0.3 us: about a second
+
+__device__ void fix_barrier(const SparsifyArgs &a, uint32_t *ctr, uint32_t target)
+{
+    wait_mem_done();          // this thread's atomics into the layer's histogram are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t it = 0;
+        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(8);
+            if (++it >= kFixSpin) {
+                atomicAdd(&a.report[kRepFixTimeout], 1u);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
+{
+    const uint32_t F = a.fix_groups, wg = blockIdx.x, t = threadIdx.x;
+    const SampledInfo S = a.sinfo[sid];
+    const LayerInfo L = a.linfo[S.layer];
+    uint32_t *fb = a.fb + (uint64_t)sid * kFbWords;
+    uint32_t *bar = &a.state[sid].fix_bar;
+    MainWork mw{};                        // the fields seg_view reads
+    mw.off = L.off;
+    mw.end = L.off + L.n;
+    mw.a4 = S.a4;
+    mw.b4 = S.b4;
+    mw.nseg = S.nseg;
+    const uint32_t s_lo = (uint32_t)((uint64_t)S.nseg * wg / F);
+    const uint32_t s_hi = (uint32_t)((uint64_t)S.nseg * (wg + 1u) / F);
+
+    uint32_t prefix = 0, rank = L.k, gt22 = 0;
+    for (uint32_t level = 0; level < 3u; ++level) {
+        const uint32_t sh = x_shift(level), nb = x_bins(level);
+        const uint32_t top = level == 0u ? 32u : x_shift(level - 1u);
+        for (uint32_t b = t; b < 2048u; b += kBlock) x.hl[b] = 0;
+        __syncthreads();
+        for (uint32_t sg = s_lo; sg < s_hi; ++sg) {
+            XSeg xs;
+            xs.load(a, mw, sg);
+            xs.each([&](uint32_t, float v) {
+                const uint32_t key = key_of(v);
+                if (top >= 32u || (key >> top) == (prefix >> top)) atomicAdd(&x.hl[(key >> sh) & (nb - 1u)], 1u);
+                if (level == 2u && (key >> kXShift1) > (prefix >> kXShift1)) ++gt22;
+            });
+        }
+        __syncthreads();
+        uint32_t *gh = fb + (level == 0u ? kFbHist0 : (level == 1u ? kFbHist1 : kFbHist2));
+        for (uint32_t b = t; b < nb; b += kBlock)
+            if (x.hl[b]) atomicAdd(&gh[b], x.hl[b]);
+        fix_barrier(a, bar, F * (level + 1u));
+        for (uint32_t b = t; b < nb; b += kBlock) x.hp[b] = ld_coherent(&gh[b]);
+        __syncthreads();
+        block_find_rank(x.hp, nb, rank, x.res, x.tmp);
+        prefix |= x.res[0] << sh;
+        rank -= x.res[1];
+        __syncthreads();
+    }
+    const uint32_t T = prefix, e = rank, d2 = T & 511u;
+
+    // this workgroup's keys above T (top 22 bits above, or the last digit
+    // above) and equal to T; x.hl still holds its last-digit histogram
+    uint32_t above = gt22;
+    for (uint32_t b = t; b < 512u; b += kBlock) above += b > d2 ? x.hl[b] : 0u;
+    uint32_t wgt;
+    block_excl_scan(above, x.tmp, wgt);
+    if (t == 0) {
+        __hip_atomic_store(&fb[kFbCount + wg], wgt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&fb[kFbCount + F + wg], x.hl[d2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    fix_barrier(a, bar, F * 4u);
+
+    // ties and sent entries of the workgroups before this one
+    uint32_t ceq = 0, csel = 0;
+    for (uint32_t base = 0; base < F; base += kBlock) {
+        const uint32_t v = base + t;
+        const uint32_t g = v < F ? ld_coherent(&fb[kFbCount + v]) : 0u;
+        const uint32_t q = v < F ? ld_coherent(&fb[kFbCount + F + v]) : 0u;
+        uint32_t teq, tsel;
+        const uint32_t eqx = ceq + block_excl_scan(q, x.tmp, teq);
+        const uint32_t take = eqx >= e ? 0u : min(q, e - eqx);
+        const uint32_t selx = csel + block_excl_scan(g + take, x.tmp, tsel);
+        if (v == wg) {
+            x.run[0] = eqx;
+            x.run[1] = selx;
+        }
+        ceq += teq;
+        csel += tsel;
+    }
+    __syncthreads();
+    uint32_t run_eq = x.run[0], run_sel = x.run[1];
+
+    // emission, segment by segment in index order; the segment's values are
+    // staged in LDS (the histograms are no longer needed) so that only their
+    // flags stay in registers
+    float *stage = reinterpret_cast<float *>(x.hl);   // hl and hp: kSeg floats
+    static_assert(sizeof(x.hl) + sizeof(x.hp) >= kSeg * sizeof(float), "a segment fits the stage");
+    const uint32_t mend = L.moff + L.k;
+    for (uint32_t sg = s_lo; sg < s_hi; ++sg) {
+        SegView sv;
+        uint32_t fgt = 0, feq = 0;        // bit 4u + j: entry j of row u
+        float hv, tv;
+        {
+            XSeg xs;
+            xs.load(a, mw, sg);
+            sv = xs.sv;
+            hv = xs.hv;
+            tv = xs.tv;
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                reinterpret_cast<v4f *>(stage)[u * kBlock + t] = xs.x[u];
+                if (sv.row_in(u)) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t key = key_of(xs.x[u][j]);
+                        if (key > T) fgt |= 1u << (4 * u + j);
+                        else if (key == T) feq |= 1u << (4 * u + j);
+                    }
+                }
+            }
+        }
+        const bool hin = t < sv.nh, tin = t < sv.ntl;
+        const uint32_t hk = key_of(hv), tk = key_of(tv);
+        uint32_t c[kParts], p[kParts];
+        c[0] = (hin && hk == T) ? 1u : 0u;
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((feq >> (4 * u)) & 15u);
+        c[kParts - 1] = (tin && tk == T) ? 1u : 0u;
+        const uint32_t neq = block_positions(c, p, x.wtot);
+        __syncthreads();
+        // ties are sent while fewer than e came before them
+        const bool hsel = hin && (hk > T || (hk == T && run_eq + p[0] < e));
+        const bool tsel = tin && (tk > T || (tk == T && run_eq + p[kParts - 1] < e));
+        uint32_t fsel = fgt;
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            uint32_t r = run_eq + p[1 + u];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((feq >> (4 * u + j)) & 1u) {
+                    if (r < e) fsel |= 1u << (4 * u + j);
+                    ++r;
+                }
+        }
+        c[0] = hsel ? 1u : 0u;
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) c[1 + u] = (uint32_t)__popc((fsel >> (4 * u)) & 15u);
+        c[kParts - 1] = tsel ? 1u : 0u;
+        const uint32_t nsel = block_positions(c, p, x.wtot);
+        auto put = [&](uint32_t pos, uint32_t idx, float v) {
+            const uint32_t m = L.moff + run_sel + pos;
+            if (m < mend) {                  // the layer's selection holds exactly k entries
+                a.msg_idx[m] = idx;
+                a.msg_val[m] = v;
+            }
+            a.res[idx] = 0.0f;
+        };
+        if (hsel) put(p[0], sv.hlo + t, hv);
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            uint32_t q = p[1 + u];
+            for (int j = 0; j < 4; ++j)
+                if ((fsel >> (4 * u + j)) & 1u) put(q++, 4u * sv.row(u) + j, stage[(u * kBlock + t) * 4 + j]);
+        }
+        if (tsel) put(p[kParts - 1], sv.tlo + t, tv);
+        run_eq += neq;
+        run_sel += nsel;
+        __syncthreads();
+    }
+}
+
+// Select every layer of the launched range that is marked for the fallback,
+// one after another (each with its own barrier counter and histograms).
+__device__ void fix_layers(const SparsifyArgs &a, FixLds &x)
+{
+    if (a.nsampled == 0 || a.state[a.sample_base].nfail == 0) return;   // uniform
+    __syncthreads();
+    for (uint32_t base = 0; base < a.nsampled; base += kBlock) {
+        const uint32_t i = base + threadIdx.x;
+        x.flag[threadIdx.x] = (i < a.nsampled && a.state[a.sample_base + i].status == kStFix) ? 1u : 0u;
+        __syncthreads();
+        for (uint32_t j = 0; j < (uint32_t)kBlock && base + j < a.nsampled; ++j)
+            if (x.flag[j]) fix_layer(a, a.sample_base + base + j, x);
+        __syncthreads();
     }
 }
 

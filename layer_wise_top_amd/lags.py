@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblags.so")
 
 LAGS_OK = 0
+LAGS_ENOTINIT = -7
 LAGS_SPARSIFY_EXACT = 1
 LAGS_MAX_LAYERS = 65536
 LAGS_MAX_WORKERS = 1024
@@ -28,6 +29,7 @@ EXPORTED = (
     "lags_aggregate_apply", "lags_workspace_report", "lags_trace_enable",
     "lags_trace_read", "lags_num_kernels", "lags_kernel_name", "lags_sparsify_range",
     "lags_aggregate_range", "lags_merge_schedule", "lags_schedule_finish", "lags_adaptive_k",
+    "lags_workspace_init",
 )
 
 
@@ -40,7 +42,7 @@ class LagsError(RuntimeError):
 class Report(ctypes.Structure):
     _fields_ = [("layers_sampled", ctypes.c_int32), ("layers_exact", ctypes.c_int32),
                 ("bad_entries", ctypes.c_uint32), ("slow_chunks", ctypes.c_uint32),
-                ("layers_wide_bin", ctypes.c_int32)]
+                ("layers_wide_bin", ctypes.c_int32), ("fix_timeouts", ctypes.c_uint32)]
 
 
 _lib = None
@@ -73,6 +75,8 @@ def lib():
     L.lags_layout_msg_offset.argtypes = [vp, i32]
     L.lags_workspace_bytes.restype = sz
     L.lags_workspace_bytes.argtypes = [vp, i32]
+    L.lags_workspace_init.restype = ctypes.c_int
+    L.lags_workspace_init.argtypes = [vp, vp, sz, i32, vp]
     L.lags_sparsify_layers.restype = ctypes.c_int
     L.lags_sparsify_layers.argtypes = [vp, vp, vp, vp, vp, vp, sz, u32, vp]
     L.lags_aggregate_apply.restype = ctypes.c_int
@@ -187,13 +191,27 @@ def _dev_tensor(t, dtype, numel: int, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def workspace(layout: Layout, P: int = 1, device=None):
-    """Allocate a device workspace (uint8 tensor) for `layout` and up to P workers."""
+def workspace(layout: Layout, P: int = 1, device=None, stream=None):
+    """Allocate a device workspace (uint8 tensor) for `layout` and up to P
+    workers and initialise it (lags_workspace_init on `stream`, then that
+    stream is synchronised, so the workspace is ready for calls on any
+    stream)."""
     import torch
     nbytes = layout.workspace_bytes(P)
     if nbytes == 0:
         raise ValueError("invalid P")
-    return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+    lags_workspace_init(layout, ws, P, stream)
+    (stream if stream is not None else torch.cuda.current_stream(ws.device)).synchronize()
+    return ws
+
+
+def lags_workspace_init(layout: Layout, ws, P: int = 1, stream=None):
+    """Copy the layout's tables (and the chunk tables for P workers) into ws."""
+    import torch
+    w = _dev_tensor(ws, torch.uint8, 1, "ws")
+    rc = lib().lags_workspace_init(layout.handle, w, ws.numel(), int(P), _stream_handle(stream))
+    _check("lags_workspace_init", rc)
 
 
 def lags_sparsify_layers(layout: Layout, grad, residual, msg_idx, msg_val, ws,

@@ -77,7 +77,8 @@ def test_layout_validation():
     assert _create([0, 10, 20], [0, 1]) == -1      # k = 0
     assert _create([0, 10, 20], [11, 1]) == -1     # k > n
     assert _create([0, 2**32], [1]) == -2          # n >= 2^32
-    assert _create([0, 2**32 - 1], [1]) == -2
+    assert _create([0, 2**32 - 1], [1]) == -2      # 0xffffffff stays free as a marker
+    assert _create([0, 2**32 - 2], [1]) == 0       # the largest accepted size
     assert lags.lib().lags_layout_create(0, None, None, ctypes.byref(ctypes.c_void_p())) == -1
     off = np.array([0, 1], np.int64)
     k = np.array([1], np.int64)
@@ -125,7 +126,7 @@ def test_calls_reject_bad_arguments_without_a_device():
     wsP = lay.workspace_bytes(4)
     assert ag(h, g, mi, mv, 0, ctypes.c_float(0.1), ws, wsP, None) == -2
     assert ag(h, g, mi, mv, 1025, ctypes.c_float(0.1), ws, wsP, None) == -2
-    assert ag(h, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP - 1, None) == -3   # one byte short
+    assert ag(h, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == -7      # not initialised
     assert ag(h, g + 8, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == -1
     assert ag(h, g, mi, mi + 16, 4, ctypes.c_float(0.1), ws, wsP, None) == -1  # idx/val overlap
     # layer ranges: bad ranges are rejected, an empty range launches nothing
@@ -133,9 +134,61 @@ def test_calls_reject_bad_arguments_without_a_device():
     for l0, l1 in ((-1, 1), (0, 3), (2, 1)):
         assert spr(h, l0, l1, g, r, mi, mv, ws, ws_need, 0, None) == -2
         assert agr(h, l0, l1, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == -2
-    assert spr(h, 1, 1, g, r, mi, mv, ws, ws_need, 0, None) == 0
-    assert agr(h, 2, 2, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == 0
+    # an empty range still needs an initialised workspace
+    assert spr(h, 1, 1, g, r, mi, mv, ws, ws_need, 0, None) == -7
+    assert agr(h, 2, 2, g, mi, mv, 4, ctypes.c_float(0.1), ws, wsP, None) == -7
     assert spr(h, 0, 1, g, r, mi, mv, ws, 16, 0, None) == -3
     assert agr(h, 0, 1, g, mi, mi + 16, 4, ctypes.c_float(0.1), ws, wsP, None) == -1
     assert L.lags_trace_enable(None, 1) == -1
     lay.close()
+
+
+def test_calls_before_workspace_init_fail():
+    """The sparsify and aggregate calls accept only a workspace that
+    lags_workspace_init prepared for the layout; the check is on the host, so
+    it returns before any HIP call."""
+    L = lags.lib()
+    lay = lags.Layout([0, 5000, 9000], [5, 4])
+    h = lay.handle
+    base = 1 << 40                              # never dereferenced
+    g, r, mi, mv, ws = (base + (i << 20) for i in range(5))
+    for P in (1, 4):
+        need = lay.workspace_bytes(P)
+        assert L.lags_sparsify_layers(h, g, r, mi, mv, ws, need, 0, None) == lags.LAGS_ENOTINIT
+        assert L.lags_sparsify_range(h, 0, 2, g, r, mi, mv, ws, need, 0, None) == lags.LAGS_ENOTINIT
+        assert L.lags_aggregate_apply(h, g, mi, mv, P, ctypes.c_float(0.1), ws, need,
+                                      None) == lags.LAGS_ENOTINIT
+        assert L.lags_aggregate_range(h, 1, 2, g, mi, mv, P, ctypes.c_float(0.1), ws, need,
+                                      None) == lags.LAGS_ENOTINIT
+    assert "lags_workspace_init" in lags.strerror(lags.LAGS_ENOTINIT)
+
+
+def test_workspace_init_validation():
+    """lags_workspace_init rejects a bad layout, worker count or workspace
+    before any HIP call."""
+    L = lags.lib()
+    lay = lags.Layout([0, 5000, 9000], [5, 4])
+    h = lay.handle
+    ws = 1 << 40
+    need = lay.workspace_bytes(4)
+    assert L.lags_workspace_init(None, ws, need, 4, None) == -1
+    assert L.lags_workspace_init(h, ws, need, 0, None) == -2
+    assert L.lags_workspace_init(h, ws, need, 1025, None) == -2
+    assert L.lags_workspace_init(h, None, need, 4, None) == -3
+    assert L.lags_workspace_init(h, ws + 8, need, 4, None) == -3     # misaligned
+    assert L.lags_workspace_init(h, ws, need - 1, 4, None) == -3     # one byte short
+    # the workspace grows with the worker count (chunk-start table, chunk tables)
+    sizes = [lay.workspace_bytes(P) for P in (1, 4, 64, 1024)]
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
+
+
+def test_no_device_allocation_in_the_library():
+    """The library allocates no device memory: its sources call neither
+    hipMalloc nor hipFree (the caller's workspace holds every table)."""
+    import glob
+    srcs = glob.glob(os.path.join(ROOT, "layer_wise_top_amd", "csrc", "*"))
+    assert srcs
+    for p in srcs:
+        text = open(p).read()
+        for name in ("hipMalloc", "hipFree", "hipExtMalloc", "hipHostMalloc"):
+            assert name not in text, (p, name)
