@@ -49,12 +49,20 @@ _lib = None
 
 
 def lib():
-    """Load liblags.so (raises if it has not been built)."""
+    """Load liblags.so (raises if it has not been built).
+
+    torch is imported first: its HIP runtime (torch/lib/libamdhip64.so, soname
+    libamdhip64.so.7) must be the one the library binds to, since the device
+    pointers and streams passed in come from torch.  Loaded the other way
+    round, the library would pull the system runtime under its soname and
+    torch would still load its own under the file name its libraries need:
+    two runtimes in one process, the library's seeing no device."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m layer_wise_top_amd.build`")
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime)
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, u32, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                              ctypes.c_void_p, ctypes.c_size_t)
