@@ -62,6 +62,7 @@ extern "C" {
 #define LAGS_EDEVICE (-5)    /* current device differs from the workspace's device */
 #define LAGS_ENOMEM (-6)     /* host allocation failed */
 #define LAGS_ENOTINIT (-7)   /* workspace not initialised for this layout (lags_workspace_init) */
+#define LAGS_ESTATIC (-8)    /* layout too large for lags_sparsify_layers_static's buffer */
 
 /* Limits. */
 #define LAGS_MAX_LAYERS 65536
@@ -181,6 +182,30 @@ int lags_workspace_init(const lags_layout *layout, void *ws, size_t ws_bytes, in
 int lags_sparsify_layers(const lags_layout *layout, const float *grad,
                          float *residual, uint32_t *msg_idx, float *msg_val,
                          void *ws, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * lags_sparsify_layers without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Its scratch is a static device buffer
+ * of the library, LAGS_STATIC_SCRATCH_BYTES per device, which each device
+ * holds from the library's first use on it until the process ends; the call
+ * allocates and frees nothing.  The buffer also holds the tables of the
+ * layout last used on the device: a call with another layout first copies
+ * that layout's tables in (hipMemcpyAsync on `stream` from the layout's host
+ * image, so the layout must outlive the call, as always).  The scratch part
+ * is never read before being written in a call, so results do not depend on
+ * what an earlier call left.  Every call on one device shares its buffer:
+ * calls that may overlap in time on one device (other streams, other host
+ * threads without ordering) race and give wrong results.
+ *   grad, residual, msg_idx, msg_val, flags, stream: as lags_sparsify_layers.
+ * Returns LAGS_OK, LAGS_EINVAL, LAGS_ESTATIC (the layout's tables and scratch,
+ * lags_workspace_bytes(layout, 1) less the aggregate part, exceed the buffer),
+ * LAGS_EHIP.
+ */
+#define LAGS_STATIC_SCRATCH_BYTES (64u << 20)
+int lags_sparsify_layers_static(const lags_layout *layout, const float *grad, float *residual,
+                                uint32_t *msg_idx, float *msg_val, uint32_t flags,
+                                void *stream);
 
 /*
  * Aggregate P workers' messages and apply the SGD step (abstract: synchronous

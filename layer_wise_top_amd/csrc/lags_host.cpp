@@ -5,6 +5,7 @@
 #include "lags_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -13,6 +14,8 @@
 #include <vector>
 
 using namespace lags;
+
+static_assert(kStaticScratchBytes == LAGS_STATIC_SCRATCH_BYTES, "one size for the static scratch");
 
 namespace {
 
@@ -46,6 +49,7 @@ struct TraceRec {
 }  // namespace
 
 struct lags_layout {
+    uint64_t id = 0;               // unique per created layout
     int32_t L = 0;
     uint64_t n = 0, K = 0;
     std::vector<uint32_t> off, k, moff;
@@ -564,6 +568,7 @@ const char *lags_strerror(int status)
     case LAGS_EDEVICE: return "current device differs from the workspace's device";
     case LAGS_ENOMEM: return "out of memory";
     case LAGS_ENOTINIT: return "workspace not initialised for this layout (lags_workspace_init)";
+    case LAGS_ESTATIC: return "layout needs more scratch than the static buffer of lags_sparsify_layers_static (64 MiB) holds";
     default: return "unknown status";
     }
 }
@@ -592,6 +597,8 @@ int lags_layout_create(int32_t L, const int64_t *layer_off, const int64_t *k, la
     if (layer_off[L] >= (int64_t)0xffffffffLL || K >= 0xffffffffull) return LAGS_ERANGE;
     lags_layout *lo = new (std::nothrow) lags_layout();
     if (!lo) return LAGS_ENOMEM;
+    static std::atomic<uint64_t> next_id{1};
+    lo->id = next_id.fetch_add(1);
     lo->L = L;
     lo->n = (uint64_t)layer_off[L];
     lo->K = K;
@@ -723,6 +730,45 @@ int lags_sparsify_layers(const lags_layout *lo, const float *grad, float *residu
     if (!lo) return LAGS_EINVAL;
     return lags_sparsify_range(lo, 0, lo->L, grad, residual, msg_idx, msg_val, ws, ws_bytes, flags,
                                stream);
+}
+
+int lags_sparsify_layers_static(const lags_layout *clo, const float *grad, float *residual,
+                                uint32_t *msg_idx, float *msg_val, uint32_t flags, void *stream)
+{
+    lags_layout *lo = const_cast<lags_layout *>(clo);
+    if (!lo || !grad || !residual || !msg_idx || !msg_val) return LAGS_EINVAL;
+    if (flags & ~LAGS_SPARSIFY_EXACT) return LAGS_EINVAL;
+    if (!aligned16(grad) || !aligned16(residual) || !aligned16(msg_idx) || !aligned16(msg_val))
+        return LAGS_EINVAL;
+    const size_t nb = lo->n * 4, kb = lo->K * 4;
+    const void *bufs[4] = {grad, residual, msg_idx, msg_val};
+    const size_t lens[4] = {nb, nb, kb, kb};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(bufs[i], lens[i], bufs[j], lens[j])) return LAGS_EINVAL;
+    // tables and scratch of the sparsify call (no aggregate part)
+    if (lo->ws_agg > kStaticScratchBytes) return LAGS_ESTATIC;
+    void *ws = nullptr;
+    if (static_scratch(&ws) != hipSuccess) return LAGS_EHIP;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LAGS_EHIP;
+    hipStream_t s = (hipStream_t)stream;
+    {
+        // the tables of the layout last used on this device stay in the
+        // buffer; another layout's are copied in first (from the layout's
+        // host image, which outlives the copy as the layout outlives the call)
+        static std::mutex mu;
+        static std::map<int, uint64_t> loaded;     // device -> layout id
+        std::lock_guard<std::mutex> g(mu);
+        auto it = loaded.find(dev);
+        if (it == loaded.end() || it->second != lo->id) {
+            if (hipMemcpyAsync(ws, lo->tables.data(), lo->tables.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+                return LAGS_EHIP;
+            loaded[dev] = lo->id;
+        }
+    }
+    std::lock_guard<std::mutex> g(lo->mu);
+    return sparsify_launch(lo, 0, lo->L, grad, residual, msg_idx, msg_val, (unsigned char *)ws, flags, s);
 }
 
 int lags_aggregate_range(const lags_layout *clo, int32_t l0, int32_t l1, float *weights,

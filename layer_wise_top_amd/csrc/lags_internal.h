@@ -231,6 +231,11 @@ enum : int32_t {
     kKXCount = 11, kKXCut = 12, kNumKernels = 13
 };
 
+// the allocation-free sparsify's static scratch (lags_kernels.hip): its size,
+// and this device's address of it (looked up once per device)
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void **out);
+
 // launchers (lags_kernels.hip)
 hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);

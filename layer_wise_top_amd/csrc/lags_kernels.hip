@@ -55,6 +55,8 @@
 // subtraction of the update are separate roundings.
 #include "lags_internal.h"
 
+#include <mutex>
+
 namespace lags {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -2202,6 +2204,36 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     }
     bad = wave_sum(bad);
     if (lane_id() == 0 && bad) atomicAdd(&a.report[kRepBad], bad);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free sparsify (lags_sparsify_layers_static):
+// a file-scope device array that each device holds from the library's first
+// use on it until the process ends.  Host code never passes the array's name
+// to a kernel: it looks up this device's address of it once, with the device
+// current, and uses that address only.
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblags.so")
 
 LAGS_OK = 0
 LAGS_ENOTINIT = -7
+LAGS_ESTATIC = -8
 LAGS_SPARSIFY_EXACT = 1
 LAGS_MAX_LAYERS = 65536
 LAGS_MAX_WORKERS = 1024
@@ -29,7 +30,7 @@ EXPORTED = (
     "lags_aggregate_apply", "lags_workspace_report", "lags_trace_enable",
     "lags_trace_read", "lags_num_kernels", "lags_kernel_name", "lags_sparsify_range",
     "lags_aggregate_range", "lags_merge_schedule", "lags_schedule_finish", "lags_adaptive_k",
-    "lags_workspace_init",
+    "lags_workspace_init", "lags_sparsify_layers_static",
 )
 
 
@@ -89,6 +90,8 @@ def lib():
     L.lags_sparsify_layers.argtypes = [vp, vp, vp, vp, vp, vp, sz, u32, vp]
     L.lags_aggregate_apply.restype = ctypes.c_int
     L.lags_aggregate_apply.argtypes = [vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
+    L.lags_sparsify_layers_static.restype = ctypes.c_int
+    L.lags_sparsify_layers_static.argtypes = [vp, vp, vp, vp, vp, u32, vp]
     L.lags_sparsify_range.restype = ctypes.c_int
     L.lags_sparsify_range.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, sz, u32, vp]
     L.lags_aggregate_range.restype = ctypes.c_int
@@ -233,6 +236,19 @@ def lags_sparsify_layers(layout: Layout, grad, residual, msg_idx, msg_val, ws,
     rc = lib().lags_sparsify_layers(layout.handle, g, r, mi, mv, w, ws.numel(), int(flags),
                                     _stream_handle(stream))
     _check("lags_sparsify_layers", rc)
+
+
+def lags_sparsify_layers_static(layout: Layout, grad, residual, msg_idx, msg_val, flags: int = 0,
+                                stream=None):
+    """lags_sparsify_layers on the library's static scratch (no workspace)."""
+    import torch
+    g = _dev_tensor(grad, torch.float32, layout.n, "grad")
+    r = _dev_tensor(residual, torch.float32, layout.n, "residual")
+    mi = _dev_tensor(msg_idx, torch.int32, layout.K, "msg_idx")
+    mv = _dev_tensor(msg_val, torch.float32, layout.K, "msg_val")
+    rc = lib().lags_sparsify_layers_static(layout.handle, g, r, mi, mv, int(flags),
+                                           _stream_handle(stream))
+    _check("lags_sparsify_layers_static", rc)
 
 
 def lags_aggregate_apply(layout: Layout, weights, msg_idx, msg_val, P: int, lr: float, ws,

@@ -192,3 +192,18 @@ def test_no_device_allocation_in_the_library():
         text = open(p).read()
         for name in ("hipMalloc", "hipFree", "hipExtMalloc", "hipHostMalloc"):
             assert name not in text, (p, name)
+
+
+def test_static_sparsify_size_limit_without_a_device():
+    """lags_sparsify_layers_static refuses a layout whose tables and scratch
+    exceed its static buffer before any HIP call."""
+    from layer_wise_top_amd import workloads as W
+    wl = W.get("tfm1p3b")
+    off = wl.offsets()
+    num, den = wl.ratios()
+    lay = lags.Layout(off, lags.k_table(off, num, den))
+    base = 1 << 40                              # never dereferenced
+    rc = lags.lib().lags_sparsify_layers_static(lay.handle, base, base + (8 << 30), base + (16 << 30),
+                                                base + (17 << 30), 0, None)
+    assert rc == lags.LAGS_ESTATIC
+    assert lags.lib().lags_sparsify_layers_static(None, base, base, base, base, 0, None) == -1
