@@ -12,6 +12,11 @@ P = 16), the largest layout that fits one GPU.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME|all]
                   [--no-cpu-baseline] [--flush] [--pipeline] [--no-exact-mode]
+                  [--no-per-config]
+
+The line also carries "per_config": the pages' other workloads (ResNet-20,
+VGG-16, ResNet-50, LSTM), each timed the same way in the same run (at least
+20 steps), with their step time, rate, HBM fraction and kernel times.
 
 --pipeline adds a second measurement of the same step issued layer range by
 layer range (lags_sparsify_range / lags_aggregate_range, last layers first),
@@ -282,7 +287,11 @@ def exact_mode(lay, g_d, r_d, msg_idx0, msg_val0, ws, stream, reps):
             "same_as_sampled": same, "layers_exact": rep["layers_exact"]}
 
 
-def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True):
+def measure(name, steps, warmup, flush=False):
+    """Inputs of one workload resident in HBM, W warm-up steps, then exactly K
+    timed steps between two synchronisations (events on the launch stream),
+    and K more steps with the library's per-kernel tracer.  Returns the state
+    for further measurements and the metrics."""
     import torch
     from layer_wise_top_amd import lags, workloads as W
 
@@ -365,17 +374,47 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True):
     kernels = {kname: round(ms / max(cnt, 1), 5) for kname, (ms, cnt) in trace.items() if cnt}
     main_ms = kernels[DOMINANT]
     b_main = main_kernel_bytes(wl, k)
-    achieved = b_main / (main_ms * 1e-3) / 1e9
     B = algorithmic_bytes(wl.n, lay.K, P, U)
-    gelem = wl.n / (ms_per_step * 1e-3) / 1e9
+    m = {
+        "ms_per_step": round(ms_per_step, 5),
+        "value": round(wl.n / (ms_per_step * 1e-3) / 1e9, 3),
+        "hbm_frac_step": round(B / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "alg_bytes_step": B,
+        "step_ms_min": round(min(times), 5),
+        "step_ms_median": round(float(np.median(times)), 5),
+        "k_main_ms": main_ms,
+        "k_main_frac": round(b_main / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "k_main_alg_bytes": b_main,
+        "kernels_avg_ms": kernels,
+        "sparsify_ms": round(sum(v for kk, v in kernels.items() if not kk.startswith("k_agg")), 5),
+        "aggregate_ms": round(sum(v for kk, v in kernels.items() if kk.startswith("k_agg")), 5),
+        "report": rep,
+    }
+    state = dict(wl=wl, k=k, lay=lay, g_d=g_d, r_d=r_d, w_d=w_d, mi=mi, mv=mv, ws=ws, P=P,
+                 stream=stream, scratch=scratch, U=U, dev=dev)
+    return state, m
+
+
+def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True, per_config=()):
+    import torch
+    from layer_wise_top_amd import lags, workloads as W
+
+    st, m = measure(name, steps, warmup, flush)
+    wl, k, lay, P, U = st["wl"], st["k"], st["lay"], st["P"], st["U"]
+    g_d, r_d, w_d, mi, mv, ws = st["g_d"], st["r_d"], st["w_d"], st["mi"], st["mv"], st["ws"]
+    stream, scratch, dev = st["stream"], st["scratch"], st["dev"]
+    off = wl.offsets()
+    main_ms = m["k_main_ms"]
+    b_main = m["k_main_alg_bytes"]
+    achieved = b_main / (main_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
-        "value": round(gelem, 3),
+        "value": m["value"],
         "unit": "Gelem/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -386,22 +425,21 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True):
             "workers": P, "touched": U, "rho": "adaptive" if wl.rho_rule == "adaptive"
             else f"{wl.rho_uniform[0]}/{wl.rho_uniform[1]}", "flush_infinity_cache": bool(flush),
         },
-        "hbm_frac_step": round(B / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "alg_bytes_step": B,
+        "hbm_frac_step": m["hbm_frac_step"],
+        "alg_bytes_step": m["alg_bytes_step"],
         "roofline": {
             "kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": counters_traffic(wl.name), "alg_bytes_per_launch": b_main,
             "avg_ms": main_ms,
         },
-        "kernels_avg_ms": kernels,
-        "sparsify_ms": round(sum(v for kk, v in kernels.items() if not kk.startswith("k_agg")), 5),
-        "aggregate_ms": round(sum(v for kk, v in kernels.items() if kk.startswith("k_agg")), 5),
-        "report": rep,
+        "kernels_avg_ms": m["kernels_avg_ms"],
+        "sparsify_ms": m["sparsify_ms"],
+        "aggregate_ms": m["aggregate_ms"],
+        "report": m["report"],
+        "step_ms_min": m["step_ms_min"],
+        "step_ms_median": m["step_ms_median"],
     }
-    if times:
-        out["step_ms_min"] = round(min(times), 5)
-        out["step_ms_median"] = round(float(np.median(times)), 5)
     if exact:
         out["exact_mode"] = exact_mode(lay, g_d, r_d, mi[0], mv[0], ws, stream, 5)
     if pipeline:
@@ -466,9 +504,20 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True):
             "adaptive_k": {"sent_per_worker": int(k_ad.sum()), "runs": len(runs_ad),
                            "ms_per_step": round(ms_ad, 5)},
         }
-    del g_d, w_d, r_d, mi, mv, ws, scratch
+    del g_d, w_d, r_d, mi, mv, ws, scratch, st
     torch.cuda.empty_cache()
     out["torch_add_gbs"] = torch_add_gbs(wl.n)
+    if per_config:
+        # the other workloads, timed the same way in the same run (the
+        # headline fields above are the largest one's)
+        out["per_config"] = {}
+        for other in per_config:
+            if other == name:
+                continue
+            st2, m2 = measure(other, max(steps, 20), warmup, flush)
+            del st2
+            torch.cuda.empty_cache()
+            out["per_config"][other] = m2
     if do_cpu:
         log("timing the oracle on a bounded sample")
         out["cpu_baseline"], threaded = cpu_baseline(wl, k)
@@ -493,6 +542,9 @@ def main():
                     help="also time the step issued per merged-message layer range")
     ap.add_argument("--no-exact-mode", action="store_true",
                     help="leave out the exact-mode sparsify measured after the timed steps")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the chosen workload (by default the line also carries "
+                         "per_config: every other workload of the pages, timed the same way)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -518,9 +570,10 @@ def main():
         if nm not in W.WORKLOADS:
             print(f"unknown workload {nm}; choose from {', '.join(W.WORKLOADS)} or all", file=sys.stderr)
             sys.exit(2)
+    per_config = () if (args.no_per_config or args.config == "all") else tuple(W.ORDER)
     for name in names:
         out = run_config(name, args.steps, args.warmup, not args.no_cpu_baseline, args.flush,
-                         args.pipeline, not args.no_exact_mode)
+                         args.pipeline, not args.no_exact_mode, per_config)
         print(json.dumps(out), flush=True)
 
 

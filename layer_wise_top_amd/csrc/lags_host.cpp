@@ -478,7 +478,7 @@ int sparsify_launch(lags_layout *lo, int32_t l0, int32_t l1, const float *grad, 
     const uint32_t ns = a.nsampled;
     const uint32_t nmain = lo->stream_pre[l1] - lo->stream_pre[l0];
     const uint32_t nfin = lo->fin_pre[l1] - lo->fin_pre[l0];
-    // the fallback's workgroups: about one per 8 segments of the range's
+    // the fallback's workgroups: about one per 4 segments of the range's
     // sampled layers, at least the finishing workgroups, at most kFixGroups
     // (k_fin_emit is launched with max(nfin, fix_groups) workgroups)
     const uint32_t sid0 = lo->sid_pre[l0], sid1 = lo->sid_pre[l1];
@@ -486,7 +486,7 @@ int sparsify_launch(lags_layout *lo, int32_t l0, int32_t l1, const float *grad, 
         ns ? (sid1 < lo->sinfo.size() ? lo->sinfo[sid1].seg_base : lo->nseg_total) - lo->sinfo[sid0].seg_base
            : 0u;
     a.nfin = nfin;
-    a.fix_groups = std::min(kFixGroups, std::max(nfin, (nseg_range + 7u) / 8u));
+    a.fix_groups = std::min(kFixGroups, std::max(nfin, (nseg_range + 3u) / 4u));
     int rc;
     // k_sample always runs: its first workgroup restarts the report counters
     rc = traced(lo, kKSample, s, [&] { return launch_sample(a, std::max<uint32_t>(1, ns), s); });

@@ -45,10 +45,15 @@ constexpr uint32_t kAggMaxWidthLog2 = 30;     // chunk width cap (entries)
 // guess-failure fallback (inside k_fin_emit): the first kFixGroups workgroups
 // of the launch select every failed layer together, by a radix select over all
 // of its keys, meeting at barriers between the passes
-constexpr uint32_t kFixGroups = 512;
+constexpr uint32_t kFixGroups = 1024;
 // per sampled layer: histograms of the three key digits (11, 11 and 9 bits),
-// then per fallback workgroup its count of keys above and equal to the threshold
-constexpr uint32_t kFbHist0 = 0, kFbHist1 = 2048, kFbHist2 = 4096, kFbCount = 4608;
+// the count of keys above the range the threshold is known to lie in, the
+// barrier's top counter and its kFixSubs sub-counters (one 128-byte line
+// each), then per fallback workgroup its count of keys above and equal to the
+// threshold.  Everything before kFbCount starts at zero.
+constexpr uint32_t kFixSubs = 32;
+constexpr uint32_t kFbHist0 = 0, kFbHist1 = 2048, kFbHist2 = 4096, kFbAbove = 4608, kFbBarTop = 4640,
+                   kFbBarSub = 4672, kFbCount = kFbBarSub + 32 * kFixSubs;
 constexpr uint32_t kFbWords = kFbCount + 2 * kFixGroups;
 
 // ---- layer classes --------------------------------------------------------
@@ -147,10 +152,11 @@ struct SampledState {     // per sampled layer, per call, in the workspace
     uint32_t xrank;       // exact mode: rank still to find among keys with that prefix
     uint32_t T;           // k-th largest key of the layer
     uint32_t idx_cut;     // largest global index taken among keys == T
-    uint32_t fix_bar;     // fallback: arrivals at the barriers between its passes
+    uint32_t spare1;
     uint32_t nfail;       // (first sampled layer of a launched range only) layers of the
                           // range that need the fallback
-    uint32_t pad0[20];
+    uint32_t fix_klo, fix_khi;   // fallback: T is known to lie in [fix_klo, fix_khi]
+    uint32_t pad0[18];
     // on a cache line of its own: every finishing workgroup of the layer
     // reads the fields above while the select pass adds to this one
     uint32_t tbin_n;      // entries of bin bstar collected

@@ -360,6 +360,25 @@ __device__ void exact_layer(const Src &src, uint32_t n, uint32_t k, uint32_t off
     exact_emit<WRITE_ALL>(src, n, k, off, moff, T, e, res_layer, msg_idx, msg_val, tmp);
 }
 
+// A thread's run of equal bins, added to an LDS histogram with one atomic per
+// run: many equal keys would otherwise serialise on one LDS address.
+struct LdsRun {
+    uint32_t bin = 0, n = 0;
+    __device__ void add(uint32_t *hist, uint32_t b)
+    {
+        if (b != bin) {
+            flush(hist);
+            bin = b;
+        }
+        ++n;
+    }
+    __device__ void flush(uint32_t *hist)
+    {
+        if (n) atomicAdd(&hist[bin], n);
+        n = 0;
+    }
+};
+
 // ---------------------------------------------------------------------------
 // k_sample: one 1024-thread workgroup per sampled layer.  The whole sample is
 // requested at once (4 float4 of grad and residual per thread), its keys go
@@ -398,6 +417,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
         return;
     }
     uint32_t cnt, rank, m = 0;
+    LdsRun run;
     if (S.full_sample) {
         cnt = L.n;
         rank = L.k;
@@ -417,7 +437,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
                 const uint32_t key = key_of(gv[u] + rv[u]);
                 keys[i] = key;
                 m = max(m, key);
-                atomicAdd(&hist[key >> 19], 1u);
+                run.add(hist, key >> 19);
             }
         }
     } else {
@@ -447,10 +467,11 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
                 const uint32_t key = key_of(acc[j]);
                 keys[qi * 4 + j] = key;
                 m = max(m, key);
-                atomicAdd(&hist[key >> 19], 1u);
+                run.add(hist, key >> 19);
             }
         }
     }
+    run.flush(hist);
     __syncthreads();
     const uint32_t M = block_max<NT>(m, tmp);
     if (rank >= cnt) {
@@ -472,8 +493,9 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     __syncthreads();
     for (uint32_t e = threadIdx.x; e < cnt; e += NT) {
         const uint32_t key = keys[e];
-        if ((key >> 19) == b1) atomicAdd(&hist[(key >> 7) & (kSampleBins - 1)], 1u);
+        if ((key >> 19) == b1) run.add(hist, (key >> 7) & (kSampleBins - 1));
     }
+    run.flush(hist);
     __syncthreads();
     block_find_rank<NT>(hist, kSampleBins, rank2, res, tmp);
     if (threadIdx.x == 0) {
@@ -585,25 +607,11 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
     return min((key - G) >> SH, kNBins - 1u);
 }
 
-// Add the active lanes' bins to a device histogram with one atomic per
-// distinct bin of the wave.  All lanes of the wave call.
-__device__ __forceinline__ void wave_bin_add(uint32_t *hist, uint32_t bin, bool active)
-{
-    uint64_t todo = __ballot(active);
-    while (todo) {
-        const uint32_t leader = (uint32_t)__ffsll((unsigned long long)todo) - 1u;
-        const uint32_t b = __shfl(bin, leader, 64);
-        const uint64_t same = __ballot(active && bin == b);
-        if (lane_id() == leader) atomicAdd(&hist[b], (uint32_t)__popcll(same));
-        todo &= ~same;
-    }
-}
-
-constexpr uint32_t kHeavySeg = 256;   // candidates of a segment counted per wave beyond this
+constexpr uint32_t kHeavySeg = 256;   // candidates of a segment counted in LDS beyond this
 
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
                                 const SampledState *st, uint32_t *hist, uint2 *stage,
-                                uint32_t (*wtot)[kWaves])
+                                uint32_t (*wtot)[kWaves], uint32_t *lh)
 {
     const uint32_t t = threadIdx.x;
     const SegView sv = seg_view(w, seg);
@@ -640,15 +648,31 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
     const uint32_t cap = w.cap;
     const uint64_t slot0 = (((uint64_t)w.slot_hi << 32) | w.slot_lo) + (uint64_t)seg * cap;
     // a segment with many candidates (equal keys, clustered large values)
-    // counts them with one atomic per distinct bin of each wave instead of one
-    // per candidate: thousands of device atomics on one address serialise
+    // counts them in the workgroup's LDS histogram lh and adds its nonzero
+    // bins to the layer's copy once: thousands of device atomics on one
+    // address serialise
     const bool heavy = total > kHeavySeg;   // uniform over the workgroup
+    if (heavy) {
+        for (uint32_t b = t; b < kNBins; b += kBlock) lh[b] = 0;
+        __syncthreads();
+    }
+    uint32_t run_b = 0, run_n = 0;      // heavy: a run of one bin among the thread's candidates
     auto put = [&](uint32_t p, uint32_t idx, float v) {
         const uint2 e = make_uint2(idx, __float_as_uint(v));
         if (p < kCapMax) stage[p] = e;
         else if (p < cap) a.slots[slot0 + p] = e;   // only layers of <= kSampleMax entries
                                                      // have more than kCapMax slots
-        if (!heavy) atomicAdd(&hist[cand_bin(key_of(v), G, SH)], 1u);
+        const uint32_t bin = cand_bin(key_of(v), G, SH);
+        if (heavy) {
+            if (bin != run_b) {
+                if (run_n) atomicAdd(&lh[run_b], run_n);
+                run_b = bin;
+                run_n = 0;
+            }
+            ++run_n;
+        } else {
+            atomicAdd(&hist[bin], 1u);
+        }
     };
     if (c[0]) put(pos[0], sv.hlo + t, hv);
 #pragma unroll
@@ -659,21 +683,16 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
             if ((fl >> (4 * u + j)) & 1u) put(p++, 4u * sv.row(u) + j, acc[u][j]);
     }
     if (c[kParts - 1]) put(pos[kParts - 1], sv.tlo + t, tv);
-    if (heavy) {
-        wave_bin_add(hist, cand_bin(key_of(hv), G, SH), c[0] != 0u);
-#pragma unroll
-        for (int u = 0; u < kRows; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wave_bin_add(hist, cand_bin(key_of(acc[u][j]), G, SH), ((fl >> (4 * u + j)) & 1u) != 0u);
-        wave_bin_add(hist, cand_bin(key_of(tv), G, SH), c[kParts - 1] != 0u);
-    }
+    if (heavy && run_n) atomicAdd(&lh[run_b], run_n);
     __syncthreads();
     // a segment with more candidates than slots keeps only the first cap
     // (the finishing kernels re-read it)
     const uint32_t ns = min(total, min(cap, kCapMax));
     for (uint32_t i = t; i < ns; i += kBlock) a.slots[slot0 + i] = stage[i];
     if (t == 0) a.seg_count[w.seg_base + seg] = total;
+    if (heavy)
+        for (uint32_t b = t; b < kNBins; b += kBlock)
+            if (lh[b]) atomicAdd(&hist[b], lh[b]);
 }
 
 __device__ void dense_tile(const SparsifyArgs &a, const MainWork &w, uint32_t part, uint32_t nparts);
@@ -684,6 +703,7 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 {
     __shared__ uint2 stage[kCapMax];
     __shared__ uint32_t wtot[kParts][kWaves];
+    extern __shared__ uint32_t lh[];     // the launch's LDS pad: kNBins words at least
 
     const uint32_t part = blockIdx.x % kTileSegs;
     const MainWork w = a.main_work[a.main_base + blockIdx.x / kTileSegs];
@@ -693,7 +713,7 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
         // consecutive workgroups take consecutive histogram copies
         if (seg < w.nseg)
             sampled_segment(a, w, seg, a.state + w.sid,
-                            a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins, stage, wtot);
+                            a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins, stage, wtot, lh);
         return;
     }
 
@@ -759,12 +779,17 @@ __device__ __forceinline__ uint32_t seg_len(const FinWork &f, uint32_t s)
 // Hand a sampled layer whose guess failed to the fallback of k_fin_emit:
 // status kStFix, one more failed layer in the range's count, the layer's
 // fallback histograms cleared.  All NT threads of the workgroup call.
+// [klo, khi]: the keys the layer's threshold is known to lie between (the
+// whole range when nothing is known).
 template <int NT>
-__device__ void mark_for_fix(const SparsifyArgs &a, uint32_t sid)
+__device__ void mark_for_fix(const SparsifyArgs &a, uint32_t sid, uint32_t klo = 0u,
+                             uint32_t khi = 0x7fffffffu)
 {
     uint32_t *fb = a.fb + (uint64_t)sid * kFbWords;
     for (uint32_t t = threadIdx.x; t < kFbCount; t += NT) fb[t] = 0;
     if (threadIdx.x == 0) {
+        a.state[sid].fix_klo = klo;
+        a.state[sid].fix_khi = khi;
         a.state[sid].status = kStFix;
         atomicAdd(&a.state[a.sample_base].nfail, 1u);
         atomicAdd(&a.report[kRepExact], 1u);
@@ -824,8 +849,14 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     block_find_rank<NT>(hist, kNBins, L.k, res, tmp);
     if (hist[res[0]] > S.tbin_cap) {
         // the threshold bin holds more candidates than the layer's list (many
-        // equal keys): the fallback selects the layer
-        mark_for_fix<NT>(a, sid);
+        // equal keys): the fallback selects the layer, knowing that the
+        // threshold lies in this bin
+        const uint32_t G = st->G, SH = st->SH, b = res[0];
+        const uint64_t blo = (uint64_t)G + ((uint64_t)b << SH);
+        const uint32_t klo = (uint32_t)min(blo, (uint64_t)0x7fffffffu);
+        const uint32_t khi = (b + 1u >= kNBins) ? 0x7fffffffu
+                                                : (uint32_t)min(blo + (1ull << SH) - 1u, (uint64_t)0x7fffffffu);
+        mark_for_fix<NT>(a, sid, klo, khi);
         if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
         return;
     }
@@ -1159,12 +1190,6 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     }
 
     if (status != kStOk) return;       // kStFix: the fallback takes the layer
-    if (h > S.tbin_cap) {
-        // more threshold-bin entries than the list holds (many equal keys in
-        // segments re-read from acc): the fallback selects the layer
-        mark_for_fix<kBlock>(a, sid);
-        return;
-    }
 
     // resolve the threshold inside bin bstar: in LDS when the bin fits,
     // otherwise straight from the workspace
@@ -1176,6 +1201,12 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     const uint32_t klo = (uint32_t)min(blo, (uint64_t)0x7fffffffu);
     const uint32_t khi = (bstar + 1u >= kNBins) ? 0x7fffffffu
                                                 : (uint32_t)min(blo + (1ull << st->SH) - 1u, (uint64_t)0x7fffffffu);
+    if (h > S.tbin_cap) {
+        // more threshold-bin entries than the list holds (k_fin_bins sees this
+        // from the histogram; kept as a guard): the fallback selects the layer
+        mark_for_fix<kBlock>(a, sid, klo, khi);
+        return;
+    }
     uint32_t T, idx_cut;
     if (h <= kTbinCap) {
         constexpr int EPT = kTbinCap / kBlock;     // the whole bin requested at once
@@ -1769,17 +1800,38 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
 // in time is counted in the report and passed (the layer's output is then
 // wrong; stores stay inside the layer and its message range).
 
-constexpr uint32_t kFixSpin = 1u << 22;   // sleeps of ~0.3 us: about a second
+constexpr uint32_t kFixSpin = 1u << 21;   // sleeps of ~0.5 us: about a second
 
-__device__ void fix_barrier(const SparsifyArgs &a, uint32_t *ctr, uint32_t target)
+// Barrier round `round` (1, 2, ...) of the F fallback workgroups.  Arrivals
+// are spread over kFixSubs counters, one cache line each: workgroup w uses
+// counter w % kFixSubs, so every workgroup on a counter runs on the same XCD
+// (workgroups go to the XCDs round robin, w % 8).  What crosses workgroups
+// goes through device-scope atomics and is read back with device-coherent
+// loads; the last arrival on a counter writes that XCD's L2 back (release)
+// before it bumps the top counter, on which every workgroup waits.  One
+// address thus takes at most F / kFixSubs + 1 atomics per round, and each
+// XCD does kFixSubs / 8 L2 write-backs per round instead of one per
+// workgroup, with no L2 invalidation while other workgroups stream.
+static_assert(kFixSubs % 8 == 0, "a counter's workgroups share one XCD");
+
+__device__ void fix_barrier(const SparsifyArgs &a, uint32_t *fb, uint32_t F, uint32_t round)
 {
     wait_mem_done();          // this thread's atomics into the layer's histogram are done
     __syncthreads();
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t sub = blockIdx.x % kFixSubs;
+        const uint32_t nsub = (F - sub + kFixSubs - 1u) / kFixSubs;   // workgroups on this counter
+        const uint32_t nact = min(F, kFixSubs);                        // counters in use
+        uint32_t *top = fb + kFbBarTop;
+        const uint32_t old = __hip_atomic_fetch_add(fb + kFbBarSub + 32u * sub, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (old == round * nsub - 1u) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         uint32_t it = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(8);
+        while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < round * nact) {
+            __builtin_amdgcn_s_sleep(20);
             if (++it >= kFixSpin) {
                 atomicAdd(&a.report[kRepFixTimeout], 1u);
                 break;
@@ -1795,7 +1847,6 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
     const SampledInfo S = a.sinfo[sid];
     const LayerInfo L = a.linfo[S.layer];
     uint32_t *fb = a.fb + (uint64_t)sid * kFbWords;
-    uint32_t *bar = &a.state[sid].fix_bar;
     MainWork mw{};                        // the fields seg_view reads
     mw.off = L.off;
     mw.end = L.off + L.n;
@@ -1805,26 +1856,46 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
     const uint32_t s_lo = (uint32_t)((uint64_t)S.nseg * wg / F);
     const uint32_t s_hi = (uint32_t)((uint64_t)S.nseg * (wg + 1u) / F);
 
-    uint32_t prefix = 0, rank = L.k, gt22 = 0;
+    // bits of T known before the passes: those above vb, shared by the ends
+    // of the range it lies in; digit levels made only of known bits are
+    // skipped.  The first pass also counts the keys above that range.
+    const SampledState &stl = a.state[sid];
+    const uint32_t klo = stl.fix_klo, khi = stl.fix_khi;
+    const uint32_t vb = varying_bits(klo, khi);
+    uint32_t prefix = vb >= 32u ? 0u : (klo >> vb) << vb;
+    uint32_t rank = L.k, gt22 = 0, nbar = 0;
     for (uint32_t level = 0; level < 3u; ++level) {
         const uint32_t sh = x_shift(level), nb = x_bins(level);
-        const uint32_t top = level == 0u ? 32u : x_shift(level - 1u);
+        if (sh >= vb) continue;           // every bit of this digit is known
+        const bool first = nbar == 0u;
+        const uint32_t ms = first ? vb : (level == 0u ? 32u : x_shift(level - 1u));  // match shift
+        uint32_t hi = 0;                  // (first pass) keys above the known range
         for (uint32_t b = t; b < 2048u; b += kBlock) x.hl[b] = 0;
         __syncthreads();
         for (uint32_t sg = s_lo; sg < s_hi; ++sg) {
             XSeg xs;
             xs.load(a, mw, sg);
+            LdsRun run;
             xs.each([&](uint32_t, float v) {
                 const uint32_t key = key_of(v);
-                if (top >= 32u || (key >> top) == (prefix >> top)) atomicAdd(&x.hl[(key >> sh) & (nb - 1u)], 1u);
+                if (ms >= 32u || (key >> ms) == (prefix >> ms)) run.add(x.hl, (key >> sh) & (nb - 1u));
+                if (first && ms < 32u && (key >> ms) > (prefix >> ms)) ++hi;
                 if (level == 2u && (key >> kXShift1) > (prefix >> kXShift1)) ++gt22;
             });
+            run.flush(x.hl);
         }
-        __syncthreads();
         uint32_t *gh = fb + (level == 0u ? kFbHist0 : (level == 1u ? kFbHist1 : kFbHist2));
+        if (first) {
+            uint32_t tot;
+            block_excl_scan(hi, x.tmp, tot);     // its barriers also end the LDS histogram
+            if (t == 0 && tot) atomicAdd(&fb[kFbAbove], tot);
+        } else {
+            __syncthreads();
+        }
         for (uint32_t b = t; b < nb; b += kBlock)
             if (x.hl[b]) atomicAdd(&gh[b], x.hl[b]);
-        fix_barrier(a, bar, F * (level + 1u));
+        fix_barrier(a, fb, F, ++nbar);
+        if (first) rank = L.k - ld_coherent(&fb[kFbAbove]);
         for (uint32_t b = t; b < nb; b += kBlock) x.hp[b] = ld_coherent(&gh[b]);
         __syncthreads();
         block_find_rank(x.hp, nb, rank, x.res, x.tmp);
@@ -1844,7 +1915,7 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
         __hip_atomic_store(&fb[kFbCount + wg], wgt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&fb[kFbCount + F + wg], x.hl[d2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    fix_barrier(a, bar, F * 4u);
+    fix_barrier(a, fb, F, ++nbar);
 
     // ties and sent entries of the workgroups before this one
     uint32_t ceq = 0, csel = 0;
@@ -2269,8 +2340,10 @@ hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
 {
     const uint32_t ngroups = nblocks * kTileSegs;
-    hipLaunchKernelGGL(k_main, dim3(ngroups), dim3(kBlock),
-                       stream_lds_pad(ngroups, (kCapMax * 2 + kParts * kWaves) * 4), s, a);
+    // the pad doubles as a heavy segment's LDS histogram
+    const size_t pad = std::max<size_t>(stream_lds_pad(ngroups, (kCapMax * 2 + kParts * kWaves) * 4),
+                                        kNBins * sizeof(uint32_t));
+    hipLaunchKernelGGL(k_main, dim3(ngroups), dim3(kBlock), pad, s, a);
     return hipGetLastError();
 }
 

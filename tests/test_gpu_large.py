@@ -128,6 +128,15 @@ def test_tfm1p3b_full_size(oracle):
         w_o = oracle.aggregate(ai, av, w0[a:b], wl.lr, lo=a, hi=b)
         assert_bits_equal(f"layer {l} weights", w_h[a:b], w_o)
 
+    # ---- the aggregate of every layer against the oracle: worker 0's
+    # message is the GPU's own, which the invariants above pin on every layer
+    # (the selected set is unique and its values are acc's bits)
+    _say("oracle aggregate over all layers")
+    ai = np.concatenate([mi_h[None], oi], 0)
+    av = np.concatenate([mv_h[None], ov], 0)
+    w_o = oracle.aggregate(ai, av, w0, wl.lr)
+    assert_bits_equal("weights of all layers", w_h, w_o)
+
 
 @pytest.mark.timeout(1200)
 def test_slgs1p3b_full_size(oracle):
@@ -137,8 +146,8 @@ def test_slgs1p3b_full_size(oracle):
     partition (the k-th largest key, then the lowest-index ties): the GPU must
     send exactly that set, with the residual and value bits it implies, and
     its weights must match the oracle's aggregate on three windows of one
-    million indices (worker 0's entries there taken from the host
-    selection)."""
+    million indices and over every index (worker 0's message taken from the
+    host selection)."""
     import torch
     wl = W.get("slgs1p3b")
     off = wl.offsets()
@@ -200,3 +209,6 @@ def test_slgs1p3b_full_size(oracle):
         wi = np.where((ai >= a) & (ai < b), ai, np.uint32(0xFFFFFFFF))
         w_o = oracle.aggregate(wi, av, w0[a:b], wl.lr, lo=a, hi=b)
         assert_bits_equal(f"weights [{a}, {b})", to_np_f32(w_d[a:b]), w_o)
+    _say("oracle aggregate over every index")
+    w_o = oracle.aggregate(ai, av, w0, wl.lr)
+    assert_bits_equal("weights of every index", to_np_f32(w_d), w_o)
