@@ -29,8 +29,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct AggPlan {
     uint32_t NC = 0;
     std::vector<uint32_t> h_cbase;    // [L+1]
-    size_t b_cbase = 0, b_csh = 0, b_info = 0;   // byte offsets inside the image
-    std::vector<unsigned char> image; // cbase[L+1], csh[L], chunk_info[NC]
+    size_t b_cbase = 0, b_csh = 0, b_info = 0, b_desc = 0;   // byte offsets inside the image
+    std::vector<unsigned char> image; // cbase[L+1], csh[L], chunk_info[NC], sdesc[npb][2]
 };
 
 // A workspace that lags_workspace_init prepared for this layout.
@@ -65,6 +65,7 @@ struct lags_layout {
     // small-layer work entries, streaming work entries, sampled layers and
     // finishing workgroups before layer l
     std::vector<uint32_t> small_pre, stream_pre, sid_pre, fin_pre;
+    std::vector<uint32_t> bins_pre;   // sampled layers that need k_fin_bins (many histogram copies)
     uint32_t nseg_total = 0;
     uint64_t slots_total = 0;
     uint64_t hist_words = 0;
@@ -136,6 +137,8 @@ int build_plan(lags_layout *lo)
     lo->stream_pre.assign(L + 1, 0);
     lo->sid_pre.assign(L + 1, 0);
     lo->fin_pre.assign(L + 1, 0);
+    lo->bins_pre.assign(L + 1, 0);
+    uint32_t nbig = 0;
     auto work = [](uint32_t l, uint32_t cls, uint32_t tile) {
         MainWork w{};
         w.layer = l;
@@ -148,6 +151,7 @@ int build_plan(lags_layout *lo)
         lo->stream_pre[l] = (uint32_t)stream_work.size();
         lo->sid_pre[l] = (uint32_t)lo->sinfo.size();
         lo->fin_pre[l] = (uint32_t)lo->fin_work.size();
+        lo->bins_pre[l] = nbig;
         LayerInfo &li = lo->linfo[l];
         li = LayerInfo{};
         li.off = lo->off[l];
@@ -203,6 +207,7 @@ int build_plan(lags_layout *lo)
             si.hcopies = 1;
             while (si.hcopies < kHistMaxCopies && si.hcopies * kTilesPerCopy < li.ntiles) si.hcopies *= 2;
             si.hist_off = (uint32_t)lo->hist_words;
+            if (si.hcopies > kSelfBinsCopies) ++nbig;
             lo->hist_words += (uint64_t)si.hcopies * kNBins;
             for (uint32_t t = 0; t < li.ntiles; ++t) {
                 MainWork w = work((uint32_t)l, kClsSampled, t);
@@ -237,6 +242,8 @@ int build_plan(lags_layout *lo)
                 f.k = li.k;
                 f.tbin_cap = si.tbin_cap;
                 f.a4 = si.a4;
+                f.hist_off = si.hist_off;
+                f.hcopies = si.hcopies;
                 lo->fin_work.push_back(f);
             }
             seg_base += si.nseg;
@@ -248,6 +255,7 @@ int build_plan(lags_layout *lo)
     lo->stream_pre[L] = (uint32_t)stream_work.size();
     lo->sid_pre[L] = (uint32_t)lo->sinfo.size();
     lo->fin_pre[L] = (uint32_t)lo->fin_work.size();
+    lo->bins_pre[L] = nbig;
     lo->main_work = stream_work;
     lo->nseg_total = seg_base;
     lo->slots_total = slot_base;
@@ -348,13 +356,32 @@ const AggPlan &agg_plan(lags_layout *lo, int32_t P)
                           (uint32_t)(lo->moff[l] + lo->k[l])};
         }
     }
+    // per position block of the start pass: the layers of its first
+    // position's predecessor and of its last position, and the first one's
+    // fields (a block inside one layer needs nothing else)
+    const size_t npb = lo->pos_layer.size();
+    std::vector<uint4> sd(2 * npb, uint4{0, 0, 0, 0});
+    auto layer_at = [&](uint64_t j) -> uint32_t {   // largest l with moff[l] <= j
+        return (uint32_t)(std::upper_bound(lo->moff.begin(), lo->moff.begin() + lo->L, (uint32_t)j) -
+                          lo->moff.begin()) - 1u;
+    };
+    for (size_t b = 0; b < npb; ++b) {
+        const uint64_t jfirst = b * kStartsBlock;
+        const uint64_t jlast = std::min<uint64_t>(jfirst + kStartsBlock, lo->K) - 1;
+        const uint32_t l0 = layer_at(jfirst ? jfirst - 1 : 0);
+        const uint32_t l1 = layer_at(std::max<uint64_t>(jlast, jfirst ? jfirst - 1 : 0));
+        sd[2 * b] = uint4{l0, l1, lo->off[l0], lo->off[l0 + 1] - lo->off[l0]};
+        sd[2 * b + 1] = uint4{cb[l0], cs[l0], 0, 0};
+    }
     t.b_cbase = 0;
     t.b_csh = align_up(cb.size() * 4, kAlign);
     t.b_info = t.b_csh + align_up(cs.size() * 4, kAlign);
-    t.image.assign(t.b_info + align_up(ci.size() * sizeof(uint4), kAlign), 0);
+    t.b_desc = t.b_info + align_up(ci.size() * sizeof(uint4), kAlign);
+    t.image.assign(t.b_desc + align_up(sd.size() * sizeof(uint4), kAlign), 0);
     std::memcpy(t.image.data() + t.b_cbase, cb.data(), cb.size() * 4);
     std::memcpy(t.image.data() + t.b_csh, cs.data(), cs.size() * 4);
     std::memcpy(t.image.data() + t.b_info, ci.data(), ci.size() * sizeof(uint4));
+    std::memcpy(t.image.data() + t.b_desc, sd.data(), sd.size() * sizeof(uint4));
     t.h_cbase = std::move(cb);
     return lo->agg.emplace(P, std::move(t)).first->second;
 }
@@ -497,8 +524,11 @@ int sparsify_launch(lags_layout *lo, int32_t l0, int32_t l1, const float *grad, 
         if (rc != LAGS_OK) return rc;
     }
     if (ns) {
-        rc = traced(lo, kKFinBins, s, [&] { return launch_fin_bins(a, ns, s); });
-        if (rc != LAGS_OK) return rc;
+        // layers with few histogram copies are decided inside k_fin_select
+        if (lo->bins_pre[l1] > lo->bins_pre[l0]) {
+            rc = traced(lo, kKFinBins, s, [&] { return launch_fin_bins(a, ns, s); });
+            if (rc != LAGS_OK) return rc;
+        }
         rc = traced(lo, kKFinSelect, s, [&] { return launch_fin_select(a, nfin, s); });
         if (rc != LAGS_OK) return rc;
     }
@@ -531,6 +561,7 @@ int aggregate_launch(lags_layout *lo, int32_t l0, int32_t l1, float *weights, co
     a.cbase = (const uint32_t *)(tab + t.b_cbase);
     a.csh = (const uint32_t *)(tab + t.b_csh);
     a.chunk_info = (const uint4 *)(tab + t.b_info);
+    a.sdesc = (const uint4 *)(tab + t.b_desc);
     a.start = (uint32_t *)(w + lo->ws_agg);
     a.report = (uint32_t *)(w + lo->ws_report);
     a.L = (uint32_t)lo->L;

@@ -23,6 +23,8 @@ constexpr uint32_t kCapMax = 1024;       // candidate slots per segment, at most
 constexpr uint32_t kNBins = 2048;        // candidate histogram bins per layer
 constexpr uint32_t kHistMaxCopies = 64;  // copies of a layer's histogram, at most (spread atomics)
 constexpr uint32_t kTilesPerCopy = 128;  // streaming workgroups per histogram copy, about
+constexpr uint32_t kSelfBinsCopies = 4;  // layers with at most this many copies are decided
+                                         // by their finishing workgroups (no k_fin_bins)
 constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LDS (larger: global)
 constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup (at most)
 constexpr uint32_t kFinSegsSmall = 16;   // ... in a layer of at most kFinSmallLayer segments
@@ -138,7 +140,9 @@ struct FinWork {
     uint32_t tbin_cap;
     uint32_t grain;       // segments per finishing workgroup of the layer
     uint32_t a4;          // 4-aligned start of the layer's interior
-    uint32_t pad;
+    uint32_t hist_off;    // the layer's histogram copies (first word, count)
+    uint32_t hcopies;
+    uint32_t pad[2];
 };
 
 struct SampledState {     // per sampled layer, per call, in the workspace
@@ -215,6 +219,10 @@ struct AggArgs {
     const uint32_t *csh;        // [L] log2 chunk width
     const uint4 *chunk_info;    // [NC] per chunk: first index, end index, and the
                                 // message range [moff, moff + k) of its layer
+    const uint4 *sdesc;         // [npb][2] per position block b: {layer of position
+                                // b*kStartsBlock - 1 (0 for b = 0), layer of the block's
+                                // last position (or of position K - 1), that first
+                                // layer's off and n}, {its first chunk, log2 chunk width}
     uint32_t *start;            // [P][NC+1]
     uint32_t *report;
     uint32_t L;

@@ -796,11 +796,89 @@ __device__ void mark_for_fix(const SparsifyArgs &a, uint32_t sid, uint32_t klo =
     }
 }
 
-// k_fin_bins: one 1024-thread workgroup per sampled layer, after the
-// streaming pass has filled the layer's histogram copies.  Sums the copies
-// (eight loads in flight per thread), then locates the candidate bin that
-// holds the k-th largest, or marks the layer for zero mode or (too few
-// candidates above a nonzero guess) for the exact path.
+// The threshold-bin decision for one sampled layer, after the streaming pass
+// has filled the layer's histogram copies, by the NT threads of one
+// workgroup: sum the copies into hist (LDS; eight loads in flight per thread),
+// then the layer's status: zero mode (G = 0 and fewer than k nonzero keys),
+// the fallback (too few candidates above a nonzero G, or a threshold bin
+// larger than the layer's list), or Ok with the bin bstar holding the k-th
+// largest candidate and the candidate count above it.  With `write` the
+// workgroup records the decision in the layer's state and the report (and
+// marks the layer for the fallback); every workgroup that calls it for the
+// layer reaches the same decision.
+struct BinsDecision {
+    uint32_t status, bstar, c_above;
+};
+
+template <int NT>
+__device__ BinsDecision layer_bins(const SparsifyArgs &a, uint32_t sid, uint32_t hist_off, uint32_t hcopies,
+                                   uint32_t tbin_cap, uint32_t k, uint32_t G, uint32_t SH, uint32_t *hist,
+                                   uint32_t *tmp, uint32_t *res, bool write)
+{
+    SampledState *st = a.state + sid;
+    const uint32_t *lh = a.hist + hist_off;
+    uint32_t part = 0;
+    for (uint32_t b = threadIdx.x; b < kNBins; b += NT) {
+        uint32_t h = 0;
+        for (uint32_t c0 = 0; c0 < hcopies; c0 += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) v[u] = (c0 + u < hcopies) ? lh[(c0 + u) * kNBins + b] : 0u;
+#pragma unroll
+            for (uint32_t u = 0; u < 8; ++u) h += v[u];
+        }
+        hist[b] = h;
+        part += h;
+    }
+    uint32_t C;
+    block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above
+    if (C < k && G != 0) {
+        if (write) {
+            mark_for_fix<NT>(a, sid);
+            if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
+        }
+        return {kStFix, 0u, 0u};
+    }
+    if (C < k) {
+        // G = 0 and fewer than k nonzero keys: the k-th largest key is 0, so
+        // every stored (nonzero) candidate is sent, plus the k - C zeros of
+        // lowest index
+        if (write && threadIdx.x == 0) {
+            st->status = kStZero;
+            st->c_above = C;
+            atomicAdd(&a.report[kRepSampled], 1u);
+        }
+        return {kStZero, 0u, C};
+    }
+    block_find_rank<NT>(hist, kNBins, k, res, tmp);
+    const uint32_t bstar = res[0], above = res[1];
+    if (hist[bstar] > tbin_cap) {
+        // the threshold bin holds more candidates than the layer's list (many
+        // equal keys): the fallback selects the layer, knowing that the
+        // threshold lies in this bin
+        if (write) {
+            const uint64_t blo = (uint64_t)G + ((uint64_t)bstar << SH);
+            const uint32_t klo = (uint32_t)min(blo, (uint64_t)0x7fffffffu);
+            const uint32_t khi = (bstar + 1u >= kNBins)
+                                     ? 0x7fffffffu
+                                     : (uint32_t)min(blo + (1ull << SH) - 1u, (uint64_t)0x7fffffffu);
+            mark_for_fix<NT>(a, sid, klo, khi);
+            if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
+        }
+        return {kStFix, 0u, 0u};
+    }
+    if (write && threadIdx.x == 0) {
+        st->bstar = bstar;
+        st->c_above = above;
+        st->status = kStOk;
+        atomicAdd(&a.report[kRepSampled], 1u);
+    }
+    return {kStOk, bstar, above};
+}
+
+// k_fin_bins: one 1024-thread workgroup per sampled layer with more than
+// kSelfBinsCopies histogram copies (the finishing workgroups of a layer with
+// fewer decide for themselves in k_fin_select).
 constexpr int kBinsThreads = 1024;
 
 __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
@@ -812,60 +890,10 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     if (blockIdx.x >= a.nsampled) return;
     const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
+    if (S.hcopies <= kSelfBinsCopies) return;
     const LayerInfo L = a.linfo[S.layer];
-    SampledState *st = a.state + sid;
-    const uint32_t *lh = a.hist + S.hist_off;
-    uint32_t part = 0;
-    for (uint32_t b = threadIdx.x; b < kNBins; b += NT) {
-        uint32_t h = 0;
-        for (uint32_t c0 = 0; c0 < S.hcopies; c0 += 8) {
-            uint32_t v[8];
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u) v[u] = (c0 + u < S.hcopies) ? lh[(c0 + u) * kNBins + b] : 0u;
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u) h += v[u];
-        }
-        hist[b] = h;
-        part += h;
-    }
-    uint32_t C;
-    block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above
-    if (C < L.k && st->G != 0) {
-        mark_for_fix<NT>(a, sid);
-        if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
-        return;
-    }
-    if (C < L.k) {
-        // G = 0 and fewer than k nonzero keys: the k-th largest key is 0, so
-        // every stored (nonzero) candidate is sent, plus the k - C zeros of
-        // lowest index
-        if (threadIdx.x == 0) {
-            st->status = kStZero;
-            st->c_above = C;
-            atomicAdd(&a.report[kRepSampled], 1u);
-        }
-        return;
-    }
-    block_find_rank<NT>(hist, kNBins, L.k, res, tmp);
-    if (hist[res[0]] > S.tbin_cap) {
-        // the threshold bin holds more candidates than the layer's list (many
-        // equal keys): the fallback selects the layer, knowing that the
-        // threshold lies in this bin
-        const uint32_t G = st->G, SH = st->SH, b = res[0];
-        const uint64_t blo = (uint64_t)G + ((uint64_t)b << SH);
-        const uint32_t klo = (uint32_t)min(blo, (uint64_t)0x7fffffffu);
-        const uint32_t khi = (b + 1u >= kNBins) ? 0x7fffffffu
-                                                : (uint32_t)min(blo + (1ull << SH) - 1u, (uint64_t)0x7fffffffu);
-        mark_for_fix<NT>(a, sid, klo, khi);
-        if (threadIdx.x == 0) atomicAdd(&a.report[kRepSampled], 1u);
-        return;
-    }
-    if (threadIdx.x == 0) {
-        st->bstar = res[0];
-        st->c_above = res[1];
-        st->status = kStOk;
-        atomicAdd(&a.report[kRepSampled], 1u);
-    }
+    const SampledState *st = a.state + sid;
+    layer_bins<NT>(a, sid, S.hist_off, S.hcopies, S.tbin_cap, L.k, st->G, st->SH, hist, tmp, res, true);
 }
 
 // Walk segment seg of a sampled layer in index order, one wave: fn(valid,
@@ -956,13 +984,28 @@ __global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
 {
     __shared__ uint32_t wtot[kWaves];
     __shared__ uint32_t wzero[kWaves];
+    __shared__ uint32_t bins[kNBins];
+    __shared__ uint32_t btmp[kWaves];
+    __shared__ uint32_t bres[2];
     const FinWork f = a.fin_work[a.fin_base + blockIdx.x];
     SampledState *st = a.state + f.sid;
     const uint32_t ln = lane_id();
     const uint32_t wv = threadIdx.x >> 6;
     WaveSegs ws;
     ws.load(a, f, wv, ln);            // issued before the layer's status arrives
-    const uint32_t status = st->status;   // uniform over the workgroup
+    const uint32_t G = st->G, SH = st->SH;
+    uint32_t status, bstar;
+    if (f.hcopies <= kSelfBinsCopies) {
+        // few histogram copies: every finishing workgroup of the layer sums
+        // them and decides; the layer's first records the decision
+        const BinsDecision d = layer_bins<kBlock>(a, f.sid, f.hist_off, f.hcopies, f.tbin_cap, f.k, G, SH, bins,
+                                                  btmp, bres, f.seg0 == 0u);
+        status = d.status;
+        bstar = d.bstar;
+    } else {
+        status = st->status;          // uniform over the workgroup
+        bstar = st->bstar;
+    }
     if (status == kStZero) {
         // every candidate (every nonzero entry) is sent; count the
         // workgroup's zeros
@@ -989,8 +1032,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
         }
         return;
     }
-    if (status != kStOk) return;      // the exact path takes the layer
-    const uint32_t G = st->G, SH = st->SH, bstar = st->bstar;
+    if (status != kStOk) return;      // the fallback takes the layer
     const uint32_t Gs = G ? G : 1u;           // candidates: key >= Gs
     // pass 1: per segment, candidates above the threshold bin; per lane,
     // candidates in it.  A segment with more candidates than slots is
@@ -2070,6 +2112,29 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg_starts(AggArgs a)
         x[q] = row[min(max(j, a.j_lo), a.j_hi - 1u)];
         xp[q] = row[min(max(j, a.j_lo + 1u), a.j_hi) - 1u];
     }
+    uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
+    // The usual case: the workgroup's positions, and the one before them, lie
+    // in one layer; the blocks' descriptors then hold that layer's fields and
+    // are requested together with the message entries.
+    const uint4 d0 = a.sdesc[2u * bb], d1 = a.sdesc[2u * bb + 1u];
+    const uint32_t lhi = a.sdesc[2u * min(bb + (uint32_t)BPW - 1u, a.npb - 1u)].y;
+    if (d0.x == lhi) {                      // uniform over the workgroup
+        auto chunk1 = [&](uint32_t xx) -> uint32_t {
+            uint32_t rel = xx - d0.z;
+            if (rel >= d0.w) rel = 0;            // invalid entry: counted by k_agg
+            return d1.x + (rel >> d1.y);
+        };
+#pragma unroll
+        for (int q = 0; q < PPT; ++q) {
+            const uint32_t j = j0 + threadIdx.x + q * kBlock;
+            if (j < a.j_lo || j > a.j_hi) continue;
+            const uint32_t c = (j == a.j_hi) ? a.c_hi : chunk1(x[q]);
+            const uint32_t cp = (j == a.j_lo) ? a.c_lo - 1u : chunk1(xp[q]);
+            for (uint32_t cc = cp + 1u; cc <= c && cc <= a.NC; ++cc) srow[cc] = j;
+        }
+        return;
+    }
+    // positions of several layers: stage the layers' fields in LDS
     if (threadIdx.x == 0) {
         const uint32_t l0 = a.pos_layer[bb];
         const uint32_t l1 = (bb + BPW < a.npb) ? a.pos_layer[bb + BPW] : a.L - 1;
@@ -2101,7 +2166,6 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg_starts(AggArgs a)
         }
         return lo;
     };
-    uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
         const uint32_t j = j0 + threadIdx.x + q * kBlock;
