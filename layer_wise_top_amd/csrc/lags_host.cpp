@@ -28,6 +28,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // lags_workspace_init).
 struct AggPlan {
     uint32_t NC = 0;
+    uint32_t tl = kAggTableLog2;      // log2 of the aggregate's LDS hash slots
+    bool dense = false;               // the layout has a layer that sends every entry
     std::vector<uint32_t> h_cbase;    // [L+1]
     size_t b_cbase = 0, b_csh = 0, b_info = 0, b_desc = 0;   // byte offsets inside the image
     std::vector<unsigned char> image; // cbase[L+1], csh[L], chunk_info[NC], sdesc[npb][2]
@@ -90,19 +92,23 @@ struct lags_layout {
 namespace {
 
 // Chunk widths of the aggregate for P workers: per layer, a power of two (at
-// most 2^kAggMaxWidthLog2) such that a chunk holds about kAggTargetEntries
-// message entries over all workers.
-void plan_agg(const lags_layout *lo, int32_t P, std::vector<uint32_t> &cbase,
+// most 2^kAggMaxWidthLog2) such that a chunk holds about 2^(tl-2) message
+// entries over all workers; 2^kAggDenseLog2 for a layer that sends every
+// entry (k = n).
+void plan_agg(const lags_layout *lo, int32_t P, uint32_t tl, std::vector<uint32_t> &cbase,
               std::vector<uint32_t> &csh, uint32_t &NC)
 {
     cbase.assign(lo->L + 1, 0);
     csh.assign(lo->L, 0);
     uint64_t total = 0;
+    const double target = std::ldexp(1.0, (int)tl - 2);
     for (int32_t l = 0; l < lo->L; ++l) {
         const double nl = lo->linfo[l].n, kl = lo->linfo[l].k;
-        const double width = (double)kAggTargetEntries * nl / ((double)P * kl);
+        const double width = target * nl / ((double)P * kl);
         int s = 0;
         while (s < (int)kAggMaxWidthLog2 && std::ldexp(1.0, s + 1) <= width) ++s;
+        // a layer that sends every entry: one index per thread of a chunk
+        if (lo->linfo[l].k == lo->linfo[l].n) s = kAggDenseLog2;
         csh[l] = (uint32_t)s;
         cbase[l] = (uint32_t)total;
         total += ((uint64_t)lo->linfo[l].n + (1ull << s) - 1) >> s;
@@ -344,16 +350,22 @@ const AggPlan &agg_plan(lags_layout *lo, int32_t P)
     auto it = lo->agg.find(P);
     if (it != lo->agg.end()) return it->second;
     AggPlan t;
+    t.tl = (uint64_t)P * lo->K >= kAggWideEntries ? kAggTableLog2Wide : kAggTableLog2;
     std::vector<uint32_t> cb, cs;
-    plan_agg(lo, P, cb, cs, t.NC);
+    plan_agg(lo, P, t.tl, cb, cs, t.NC);
     std::vector<uint4> ci(std::max<uint32_t>(t.NC, 1), uint4{0, 0, 0, 0});
     for (int32_t l = 0; l < lo->L; ++l) {
         const uint64_t off = lo->off[l], end = lo->off[l + 1];
+        const bool dense = lo->k[l] == end - off;
+        t.dense = t.dense || dense;
         for (uint32_t c = cb[l]; c < cb[l + 1]; ++c) {
             const uint64_t clo = off + ((uint64_t)(c - cb[l]) << cs[l]);
             const uint64_t chi = std::min<uint64_t>(clo + ((uint64_t)1 << cs[l]), end);
-            ci[c] = uint4{(uint32_t)clo, (uint32_t)chi, (uint32_t)lo->moff[l],
-                          (uint32_t)(lo->moff[l] + lo->k[l])};
+            // a k = n layer's chunk: where index clo sits in every valid
+            // message, and the marker kAggDenseChunk (no message range ends there)
+            ci[c] = dense ? uint4{(uint32_t)clo, (uint32_t)chi, (uint32_t)(lo->moff[l] + (clo - off)), kAggDenseChunk}
+                          : uint4{(uint32_t)clo, (uint32_t)chi, (uint32_t)lo->moff[l],
+                                  (uint32_t)(lo->moff[l] + lo->k[l])};
         }
     }
     // per position block of the start pass: the layers of its first
@@ -582,7 +594,7 @@ int aggregate_launch(lags_layout *lo, int32_t l0, int32_t l1, float *weights, co
     a.tl = wide ? lo->starts_tl4 : lo->starts_tl;
     int rc = traced(lo, kKAggStarts, s, [&] { return launch_agg_starts(a, s); });
     if (rc != LAGS_OK) return rc;
-    return traced(lo, kKAgg, s, [&] { return launch_agg(a, a.c_hi - a.c_lo, s); });
+    return traced(lo, kKAgg, s, [&] { return launch_agg(a, a.c_hi - a.c_lo, t.tl, t.dense, s); });
 }
 }  // namespace
 

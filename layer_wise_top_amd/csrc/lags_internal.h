@@ -36,14 +36,23 @@ __host__ __device__ inline uint32_t fin_grain(uint32_t nseg)
 {
     return nseg <= kFinSmallLayer ? kFinSegsSmall : kFinSegs;
 }
-// aggregate
-constexpr uint32_t kAggTargetEntries = 512;   // expected entries per chunk
-constexpr uint32_t kAggCap = 1024;            // fast-path capacity (entries per chunk)
-constexpr uint32_t kStartsBlock = 1024;       // message positions per start-pass block
+// aggregate: a chunk's workgroup keeps an LDS hash table of 2^TL slots (also
+// the slow path's dense window) for at most 2^(TL-1) message entries (the
+// fast path) and expects 2^(TL-2); TL is kAggTableLog2 in general and
+// kAggTableLog2Wide when a call reads at least kAggWideEntries message entries
+// (measured: 1.31B entries, 21M entries read: 0.879 ms against 0.890 ms;
+// 25.6M entries, 2.8M read: 0.056 ms against 0.046 ms)
 constexpr uint32_t kAggTableLog2 = 11;
-constexpr uint32_t kAggTable = 1u << kAggTableLog2;  // LDS hash slots (>= 2 * kAggCap);
-                                                     // also the slow path's dense window
+constexpr uint32_t kAggTableLog2Wide = 10;
+constexpr uint64_t kAggWideEntries = uint64_t(8) << 20;
+constexpr uint32_t kStartsBlock = 1024;       // message positions per start-pass block
 constexpr uint32_t kAggMaxWidthLog2 = 30;     // chunk width cap (entries)
+// A layer whose workers send every entry (k = n) is cut into chunks of one
+// index per thread; every valid message holds index off + i at position
+// moff + i, so the chunk's entries are found without the chunk-start table.
+constexpr uint32_t kAggDenseLog2 = 8;
+static_assert((1u << kAggDenseLog2) == (uint32_t)kBlock, "one index per thread");
+constexpr uint32_t kAggDenseChunk = 0xffffffffu;   // chunk_info.w of such a chunk
 // guess-failure fallback (inside k_fin_emit): the first kFixGroups workgroups
 // of the launch select every failed layer together, by a radix select over all
 // of its keys, meeting at barriers between the passes
@@ -218,7 +227,9 @@ struct AggArgs {
     const uint32_t *cbase;      // [L+1] first chunk of each layer
     const uint32_t *csh;        // [L] log2 chunk width
     const uint4 *chunk_info;    // [NC] per chunk: first index, end index, and the
-                                // message range [moff, moff + k) of its layer
+                                // message range [moff, moff + k) of its layer; for a
+                                // chunk of a k = n layer: first index, end index, the
+                                // position of the first index, kAggDenseChunk
     const uint4 *sdesc;         // [npb][2] per position block b: {layer of position
                                 // b*kStartsBlock - 1 (0 for b = 0), layer of the block's
                                 // last position (or of position K - 1), that first
@@ -263,6 +274,6 @@ hipError_t launch_x_pick(const SparsifyArgs &a, uint32_t nblocks, uint32_t level
 hipError_t launch_x_count(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_x_cut(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s);
-hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s);
+hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, uint32_t table_log2, bool dense, hipStream_t s);
 
 }  // namespace lags

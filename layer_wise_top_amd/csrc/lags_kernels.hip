@@ -2176,14 +2176,24 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg_starts(AggArgs a)
     }
 }
 
-// k_agg: one workgroup per index chunk [lo, hi) of one layer.  Dynamic LDS:
-// keys[kAggTable], vals[kAggTable], ws0[P], pre[P+1].
-__global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
+// k_agg: one workgroup per index chunk [lo, hi) of one layer, with an LDS
+// hash table of 2^TL slots.  Dynamic LDS: keys[2^TL], vals[2^TL], ws0[P],
+// pre[P+1].  The chunk's message entries are laid out worker by worker
+// (entry e of worker p: pre[p] <= e < pre[p+1]), so each slot's sum must add
+// its entries in increasing worker order, starting from +0.0.  With at most
+// 32 workers every entry finds its rank among the entries of its slot from a
+// bitmask of the slot's workers, and the sums take one barrier phase per rank
+// (the most entries any slot has), not one per worker.
+template <uint32_t TL, bool DENSE>
+__global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
 {
+    constexpr uint32_t kTable = 1u << TL;
+    constexpr uint32_t kCap = kTable / 2;      // fast-path entries
     extern __shared__ uint32_t dyn[];
     uint32_t *keys = dyn;
-    float *vals = reinterpret_cast<float *>(dyn + kAggTable);
-    uint32_t *ws0 = dyn + 2 * kAggTable;
+    float *vals = reinterpret_cast<float *>(dyn + kTable);
+    uint32_t *vmask = dyn + kTable;           // the same words: the slots' worker masks first
+    uint32_t *ws0 = dyn + 2 * kTable;
     uint32_t *pre = ws0 + a.P;
     __shared__ uint32_t tmp[kWaves];
 
@@ -2199,7 +2209,52 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     }
     const uint4 ci = a.chunk_info[c];
     const uint32_t lo = ci.x, hi = ci.y;     // the chunk's indices
-    const uint32_t m0 = ci.z, m1 = ci.w;     // its layer's message range
+    // (the DENSE instances serve layouts with k = n layers; the others keep
+    // the sparse path's registers free of the dense loop)
+    const bool dense = DENSE && ci.w == kAggDenseChunk;   // uniform
+    // its layer's message range; for a chunk of a k = n layer, the positions
+    // its indices take in every valid message
+    const uint32_t m0 = ci.z, m1 = dense ? ci.z + (hi - lo) : ci.w;
+    const float s = a.s;
+
+    if (dense) {
+        // every worker sends every index of the layer, in order: thread t
+        // sums index lo + t from position m0 + t of each message, in worker
+        // order, with one coalesced load per worker, and updates its weight
+        constexpr uint32_t kW = 16;           // workers whose loads are in flight together
+        const bool in = threadIdx.x < hi - lo;
+        // loads are unconditional, at a thread offset and worker clamped into
+        // the chunk, so that none waits for another
+        const uint32_t t = min((uint32_t)threadIdx.x, hi - lo - 1u);
+        const uint32_t x = lo + t;
+        const float wv = a.w[x];
+        float u = 0.0f;
+        uint32_t off_place = 0;
+        for (uint32_t p0 = 0; p0 < P; p0 += kW) {
+            uint32_t xi[kW];
+            float xv[kW];
+#pragma unroll
+            for (uint32_t q = 0; q < kW; ++q) {
+                // the row's start is uniform; the thread adds its own offset
+                const uint64_t row = (uint64_t)min(p0 + q, P - 1u) * a.K + m0;
+                xi[q] = (a.msg_idx + row)[t];
+                xv[q] = (a.msg_val + row)[t];
+            }
+#pragma unroll
+            for (uint32_t q = 0; q < kW; ++q) {
+                if (p0 + q < P) {
+                    u = u + xv[q];
+                    off_place |= (in && xi[q] != x) ? 1u : 0u;
+                }
+            }
+        }
+        if (!__syncthreads_or((int)off_place)) {
+            if (in) a.w[x] = __fsub_rn(wv, __fmul_rn(s, u));
+            return;
+        }
+        // an entry out of place: the chunk is summed by index below, from the
+        // same positions
+    }
 
     uint32_t carry = 0;
     for (uint32_t base = 0; base < P; base += kBlock) {
@@ -2208,6 +2263,10 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
         if (p < P) {
             const uint32_t *srow = a.start + (uint64_t)p * (a.NC + 1);
             uint32_t s0 = base == 0 ? s0f : srow[c], s1 = base == 0 ? s1f : srow[c + 1];
+            if (dense) {
+                s0 = m0;
+                s1 = m1;
+            }
             s0 = min(max(s0, m0), m1);
             s1 = min(max(s1, s0), m1);
             ws0[p] = s0;
@@ -2221,16 +2280,15 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
     if (threadIdx.x == 0) pre[P] = carry;
     __syncthreads();
     const uint32_t E = carry;
-    const float s = a.s;
     uint32_t bad = 0;
 
-    if (E <= kAggCap) {
-        for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
+    if (E <= kCap) {
+        for (uint32_t t = threadIdx.x; t < kTable; t += kBlock) {
             keys[t] = 0xffffffffu;
-            vals[t] = 0.0f;
+            vmask[t] = 0u;
         }
         __syncthreads();
-        constexpr int EPT = kAggCap / kBlock;
+        constexpr int EPT = kCap / kBlock;
         int slot[EPT];
         uint32_t wk[EPT];
         float v[EPT];
@@ -2254,6 +2312,7 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
                 v[q] = a.msg_val[at];
             }
         }
+        const bool masks = P <= 32u;          // uniform
 #pragma unroll
         for (int q = 0; q < EPT; ++q) {
             const uint32_t e = threadIdx.x + q * kBlock;
@@ -2264,27 +2323,52 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
                 continue;
             }
             const uint32_t key = x - lo;
-            uint32_t hsh = (key * 2654435761u) >> (32 - kAggTableLog2);
+            uint32_t hsh = (key * 2654435761u) >> (32 - TL);
             while (true) {
                 const uint32_t old = atomicCAS(&keys[hsh], 0xffffffffu, key);
                 if (old == 0xffffffffu || old == key) break;
-                hsh = (hsh + 1u) & (kAggTable - 1u);
+                hsh = (hsh + 1u) & (kTable - 1u);
             }
             slot[q] = (int)hsh;
+            if (masks) atomicOr(&vmask[hsh], 1u << wk[q]);
         }
         __syncthreads();
-        for (uint32_t p = 0; p < P; ++p) {   // worker order, one worker at a time
-            if (pre[p + 1] == pre[p]) continue;
+        if (masks) {
+            // rank of each entry among its slot's entries (workers in order)
+            uint32_t rk[EPT];
 #pragma unroll
             for (int q = 0; q < EPT; ++q)
-                if (slot[q] >= 0 && wk[q] == p) vals[slot[q]] = vals[slot[q]] + v[q];
-            __syncthreads();
+                rk[q] = slot[q] >= 0 ? (uint32_t)__popc(vmask[slot[q]] & ((1u << wk[q]) - 1u)) : 0xffffffffu;
+            __syncthreads();                  // every mask is read before the sums overwrite it
+            uint32_t more = 0;
+#pragma unroll
+            for (int q = 0; q < EPT; ++q) {
+                if (rk[q] == 0u) vals[slot[q]] = 0.0f + v[q];
+                more |= (rk[q] != 0xffffffffu && rk[q] > 0u) ? 1u : 0u;
+            }
+            // phase r adds the entries of rank r; the barrier ends phase r - 1
+            for (uint32_t r = 1; __syncthreads_or((int)more); ++r) {
+                more = 0;
+#pragma unroll
+                for (int q = 0; q < EPT; ++q) {
+                    if (rk[q] == r) vals[slot[q]] = vals[slot[q]] + v[q];
+                    more |= (rk[q] != 0xffffffffu && rk[q] > r) ? 1u : 0u;
+                }
+            }
+        } else {
+            for (uint32_t p = 0; p < P; ++p) {   // worker order, one worker at a time
+                if (pre[p + 1] == pre[p]) continue;
+#pragma unroll
+                for (int q = 0; q < EPT; ++q)
+                    if (slot[q] >= 0 && wk[q] == p) vals[slot[q]] = vals[slot[q]] + v[q];
+                __syncthreads();
+            }
         }
         // apply at every touched index: every weight load of the thread is
         // requested before the first store (a store may alias a later load as
         // far as the compiler knows, so a plain loop waits one memory round
         // trip per slot)
-        constexpr int TPT = kAggTable / kBlock;
+        constexpr int TPT = kTable / kBlock;
         uint32_t tk[TPT];
         float tu[TPT], tw[TPT];
 #pragma unroll
@@ -2303,11 +2387,11 @@ __global__ __launch_bounds__(kBlock) void k_agg(AggArgs a)
         // once per window, workers in order
         uint32_t *touched = keys;
         float *u = vals;
-        const uint32_t nwin = (hi - lo + kAggTable - 1) / kAggTable;
+        const uint32_t nwin = (hi - lo + kTable - 1) / kTable;
         for (uint32_t win = 0; win < nwin; ++win) {
-            const uint32_t wlo = lo + win * kAggTable;
-            const uint32_t whi = min(wlo + kAggTable, hi);
-            for (uint32_t t = threadIdx.x; t < kAggTable; t += kBlock) {
+            const uint32_t wlo = lo + win * kTable;
+            const uint32_t whi = min(wlo + kTable, hi);
+            for (uint32_t t = threadIdx.x; t < kTable; t += kBlock) {
                 touched[t] = 0;
                 u[t] = 0.0f;
             }
@@ -2481,10 +2565,20 @@ hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, hipStream_t s)
+hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, uint32_t table_log2, bool dense, hipStream_t s)
 {
-    const size_t lds = (2u * kAggTable + 2u * a.P + 1u) * sizeof(uint32_t);
-    hipLaunchKernelGGL(k_agg, dim3(nchunks), dim3(kBlock), lds, s, a);
+    const size_t lds = ((2u << table_log2) + 2u * a.P + 1u) * sizeof(uint32_t);
+    const dim3 g(nchunks), b(kBlock);
+    if (table_log2 == kAggTableLog2 && dense)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_agg<kAggTableLog2, true>), g, b, lds, s, a);
+    else if (table_log2 == kAggTableLog2)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_agg<kAggTableLog2, false>), g, b, lds, s, a);
+    else if (table_log2 == kAggTableLog2Wide && dense)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_agg<kAggTableLog2Wide, true>), g, b, lds, s, a);
+    else if (table_log2 == kAggTableLog2Wide)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_agg<kAggTableLog2Wide, false>), g, b, lds, s, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

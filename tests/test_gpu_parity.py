@@ -486,3 +486,117 @@ def test_aggregate_rejects_invalid_messages(oracle):
         a, b = int(off[l]), int(off[l + 1])
         w_o = oracle.aggregate(idx, val, w[a:b], 0.1, lo=a, hi=b)
         assert_bits_equal(f"layer {l} weights", w_g[a:b], w_o)
+
+
+def _aggregate_case(oracle, sizes, k, P, seed, collide=0.0):
+    """Messages for P workers over a layout (sorted distinct indices per layer,
+    k[l] of them), with a share `collide` of each worker's sparse entries
+    drawn from one common random set so that many indices are summed by
+    several workers; returns (off, moff, idx, val, w)."""
+    off = np.zeros(len(sizes) + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    moff = np.concatenate([[0], np.cumsum(k)]).astype(np.int64)
+    rng = np.random.default_rng(seed)
+    idx = np.empty((P, int(k.sum())), np.uint32)
+    for l in range(len(sizes)):
+        n, kl = int(sizes[l]), int(k[l])
+        base = rng.choice(n, kl, replace=False)     # worker 0's share, in random order
+        for p in range(P):
+            if kl == n:
+                sel = np.arange(n)
+            elif p and collide:
+                m = int(collide * kl)                    # shared with the other workers
+                rest = np.setdiff1d(np.arange(n), base[:m])
+                sel = np.sort(np.concatenate([base[:m], rng.choice(rest, kl - m, replace=False)]))
+            else:
+                sel = np.sort(base) if p == 0 else np.sort(rng.choice(n, kl, replace=False))
+            idx[p, moff[l]:moff[l + 1]] = sel + off[l]
+    val = rng.standard_normal(idx.shape).astype(np.float32)
+    val[:, ::7] = -val[:, ::7]
+    w = W.adversarial_values(seed + 1, int(off[-1]), "normal")
+    return off, moff, idx, val, w
+
+
+@pytest.mark.parametrize("P", [1, 3, 16, 20, 40])
+def test_aggregate_dense_and_shared_indices(oracle, P):
+    """Layers that send every entry (k = n: summed per index from fixed
+    message positions) beside sparse layers whose indices are shared by many
+    workers (worker-ordered sums through the LDS table: ranks of up to P - 1
+    for P <= 32, one phase per worker beyond), against the oracle bit for
+    bit."""
+    import torch
+    sizes = [1, 63, 256, 257, 1000, 5000, 40_000, 9000, 70_001]
+    k = np.array([1, 63, 256, 257, 1000, 5000, 400, 9000, 701], np.int64)
+    off, moff, idx, val, w = _aggregate_case(oracle, sizes, k, P, 40 + P, collide=0.5)
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(idx))
+    run.msg_val.copy_(to_dev(val))
+    w_d = to_dev(w)
+    run.aggregate(w_d, 0.05)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["bad_entries"] == 0 and rep["slow_chunks"] == 0, rep
+    assert_bits_equal(f"P={P} weights", to_np_f32(w_d), oracle.aggregate(idx, val, w, 0.05))
+
+
+def test_aggregate_dense_layer_with_entries_out_of_place(oracle):
+    """A k = n layer whose message holds an index of another layer and a
+    swapped pair: those chunks are summed by index instead, the foreign entry
+    is skipped and counted, and the other layers match the oracle."""
+    import torch
+    sizes = [3000, 700, 20_000, 5000]
+    k = np.array([3000, 700, 200, 5000], np.int64)
+    P = 5
+    off, moff, idx, val, w = _aggregate_case(oracle, sizes, k, P, 77)
+    bad = idx.copy()
+    bad[2, moff[0] + 1000] = off[2] + 11                 # into the sparse layer
+    bad[3, moff[3] + 17], bad[3, moff[3] + 300] = bad[3, moff[3] + 300], bad[3, moff[3] + 17]  # far swap
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(bad))
+    run.msg_val.copy_(to_dev(val))
+    w_d = to_dev(w)
+    run.aggregate(w_d, 0.1)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["bad_entries"] >= 1, rep
+    w_g = to_np_f32(w_d)
+    for l in (1, 2):                                     # layers whose entries are all valid
+        a, b = int(off[l]), int(off[l + 1])
+        assert_bits_equal(f"layer {l} weights", w_g[a:b], oracle.aggregate(idx, val, w[a:b], 0.1, lo=a, hi=b))
+
+
+def test_aggregate_wide_call_with_dense_layers(oracle):
+    """A call that reads at least 8M message entries takes the aggregate's
+    smaller chunks (2^10-slot tables); with layers that send every entry in
+    the layout it takes the instance with the per-index path too.  Weights
+    against the oracle bit for bit."""
+    import torch
+    P = 16
+    sizes = [3000, 40_000_000, 700, 2_000_000]
+    n_sparse = sizes[1] // 64
+    k = np.array([3000, n_sparse, 700, 2_000_000 // 64], np.int64)
+    off = np.zeros(len(sizes) + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    moff = np.concatenate([[0], np.cumsum(k)]).astype(np.int64)
+    assert P * int(k.sum()) >= 8 << 20
+    rng = np.random.default_rng(5)
+    idx = np.empty((P, int(k.sum())), np.uint32)
+    for p in range(P):
+        for l in range(len(sizes)):
+            kl = int(k[l])
+            if kl == sizes[l]:
+                sel = np.arange(kl, dtype=np.int64)
+            else:                                    # one index in every 64-entry block
+                sel = np.arange(kl, dtype=np.int64) * 64 + rng.integers(0, 64, kl)
+            idx[p, moff[l]:moff[l + 1]] = sel + off[l]
+    val = rng.standard_normal(idx.shape).astype(np.float32)
+    w = W.adversarial_values(6, int(off[-1]), "normal")
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(idx))
+    run.msg_val.copy_(to_dev(val))
+    w_d = to_dev(w)
+    run.aggregate(w_d, 0.03)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["bad_entries"] == 0 and rep["slow_chunks"] == 0, rep
+    assert_bits_equal("wide call weights", to_np_f32(w_d), oracle.aggregate(idx, val, w, 0.03))
