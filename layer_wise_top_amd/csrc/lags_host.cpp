@@ -58,7 +58,7 @@ struct lags_layout {
     std::vector<LayerInfo> linfo;
     std::vector<SampledInfo> sinfo;
     std::vector<MainWork> main_work;
-    std::vector<uint32_t> small_layers;
+    std::vector<LayerInfo> small_info;   // copies of the small layers' entries
     std::vector<FinWork> fin_work;
     std::vector<uint32_t> pos_layer;
     uint32_t starts_tl = 0;        // LDS table entries the start pass needs (one block per workgroup)
@@ -153,7 +153,7 @@ int build_plan(lags_layout *lo)
         return w;
     };
     for (int32_t l = 0; l < L; ++l) {
-        lo->small_pre[l] = (uint32_t)lo->small_layers.size();
+        lo->small_pre[l] = (uint32_t)lo->small_info.size();
         lo->stream_pre[l] = (uint32_t)stream_work.size();
         lo->sid_pre[l] = (uint32_t)lo->sinfo.size();
         lo->fin_pre[l] = (uint32_t)lo->fin_work.size();
@@ -168,7 +168,7 @@ int build_plan(lags_layout *lo)
         if (li.n <= kSmallMax) {
             li.cls = kClsSmall;
             li.ntiles = 1;
-            lo->small_layers.push_back((uint32_t)l);
+            lo->small_info.push_back(li);
         } else if (li.k == li.n) {
             li.cls = kClsDense;
             li.ntiles = (li.n + kDenseTile - 1) / kDenseTile;
@@ -207,6 +207,11 @@ int build_plan(lags_layout *lo)
             // so a large bin (many equal keys) never forces the exact path
             si.tbin_cap = (uint32_t)std::min<uint64_t>((uint64_t)si.nseg * si.cap, 0xffffffffu);
             si.fin_first = (uint32_t)lo->fin_work.size();
+            si.off = li.off;
+            si.n = li.n;
+            si.k = li.k;
+            si.moff = li.moff;
+            si.grain = grain;
             li.ntiles = (si.nseg + kTileSegs - 1) / kTileSegs;
             // histogram copies grow with the layer, so that the streaming
             // workgroups' atomics on its hottest bins stay spread
@@ -257,7 +262,7 @@ int build_plan(lags_layout *lo)
             lo->sinfo.push_back(si);
         }
     }
-    lo->small_pre[L] = (uint32_t)lo->small_layers.size();
+    lo->small_pre[L] = (uint32_t)lo->small_info.size();
     lo->stream_pre[L] = (uint32_t)stream_work.size();
     lo->sid_pre[L] = (uint32_t)lo->sinfo.size();
     lo->fin_pre[L] = (uint32_t)lo->fin_work.size();
@@ -301,7 +306,7 @@ int build_plan(lags_layout *lo)
     lo->tb_fin = part(lo->fin_work.size() * sizeof(FinWork));
     lo->tb_moff = part(lo->moff.size() * 4);
     lo->tb_pos = part(lo->pos_layer.size() * 4);
-    lo->tb_small = part(lo->small_layers.size() * 4);
+    lo->tb_small = part(lo->small_info.size() * sizeof(LayerInfo));
     lo->tables.assign(at, 0);
     unsigned char *h = lo->tables.data();
     auto put = [&](size_t o, const void *src, size_t bytes) {
@@ -313,7 +318,7 @@ int build_plan(lags_layout *lo)
     put(lo->tb_fin, lo->fin_work.data(), lo->fin_work.size() * sizeof(FinWork));
     put(lo->tb_moff, lo->moff.data(), lo->moff.size() * 4);
     put(lo->tb_pos, lo->pos_layer.data(), lo->pos_layer.size() * 4);
-    put(lo->tb_small, lo->small_layers.data(), lo->small_layers.size() * 4);
+    put(lo->tb_small, lo->small_info.data(), lo->small_info.size() * sizeof(LayerInfo));
 
     // scratch: never read before being written in a call
     const size_t ns = lo->sinfo.size();
@@ -496,7 +501,7 @@ int sparsify_launch(lags_layout *lo, int32_t l0, int32_t l1, const float *grad, 
     a.sinfo = (const SampledInfo *)(w + lo->tb_sinfo);
     a.main_work = (const MainWork *)(w + lo->tb_main);
     a.fin_work = (const FinWork *)(w + lo->tb_fin);
-    a.small_layers = (const uint32_t *)(w + lo->tb_small);
+    a.small_info = (const LayerInfo *)(w + lo->tb_small);
     a.report = (uint32_t *)(w + lo->ws_report);
     a.state = (SampledState *)(w + lo->ws_state);
     a.hist = (uint32_t *)(w + lo->ws_hist);
@@ -532,7 +537,8 @@ int sparsify_launch(lags_layout *lo, int32_t l0, int32_t l1, const float *grad, 
     if (rc != LAGS_OK) return rc;
     if (a.force_exact) return sparsify_exact(lo, a, ns, nmain, nfin, s);
     if (nmain) {
-        rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, s); });
+        const bool nt_store = (uint64_t)lo->off[l1] - lo->off[l0] > kCachedStreamMax;
+        rc = traced(lo, kKMain, s, [&] { return launch_main(a, nmain, nt_store, s); });
         if (rc != LAGS_OK) return rc;
     }
     if (ns) {

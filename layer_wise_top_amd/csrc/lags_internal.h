@@ -25,6 +25,13 @@ constexpr uint32_t kHistMaxCopies = 64;  // copies of a layer's histogram, at mo
 constexpr uint32_t kTilesPerCopy = 128;  // streaming workgroups per histogram copy, about
 constexpr uint32_t kSelfBinsCopies = 4;  // layers with at most this many copies are decided
                                          // by their finishing workgroups (no k_fin_bins)
+// a streaming pass over at most this many entries stores the residual with
+// ordinary stores (it stays in the 256 MB cache for the scattered residual
+// writes that follow: ResNet-50, 25.6M entries, step 0.1525 -> 0.1499 ms);
+// larger ones store non-temporally (with ordinary stores the 66M-entry LSTM
+// step took 0.278 ms instead of 0.244, and the 1.31B-entry step 4.11 ms
+// instead of 3.52)
+constexpr uint64_t kCachedStreamMax = uint64_t(32) << 20;
 constexpr uint32_t kTbinCap = 4096;      // threshold-bin entries resolved in LDS (larger: global)
 constexpr uint32_t kFinSegs = 32;        // segments per finishing workgroup (at most)
 constexpr uint32_t kFinSegsSmall = 16;   // ... in a layer of at most kFinSmallLayer segments
@@ -114,8 +121,12 @@ struct SampledInfo {      // one per sampled layer, device table
                           // (the list sits at the layer's slot offset in its own region)
     uint32_t hist_off;    // first word of the layer's histogram copies in the workspace
     uint32_t hcopies;     // copies (a power of two), kNBins words each
-    uint32_t pad[3];
+    // the layer's own fields, so that one load starts a per-layer workgroup
+    uint32_t off, n, k, moff;
+    uint32_t grain;       // segments per finishing workgroup of the layer
+    uint32_t pad[10];
 };
+static_assert(sizeof(SampledInfo) == 128, "two per 256-byte line");
 
 // One entry per k_main workgroup: everything a streaming tile needs, so one
 // load starts it (small and k == n layers use layer and tile only).
@@ -212,7 +223,7 @@ struct SparsifyArgs {
     uint32_t sample_base;     // first sampled-layer id
     uint32_t main_base;       // first streaming work entry
     uint32_t fin_base;        // first finishing workgroup
-    const uint32_t *small_layers;   // ids of the small layers (n <= kSmallMax), ascending
+    const LayerInfo *small_info;    // the small layers (n <= kSmallMax), ascending
     uint32_t small_base;      // first small layer of the range in that list
     uint32_t nsmall;          // small layers in the range
 };
@@ -263,7 +274,7 @@ hipError_t static_scratch(void **out);
 
 // launchers (lags_kernels.hip)
 hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
-hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
+hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, bool nt_store, hipStream_t s);
 hipError_t launch_fin_bins(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_select(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);
 hipError_t launch_fin_resolve(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s);

@@ -403,7 +403,6 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     if (blockIdx.x >= a.nsampled) return;
     const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
-    const LayerInfo L = a.linfo[S.layer];
     SampledState *st = a.state + sid;
     uint32_t *stw = reinterpret_cast<uint32_t *>(st);
     for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += NT) stw[t] = 0;
@@ -413,22 +412,22 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     __syncthreads();
     if (a.force_exact) {
         // exact mode: the radix select starts from an empty prefix at rank k
-        if (threadIdx.x == 0) st->xrank = L.k;
+        if (threadIdx.x == 0) st->xrank = S.k;
         return;
     }
     uint32_t cnt, rank, m = 0;
     LdsRun run;
     if (S.full_sample) {
-        cnt = L.n;
-        rank = L.k;
+        cnt = S.n;
+        rank = S.k;
         // the whole layer is requested at once (cnt <= kSampleMax entries)
         constexpr int EPT = kSampleMax / NT;
         float gv[EPT], rv[EPT];
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const uint32_t i = threadIdx.x + u * NT;
-            gv[u] = (i < cnt) ? a.grad[L.off + i] : 0.0f;
-            rv[u] = (i < cnt) ? a.res[L.off + i] : 0.0f;
+            gv[u] = (i < cnt) ? a.grad[S.off + i] : 0.0f;
+            rv[u] = (i < cnt) ? a.res[S.off + i] : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
@@ -609,6 +608,7 @@ __device__ __forceinline__ uint32_t cand_bin(uint32_t key, uint32_t G, uint32_t 
 
 constexpr uint32_t kHeavySeg = 256;   // candidates of a segment counted in LDS beyond this
 
+template <bool NTS>
 __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32_t seg,
                                 const SampledState *st, uint32_t *hist, uint2 *stage,
                                 uint32_t (*wtot)[kWaves], uint32_t *lh)
@@ -630,7 +630,8 @@ __device__ void sampled_segment(const SparsifyArgs &a, const MainWork &w, uint32
     for (int u = 0; u < kRows; ++u) {
         acc[u] = acc[u] + rv[u];
         if (sv.row_in(u)) {
-            __builtin_nontemporal_store(acc[u], r4 + sv.row(u));
+            if (NTS) __builtin_nontemporal_store(acc[u], r4 + sv.row(u));
+            else r4[sv.row(u)] = acc[u];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (key_of(acc[u][j]) >= Gs) fl |= 1u << (4 * u + j);
@@ -699,6 +700,10 @@ __device__ void dense_tile(const SparsifyArgs &a, const MainWork &w, uint32_t pa
 
 // Grid: kTileSegs workgroups per work entry.  A sampled tile's workgroup
 // takes one segment; a k == n tile is split into kTileSegs equal parts.
+// NTS: the residual is stored non-temporally (streams beyond the caches);
+// otherwise with ordinary stores, which keep a layout small enough for the
+// 256 MB cache there for the finishing kernels' scattered residual writes.
+template <bool NTS>
 __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
 {
     __shared__ uint2 stage[kCapMax];
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(kBlock) void k_main(SparsifyArgs a)
         const uint32_t seg = w.tile * kTileSegs + part;
         // consecutive workgroups take consecutive histogram copies
         if (seg < w.nseg)
-            sampled_segment(a, w, seg, a.state + w.sid,
+            sampled_segment<NTS>(a, w, seg, a.state + w.sid,
                             a.hist + w.hist_off + (blockIdx.x & (w.hcopies - 1u)) * kNBins, stage, wtot, lh);
         return;
     }
@@ -774,6 +779,31 @@ __device__ __forceinline__ uint32_t seg_len(const FinWork &f, uint32_t s)
     if (s == 0) len += f.a4 - f.off;
     if (s == f.nseg - 1u) len += end - b4;
     return len;
+}
+
+// The static fields of sampled layer sid's finishing work (its first
+// workgroup's: seg0 = 0), from the layer's own entry.
+__device__ __forceinline__ FinWork layer_fin(const SampledInfo &S, uint32_t sid)
+{
+    FinWork f{};
+    f.sid = sid;
+    f.seg0 = 0;
+    f.nseg = S.nseg;
+    f.seg_base = S.seg_base;
+    f.cap = S.cap;
+    f.slot_lo = S.slot_lo;
+    f.slot_hi = S.slot_hi;
+    f.fin_first = S.fin_first;
+    f.off = S.off;
+    f.n = S.n;
+    f.moff = S.moff;
+    f.k = S.k;
+    f.tbin_cap = S.tbin_cap;
+    f.grain = S.grain;
+    f.a4 = S.a4;
+    f.hist_off = S.hist_off;
+    f.hcopies = S.hcopies;
+    return f;
 }
 
 // Hand a sampled layer whose guess failed to the fallback of k_fin_emit:
@@ -891,9 +921,8 @@ __global__ __launch_bounds__(kBinsThreads) void k_fin_bins(SparsifyArgs a)
     const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
     if (S.hcopies <= kSelfBinsCopies) return;
-    const LayerInfo L = a.linfo[S.layer];
     const SampledState *st = a.state + sid;
-    layer_bins<NT>(a, sid, S.hist_off, S.hcopies, S.tbin_cap, L.k, st->G, st->SH, hist, tmp, res, true);
+    layer_bins<NT>(a, sid, S.hist_off, S.hcopies, S.tbin_cap, S.k, st->G, st->SH, hist, tmp, res, true);
 }
 
 // Walk segment seg of a sampled layer in index order, one wave: fn(valid,
@@ -1114,15 +1143,17 @@ __global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
 
 // Exact threshold and tie cut among the h entries of the threshold bin (the
 // need-th largest key; among keys equal to it, the lowest indices first), and
-// the per-segment and per-workgroup counts of the bin's selected entries.
+// the per-segment and per-workgroup counts of the bin's selected entries:
+// added to seg_sel, and to the finishing workgroups' counts in LDS (wcnt,
+// which may alias hist) or, without wcnt, to fin_total in device memory.
 // Every key of the bin lies in [klo, khi] and every index in the layer
 // [f.off, f.off + f.n), so only the bits that vary there are resolved.  When
 // all keys equal to the threshold are taken, the cut is the largest index.
 template <class KeyF, class IdxF>
-__device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t h, uint32_t need,
+__device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t nfb, uint32_t h, uint32_t need,
                              uint32_t klo, uint32_t khi, const KeyF &key, const IdxF &idx,
-                             uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t &T_out,
-                             uint32_t &cut_out)
+                             uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t *wcnt,
+                             uint32_t &T_out, uint32_t &cut_out)
 {
     uint32_t e, eq;
     const uint32_t T = block_radix_select(key, [](uint32_t) { return true; }, h, need, hist, tmp, res, &e,
@@ -1135,14 +1166,20 @@ __device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t h
         cut = ~block_radix_select([&](uint32_t p) { return ~idx(p); }, [&](uint32_t p) { return key(p) == T; },
                                   h, e, hist, tmp, res, &e2, nullptr, varying_bits(nlo, nhi), nlo);
     }
+    if (wcnt) {               // the selects are done with hist (their last barrier)
+        for (uint32_t b = threadIdx.x; b < nfb; b += kBlock) wcnt[b] = 0;
+        __syncthreads();
+    }
     for (uint32_t p = threadIdx.x; p < h; p += kBlock) {
         const uint32_t kp = key(p), ip = idx(p);
         if (kp > T || (kp == T && ip <= cut)) {
             const uint32_t sg = seg_of(f, ip);
             atomicAdd(&a.seg_sel[f.seg_base + sg], 1u);
-            atomicAdd(&a.fin_total[f.fin_first + sg / f.grain], 1u);
+            if (wcnt) atomicAdd(&wcnt[sg / f.grain], 1u);
+            else atomicAdd(&a.fin_total[f.fin_first + sg / f.grain], 1u);
         }
     }
+    if (wcnt) __syncthreads();
     T_out = T;
     cut_out = cut;
 }
@@ -1163,7 +1200,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
 
     if (blockIdx.x >= a.nsampled) {
         // a small layer, start to finish: acc in LDS, exact radix select
-        const LayerInfo L = a.linfo[a.small_layers[a.small_base + (blockIdx.x - a.nsampled)]];
+        const LayerInfo L = a.small_info[a.small_base + (blockIdx.x - a.nsampled)];
         float *acc_s = reinterpret_cast<float *>(pool);
         {
             constexpr int EPT = kSmallMax / kBlock;   // the whole layer requested at once
@@ -1195,18 +1232,32 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
     }
 
     const uint32_t sid = a.sample_base + blockIdx.x;
-    const SampledInfo S = a.sinfo[sid];
-    const LayerInfo L = a.linfo[S.layer];
-    const FinWork f = a.fin_work[S.fin_first];     // the layer's static fields
     SampledState *st = a.state + sid;
-    const uint32_t status = st->status;
+    const uint32_t status = st->status;      // requested with the layer's entry
     const uint32_t h = st->tbin_n;
+    const SampledInfo S = a.sinfo[sid];
+    const FinWork f = layer_fin(S, sid);
+    const uint2 *tb = a.tbin + (((uint64_t)S.slot_hi << 32) | S.slot_lo);
+    // requested before the status and the list's length arrive: the list's
+    // first entries and the finishing workgroups' counts (all of them when
+    // their LDS counts fit hist)
+    constexpr int EPT = kTbinCap / kBlock;
+    constexpr int FPT = kNBins / kBlock;
+    const uint32_t hcap = min(S.tbin_cap, kTbinCap);      // >= 1
+    uint2 c[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) c[u] = tb[min(threadIdx.x + u * kBlock, hcap - 1u)];
+    const uint32_t nfb = S.fin_nblocks;
+    const bool lds_counts = nfb <= kNBins;
+    uint32_t ft[FPT];
+#pragma unroll
+    for (int e = 0; e < FPT; ++e) ft[e] = a.fin_total[S.fin_first + min(threadIdx.x * FPT + e, nfb - 1u)];
 
     if (status == kStZero) {
         // T = 0: the first e zeros (index order) are sent with every stored
         // candidate.  Per finishing workgroup: zeros before it, zeros it
         // sends, message offset.
-        const uint32_t e = L.k - st->c_above;
+        const uint32_t e = S.k - st->c_above;
         uint32_t zcarry = 0, carry = 0;
         for (uint32_t base = 0; base < S.fin_nblocks; base += kBlock) {
             const uint32_t b = base + threadIdx.x;
@@ -1235,8 +1286,7 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
 
     // resolve the threshold inside bin bstar: in LDS when the bin fits,
     // otherwise straight from the workspace
-    const uint32_t need = L.k - st->c_above;
-    const uint2 *tb = a.tbin + (((uint64_t)S.slot_hi << 32) | S.slot_lo);
+    const uint32_t need = S.k - st->c_above;
     // the keys of bin bstar: (key - G) >> SH == bstar, or above for the last bin
     const uint32_t bstar = st->bstar;
     const uint64_t blo = (uint64_t)st->G + ((uint64_t)bstar << st->SH);
@@ -1250,14 +1300,8 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
         return;
     }
     uint32_t T, idx_cut;
+    uint32_t *wcnt = lds_counts ? hist : nullptr;
     if (h <= kTbinCap) {
-        constexpr int EPT = kTbinCap / kBlock;     // the whole bin requested at once
-        uint2 c[EPT];
-#pragma unroll
-        for (int u = 0; u < EPT; ++u) {
-            const uint32_t p = threadIdx.x + u * kBlock;
-            c[u] = (p < h) ? tb[p] : make_uint2(0u, 0u);
-        }
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const uint32_t p = threadIdx.x + u * kBlock;
@@ -1267,20 +1311,39 @@ __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
             }
         }
         __syncthreads();
-        resolve_tbin(a, f, h, need, klo, khi, [&](uint32_t p) { return tk[p]; },
-                     [&](uint32_t p) { return ti[p]; }, hist, tmp, res, T, idx_cut);
+        resolve_tbin(a, f, nfb, h, need, klo, khi, [&](uint32_t p) { return tk[p]; },
+                     [&](uint32_t p) { return ti[p]; }, hist, tmp, res, wcnt, T, idx_cut);
     } else {
         if (threadIdx.x == 0) atomicAdd(&a.report[kRepWide], 1u);
-        resolve_tbin(a, f, h, need, klo, khi, [&](uint32_t p) { return tb[p].y & 0x7fffffffu; },
-                     [&](uint32_t p) { return tb[p].x; }, hist, tmp, res, T, idx_cut);
+        resolve_tbin(a, f, nfb, h, need, klo, khi, [&](uint32_t p) { return tb[p].y & 0x7fffffffu; },
+                     [&](uint32_t p) { return tb[p].x; }, hist, tmp, res, wcnt, T, idx_cut);
     }
-    // the workgroup's own atomics above complete before the scan reads the totals
-    wait_mem_done();
-    __syncthreads();
-    // per-workgroup totals -> exclusive message offsets (in place)
-    block_scan_items<16>(
-        S.fin_nblocks, tmp, [&](uint32_t b) { return ld_coherent(&a.fin_total[S.fin_first + b]); },
-        [&](uint32_t b, uint32_t ex, uint32_t) { a.fin_total[S.fin_first + b] = ex; });
+    // per-workgroup totals (above the bin, plus the bin's selected entries)
+    // -> exclusive message offsets (in place)
+    if (lds_counts) {
+        uint32_t v[FPT], sum = 0;
+#pragma unroll
+        for (int e = 0; e < FPT; ++e) {
+            const uint32_t b = threadIdx.x * FPT + e;
+            v[e] = b < nfb ? ft[e] + wcnt[b] : 0u;
+            sum += v[e];
+        }
+        uint32_t tot;
+        uint32_t run = block_excl_scan(sum, tmp, tot);
+#pragma unroll
+        for (int e = 0; e < FPT; ++e) {
+            const uint32_t b = threadIdx.x * FPT + e;
+            if (b < nfb) a.fin_total[S.fin_first + b] = run;
+            run += v[e];
+        }
+    } else {
+        // the workgroup's own atomics above complete before the scan reads the totals
+        wait_mem_done();
+        __syncthreads();
+        block_scan_items<16>(
+            nfb, tmp, [&](uint32_t b) { return ld_coherent(&a.fin_total[S.fin_first + b]); },
+            [&](uint32_t b, uint32_t ex, uint32_t) { a.fin_total[S.fin_first + b] = ex; });
+    }
     if (threadIdx.x == 0) {
         st->T = T;
         st->idx_cut = idx_cut;
@@ -1754,7 +1817,7 @@ __global__ __launch_bounds__(kBlock) void k_x_cut(SparsifyArgs a)
     const uint32_t sid = a.sample_base + blockIdx.x;
     const SampledInfo S = a.sinfo[sid];
     SampledState *st = a.state + sid;
-    const FinWork f = a.fin_work[S.fin_first];     // the layer's static fields
+    const FinWork f = layer_fin(S, sid);           // the layer's static fields
     const uint32_t *segeq =
         reinterpret_cast<const uint32_t *>(a.tbin + (((uint64_t)S.slot_hi << 32) | S.slot_lo));
     const uint32_t T = st->T, e = st->xrank;       // 1 <= e <= keys equal to T
@@ -1887,11 +1950,10 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
 {
     const uint32_t F = a.fix_groups, wg = blockIdx.x, t = threadIdx.x;
     const SampledInfo S = a.sinfo[sid];
-    const LayerInfo L = a.linfo[S.layer];
     uint32_t *fb = a.fb + (uint64_t)sid * kFbWords;
     MainWork mw{};                        // the fields seg_view reads
-    mw.off = L.off;
-    mw.end = L.off + L.n;
+    mw.off = S.off;
+    mw.end = S.off + S.n;
     mw.a4 = S.a4;
     mw.b4 = S.b4;
     mw.nseg = S.nseg;
@@ -1905,7 +1967,7 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
     const uint32_t klo = stl.fix_klo, khi = stl.fix_khi;
     const uint32_t vb = varying_bits(klo, khi);
     uint32_t prefix = vb >= 32u ? 0u : (klo >> vb) << vb;
-    uint32_t rank = L.k, gt22 = 0, nbar = 0;
+    uint32_t rank = S.k, gt22 = 0, nbar = 0;
     for (uint32_t level = 0; level < 3u; ++level) {
         const uint32_t sh = x_shift(level), nb = x_bins(level);
         if (sh >= vb) continue;           // every bit of this digit is known
@@ -1937,7 +1999,7 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
         for (uint32_t b = t; b < nb; b += kBlock)
             if (x.hl[b]) atomicAdd(&gh[b], x.hl[b]);
         fix_barrier(a, fb, F, ++nbar);
-        if (first) rank = L.k - ld_coherent(&fb[kFbAbove]);
+        if (first) rank = S.k - ld_coherent(&fb[kFbAbove]);
         for (uint32_t b = t; b < nb; b += kBlock) x.hp[b] = ld_coherent(&gh[b]);
         __syncthreads();
         block_find_rank(x.hp, nb, rank, x.res, x.tmp);
@@ -1984,7 +2046,7 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
     // flags stay in registers
     float *stage = reinterpret_cast<float *>(x.hl);   // hl and hp: kSeg floats
     static_assert(sizeof(x.hl) + sizeof(x.hp) >= kSeg * sizeof(float), "a segment fits the stage");
-    const uint32_t mend = L.moff + L.k;
+    const uint32_t mend = S.moff + S.k;
     for (uint32_t sg = s_lo; sg < s_hi; ++sg) {
         SegView sv;
         uint32_t fgt = 0, feq = 0;        // bit 4u + j: entry j of row u
@@ -2037,7 +2099,7 @@ __device__ void fix_layer(const SparsifyArgs &a, uint32_t sid, FixLds &x)
         c[kParts - 1] = tsel ? 1u : 0u;
         const uint32_t nsel = block_positions(c, p, x.wtot);
         auto put = [&](uint32_t pos, uint32_t idx, float v) {
-            const uint32_t m = L.moff + run_sel + pos;
+            const uint32_t m = S.moff + run_sel + pos;
             if (m < mend) {                  // the layer's selection holds exactly k entries
                 a.msg_idx[m] = idx;
                 a.msg_val[m] = v;
@@ -2485,13 +2547,16 @@ hipError_t launch_sample(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, hipStream_t s)
+hipError_t launch_main(const SparsifyArgs &a, uint32_t nblocks, bool nt_store, hipStream_t s)
 {
     const uint32_t ngroups = nblocks * kTileSegs;
     // the pad doubles as a heavy segment's LDS histogram
     const size_t pad = std::max<size_t>(stream_lds_pad(ngroups, (kCapMax * 2 + kParts * kWaves) * 4),
                                         kNBins * sizeof(uint32_t));
-    hipLaunchKernelGGL(k_main, dim3(ngroups), dim3(kBlock), pad, s, a);
+    if (nt_store)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_main<true>), dim3(ngroups), dim3(kBlock), pad, s, a);
+    else
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(k_main<false>), dim3(ngroups), dim3(kBlock), pad, s, a);
     return hipGetLastError();
 }
 
