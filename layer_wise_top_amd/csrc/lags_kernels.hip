@@ -195,19 +195,6 @@ __device__ uint32_t block_scan_items(uint32_t n, uint32_t *tmp, const Val &val, 
     return carry;
 }
 
-template <int NT = kBlock>
-__device__ uint32_t block_max(uint32_t v, uint32_t *tmp)
-{
-    const uint32_t m = wave_max(v);
-    if (lane_id() == 0) tmp[threadIdx.x >> 6] = m;
-    __syncthreads();
-    uint32_t r = 0;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) r = max(r, tmp[i]);
-    __syncthreads();
-    return r;
-}
-
 // Find, in an LDS histogram of nbins bins (nbins a multiple of NT), the bin
 // holding the rank-th largest item (rank >= 1, counting from the top bin).
 // res[0] = bin, res[1] = items in higher bins.  The caller guarantees rank <=
@@ -393,8 +380,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 {
     constexpr int NT = kSampleThreads;
     __shared__ uint32_t keys[kSampleMax];
-    __shared__ uint32_t hist[kSampleBins];
+    __shared__ uint32_t hist[kSampleBins];     // first 12 key bits below the sign
+    __shared__ uint32_t hist2[kSampleBins];    // the next 12, inside the chosen bin
     __shared__ uint32_t tmp[NT / 64];
+    __shared__ uint32_t wmax[NT / 64];
     __shared__ uint32_t res[2];
 
     if (blockIdx.x == 0 && threadIdx.x < 2) a.report[kRepSampled + threadIdx.x] = 0;
@@ -408,7 +397,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     for (uint32_t t = threadIdx.x; t < sizeof(SampledState) / 4; t += NT) stw[t] = 0;
     uint32_t *lh = a.hist + S.hist_off;
     for (uint32_t t = threadIdx.x; t < S.hcopies * kNBins; t += NT) lh[t] = 0;
-    for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
+    for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) {
+        hist[b] = 0;
+        hist2[b] = 0;
+    }
     __syncthreads();
     if (a.force_exact) {
         // exact mode: the radix select starts from an empty prefix at rank k
@@ -471,8 +463,14 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
         }
     }
     run.flush(hist);
+    {
+        const uint32_t wm = wave_max(m);
+        if (lane_id() == 0) wmax[threadIdx.x >> 6] = wm;
+    }
     __syncthreads();
-    const uint32_t M = block_max<NT>(m, tmp);
+    uint32_t M = 0;              // the largest sample key
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) M = max(M, wmax[i]);
     if (rank >= cnt) {
         // k close to n: the rank is beyond the sample, so every nonzero
         // entry is a candidate (G = 0)
@@ -484,19 +482,16 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
         }
         return;
     }
-    block_find_rank<NT>(hist, kSampleBins, rank, res, tmp);
+    block_find_rank<NT>(hist, kSampleBins, rank, res, tmp);   // ends at a barrier
     const uint32_t b1 = res[0];
     const uint32_t rank2 = rank - res[1];
-    __syncthreads();
-    for (uint32_t b = threadIdx.x; b < kSampleBins; b += NT) hist[b] = 0;
-    __syncthreads();
     for (uint32_t e = threadIdx.x; e < cnt; e += NT) {
         const uint32_t key = keys[e];
-        if ((key >> 19) == b1) run.add(hist, (key >> 7) & (kSampleBins - 1));
+        if ((key >> 19) == b1) run.add(hist2, (key >> 7) & (kSampleBins - 1));
     }
-    run.flush(hist);
-    __syncthreads();
-    block_find_rank<NT>(hist, kSampleBins, rank2, res, tmp);
+    run.flush(hist2);
+    __syncthreads();             // also: every thread has read res
+    block_find_rank<NT>(hist2, kSampleBins, rank2, res, tmp);
     if (threadIdx.x == 0) {
         const uint32_t G = (b1 << 19) | (res[0] << 7);
         uint32_t sh = 0;
@@ -847,18 +842,32 @@ __device__ BinsDecision layer_bins(const SparsifyArgs &a, uint32_t sid, uint32_t
 {
     SampledState *st = a.state + sid;
     const uint32_t *lh = a.hist + hist_off;
+    // thread t sums bins t + i * NT over the copies, all of a round's loads
+    // in flight together: 16 per thread with 1024 threads, 8 with 256 (their
+    // register budget), one copy per round
+    constexpr int BPT = kNBins / NT;
+    constexpr uint32_t R = (NT >= 1024 ? 16u : 8u) / BPT;   // copies per round
+    static_assert(BPT * NT == (int)kNBins && R >= 1u, "bins split evenly");
+    uint32_t h[BPT];
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) h[i] = 0;
+    for (uint32_t c0 = 0; c0 < hcopies; c0 += R) {
+        uint32_t v[R][BPT];
+#pragma unroll
+        for (uint32_t u = 0; u < R; ++u)
+#pragma unroll
+            for (int i = 0; i < BPT; ++i)
+                v[u][i] = (c0 + u < hcopies) ? lh[(c0 + u) * kNBins + threadIdx.x + i * NT] : 0u;
+#pragma unroll
+        for (uint32_t u = 0; u < R; ++u)
+#pragma unroll
+            for (int i = 0; i < BPT; ++i) h[i] += v[u][i];
+    }
     uint32_t part = 0;
-    for (uint32_t b = threadIdx.x; b < kNBins; b += NT) {
-        uint32_t h = 0;
-        for (uint32_t c0 = 0; c0 < hcopies; c0 += 8) {
-            uint32_t v[8];
 #pragma unroll
-            for (uint32_t u = 0; u < 8; ++u) v[u] = (c0 + u < hcopies) ? lh[(c0 + u) * kNBins + b] : 0u;
-#pragma unroll
-            for (uint32_t u = 0; u < 8; ++u) h += v[u];
-        }
-        hist[b] = h;
-        part += h;
+    for (int i = 0; i < BPT; ++i) {
+        hist[threadIdx.x + i * NT] = h[i];
+        part += h[i];
     }
     uint32_t C;
     block_excl_scan<NT>(part, tmp, C);    // also orders the LDS writes above

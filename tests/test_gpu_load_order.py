@@ -13,17 +13,32 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 CODE = """
+import os, sys
+import numpy as np
 from layer_wise_top_amd import lags
 lay = lags.Layout([0, 50000, 60000], [50, 10])    # the library is loaded here
 import torch
+import oracle
+seed = int.from_bytes(os.urandom(4), "little")
+print("seed", seed, flush=True)
 ws = lags.workspace(lay, 1)
-g = torch.randn(60000, device="cuda")
+gen = torch.Generator(device="cuda")
+gen.manual_seed(seed)
+g = torch.randn(60000, device="cuda", generator=gen)
 r = torch.zeros_like(g)
 mi = torch.empty(60, dtype=torch.int32, device="cuda")
 mv = torch.empty(60, device="cuda")
 lags.lags_sparsify_layers(lay, g, r, mi, mv, ws)
 torch.cuda.synchronize()
-assert int((r == 0).sum()) == 60, "sent entries have a zero residual"
+gn, rg = g.cpu().numpy(), r.cpu().numpy()
+mi_o, mv_o, r_o = oracle.default().sparsify(np.array([0, 50000, 60000]), np.array([50, 10]), gn,
+                                            np.zeros(60000, np.float32))
+ok_m = np.array_equal(mi.cpu().numpy().view(np.uint32), mi_o)
+diff = np.flatnonzero(rg.view(np.uint32) != r_o.view(np.uint32))
+if not ok_m or diff.size:
+    print("zeros", int((rg == 0).sum()), "messages equal", ok_m, "residual mismatches", diff[:20],
+          "report", lags.lags_workspace_report(lay, ws), flush=True)
+    sys.exit(1)
 print("load order ok", flush=True)
 """
 
