@@ -2394,7 +2394,13 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
                 continue;
             }
             const uint32_t key = x - lo;
-            uint32_t hsh = (key * 2654435761u) >> (32 - TL);
+            // a chunk no wider than the table: one slot per index, in index
+            // order, so that a wave's weight updates below fall in one narrow
+            // index range (ResNet-50 k_agg 38.4 -> 37 us); a wider chunk: a
+            // multiplicative hash (Knuth's constant), which spreads runs of
+            // consecutive indices (index-ordered buckets there made a chunk
+            // holding one run of 512 indices take ~0.2 ms of probing)
+            uint32_t hsh = (hi - lo <= kTable) ? key : (key * 2654435761u) >> (32 - TL);
             while (true) {
                 const uint32_t old = atomicCAS(&keys[hsh], 0xffffffffu, key);
                 if (old == 0xffffffffu || old == key) break;

@@ -600,3 +600,40 @@ def test_aggregate_wide_call_with_dense_layers(oracle):
     rep = run.report()
     assert rep["bad_entries"] == 0 and rep["slow_chunks"] == 0, rep
     assert_bits_equal("wide call weights", to_np_f32(w_d), oracle.aggregate(idx, val, w, 0.03))
+
+
+def test_aggregate_runs_of_consecutive_indices(oracle):
+    """A worker whose entries form one run of consecutive indices inside a
+    chunk much wider than the LDS table: the run falls into a few buckets and
+    its entries probe along consecutive slots.  Weights against the oracle."""
+    import time
+    import torch
+    P = 2
+    sizes = [4_000_000, 3_000_000]
+    k = np.array([512, 500], np.int64)
+    off = np.zeros(len(sizes) + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    moff = np.concatenate([[0], np.cumsum(k)]).astype(np.int64)
+    rng = np.random.default_rng(8)
+    idx = np.empty((P, int(k.sum())), np.uint32)
+    for l, n in enumerate(sizes):
+        kl = int(k[l])
+        start = int(rng.integers(0, n - kl))
+        idx[0, moff[l]:moff[l + 1]] = np.arange(start, start + kl) + off[l]          # one run
+        idx[1, moff[l]:moff[l + 1]] = np.sort(rng.choice(n, kl, replace=False)) + off[l]
+    val = rng.standard_normal(idx.shape).astype(np.float32)
+    w = W.adversarial_values(9, int(off[-1]), "normal")
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(idx))
+    run.msg_val.copy_(to_dev(val))
+    w_d = to_dev(w)
+    run.aggregate(w_d, 0.2)                                  # first call: setup
+    torch.cuda.synchronize()
+    w_d.copy_(to_dev(w))
+    t0 = time.perf_counter()
+    run.aggregate(w_d, 0.2)
+    torch.cuda.synchronize()
+    _progress(f"[runs] aggregate {1e3 * (time.perf_counter() - t0):.3f} ms")
+    rep = run.report()
+    assert rep["bad_entries"] == 0, rep
+    assert_bits_equal("run weights", to_np_f32(w_d), oracle.aggregate(idx, val, w, 0.2))
