@@ -1151,7 +1151,9 @@ __global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
 }
 
 // Exact threshold and tie cut among the h entries of the threshold bin (the
-// need-th largest key; among keys equal to it, the lowest indices first), and
+// need-th largest key; among keys equal to it, the lowest indices first; a
+// bin of at most kBlock entries by ranking every entry, a larger one by radix
+// selects), and
 // the per-segment and per-workgroup counts of the bin's selected entries:
 // added to seg_sel, and to the finishing workgroups' counts in LDS (wcnt,
 // which may alias hist) or, without wcnt, to fin_total in device memory.
@@ -1164,16 +1166,43 @@ __device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t n
                              uint32_t *hist, uint32_t *tmp, uint32_t *res, uint32_t *wcnt,
                              uint32_t &T_out, uint32_t &cut_out)
 {
-    uint32_t e, eq;
-    const uint32_t T = block_radix_select(key, [](uint32_t) { return true; }, h, need, hist, tmp, res, &e,
-                                          &eq, varying_bits(klo, khi), klo);
-    uint32_t cut = 0xffffffffu;
-    if (e < eq) {
-        // e-th smallest index among keys == T  ==  e-th largest of ~index
-        const uint32_t nlo = ~(f.off + (f.n - 1u)), nhi = ~f.off;
-        uint32_t e2;
-        cut = ~block_radix_select([&](uint32_t p) { return ~idx(p); }, [&](uint32_t p) { return key(p) == T; },
-                                  h, e, hist, tmp, res, &e2, nullptr, varying_bits(nlo, nhi), nlo);
+    uint32_t T, cut = 0xffffffffu;
+    if (h <= (uint32_t)kBlock) {
+        // a small bin: one entry per thread, ranked against all h entries in
+        // (key descending, index ascending) order (the entries' indices are
+        // distinct); the entry of rank need - 1 is the threshold key and,
+        // unless every entry equal to it is taken, the cut
+        if (threadIdx.x == 0) {
+            res[0] = 0u;
+            res[1] = 0xffffffffu;
+        }
+        __syncthreads();
+        const bool in = threadIdx.x < h;
+        const uint32_t km = in ? key(threadIdx.x) : 0u, im = in ? idx(threadIdx.x) : 0u;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < h; ++j) {
+            const uint32_t kj = key(j), ij = idx(j);
+            rank += (kj > km || (kj == km && ij < im)) ? 1u : 0u;
+        }
+        if (in && rank == need - 1u) {
+            res[0] = km;
+            res[1] = im;
+        }
+        __syncthreads();
+        T = res[0];
+        if (__syncthreads_or(in && km == T && rank >= need)) cut = res[1];
+    } else {
+        uint32_t e, eq;
+        T = block_radix_select(key, [](uint32_t) { return true; }, h, need, hist, tmp, res, &e, &eq,
+                               varying_bits(klo, khi), klo);
+        if (e < eq) {
+            // e-th smallest index among keys == T  ==  e-th largest of ~index
+            const uint32_t nlo = ~(f.off + (f.n - 1u)), nhi = ~f.off;
+            uint32_t e2;
+            cut = ~block_radix_select([&](uint32_t p) { return ~idx(p); },
+                                      [&](uint32_t p) { return key(p) == T; }, h, e, hist, tmp, res, &e2,
+                                      nullptr, varying_bits(nlo, nhi), nlo);
+        }
     }
     if (wcnt) {               // the selects are done with hist (their last barrier)
         for (uint32_t b = threadIdx.x; b < nfb; b += kBlock) wcnt[b] = 0;
