@@ -983,12 +983,18 @@ __device__ void walk_segment(const SparsifyArgs &a, const FinWork &f, uint32_t s
 // counts and first 64 slots loaded up front so that one memory round trip
 // serves all of them.
 constexpr int kSegsPerWave = kFinSegs / kWaves;
+// A workgroup of at most kFinSegs / 2 segments gives each wave at most half
+// of the entries of first[]: the other half holds the next 64 slots of the
+// wave's segments (layers whose segments often hold 64-128 candidates, as at
+// rho = 1/100, then need no second round trip).
 struct WaveSegs {
+    static constexpr int H = kSegsPerWave / 2;
     uint32_t s0;                      // first segment of the workgroup
     uint32_t wave;
     uint32_t send;                    // end of the workgroup's segments
     uint32_t raw[kSegsPerWave];       // candidates of the segment (may exceed its slots)
     uint32_t cap;                     // slots per segment
+    bool wide;                        // first[H + i] holds slots 64..127 of segment i
     uint2 first[kSegsPerWave];
     __device__ uint32_t seg(int i) const { return s0 + wave + (uint32_t)i * kWaves; }
     __device__ bool valid(int i) const { return seg(i) < send; }
@@ -998,20 +1004,40 @@ struct WaveSegs {
     }
     __device__ uint32_t cnt(int i) const { return min(raw[i], cap); }   // stored candidates
     __device__ bool full(int i) const { return raw[i] > cap; }          // re-read from acc
+    // slot p (< cnt(i)) of segment i; sl = slots(a, f, i)
+    __device__ uint2 at(int i, uint32_t p, const uint2 *sl) const
+    {
+        if (p < 64u) return first[i];
+        if (wide && i < H && p < 128u) {
+            uint2 r = first[0];               // (a select over constant indices: first[]
+#pragma unroll                                // stays in registers)
+            for (int j = H; j < kSegsPerWave; ++j)
+                if (j == i + H) r = first[j];
+            return r;
+        }
+        return sl[p];
+    }
     __device__ void load(const SparsifyArgs &a, const FinWork &f, uint32_t wv, uint32_t ln)
     {
         s0 = f.seg0;
         wave = wv;
         send = min(f.seg0 + f.grain, f.nseg);
         cap = f.cap;
+        wide = f.grain <= (uint32_t)(kFinSegs / 2);
 #pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) raw[i] = valid(i) ? a.seg_count[f.seg_base + seg(i)] : 0u;
 #pragma unroll
         for (int i = 0; i < kSegsPerWave; ++i) {
-            first[i] = (ln < min(raw[i], f.cap)) ? slots(a, f, i)[ln] : make_uint2(0, 0);
+            if (i >= H && wide) {           // (segment i is past the workgroup's end)
+                const int i0 = i - H;
+                first[i] = (64u + ln < min(raw[i0], f.cap)) ? slots(a, f, i0)[64u + ln] : make_uint2(0, 0);
+            } else {
+                first[i] = (ln < min(raw[i], f.cap)) ? slots(a, f, i)[ln] : make_uint2(0, 0);
+            }
         }
     }
 };
+static_assert(kSegsPerWave % 2 == 0 && kFinSegsSmall <= kFinSegs / 2, "the small grain uses half of first[]");
 
 // k_fin_select: per segment, the count of candidates above the threshold bin;
 // the threshold bin's candidates are gathered into the layer's list (one
@@ -1096,7 +1122,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
             const uint32_t cnt = ws.cnt(i);
             const uint2 *slots = ws.slots(a, f, i);
             for (uint32_t p = ln; p < cnt; p += 64) {
-                const uint2 c = (p < 64) ? ws.first[i] : slots[p];
+                const uint2 c = ws.at(i, p, slots);
                 const uint32_t bin = cand_bin(c.y & 0x7fffffffu, G, SH);
                 D += (bin > bstar) ? 1u : 0u;
                 nt += (bin == bstar) ? 1u : 0u;
@@ -1133,7 +1159,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_fin_select(SparsifyArgs a)
             const uint32_t cnt = ws.cnt(i);
             const uint2 *slots = ws.slots(a, f, i);
             for (uint32_t p = ln; p < cnt; p += 64) {
-                const uint2 c = (p < 64) ? ws.first[i] : slots[p];
+                const uint2 c = ws.at(i, p, slots);
                 if (cand_bin(c.y & 0x7fffffffu, G, SH) == bstar) {
                     if (t < f.tbin_cap) tb[t] = c;
                     ++t;
@@ -1508,7 +1534,7 @@ __device__ void emit_segments(const SparsifyArgs &a)
             bool sel = false;
             uint2 c = make_uint2(0, 0);
             if (p < cnt) {
-                c = (p < 64) ? ws.first[i] : slots[p];
+                c = ws.at(i, p, slots);
                 const uint32_t key = c.y & 0x7fffffffu;
                 // candidates always lie in their layer; the range test keeps a
                 // damaged workspace from turning into a stray store

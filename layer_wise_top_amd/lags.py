@@ -2,9 +2,8 @@
 
 Every step of the hot path runs in the library's HIP kernels; torch provides
 device memory and the current stream.  The functions keep the C names.  The
-library must be built (``__graft_entry__.build()`` or
-``python -m layer_wise_top_amd.build``); importing this module without it
-raises, there is no fallback.
+library must be built (``python -m layer_wise_top_amd.build``); loading it
+without that raises, there is no fallback.
 """
 from __future__ import annotations
 
