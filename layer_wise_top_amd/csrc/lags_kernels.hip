@@ -2304,12 +2304,14 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg_starts(AggArgs a)
 
 // k_agg: one workgroup per index chunk [lo, hi) of one layer, with an LDS
 // hash table of 2^TL slots.  Dynamic LDS: keys[2^TL], vals[2^TL], ws0[P],
-// pre[P+1].  The chunk's message entries are laid out worker by worker
-// (entry e of worker p: pre[p] <= e < pre[p+1]), so each slot's sum must add
-// its entries in increasing worker order, starting from +0.0.  With at most
-// 32 workers every entry finds its rank among the entries of its slot from a
-// bitmask of the slot's workers, and the sums take one barrier phase per rank
-// (the most entries any slot has), not one per worker.
+// pre[P+1] and, with more than 32 workers, minpos[2^TL].  The chunk's message
+// entries are laid out worker by worker (entry e of worker p: pre[p] <= e <
+// pre[p+1]), so each slot's sum must add its entries in increasing worker
+// order, starting from +0.0.  With at most 32 workers every entry finds its
+// rank among the entries of its slot from a bitmask of the slot's workers, and
+// the sums take one barrier phase per rank; with more, each round adds every
+// slot's pending entry of lowest position.  Either way the sums take as many
+// phases as the fullest slot has entries, not one per worker.
 template <uint32_t TL, bool DENSE>
 __global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
 {
@@ -2321,6 +2323,7 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
     uint32_t *vmask = dyn + kTable;           // the same words: the slots' worker masks first
     uint32_t *ws0 = dyn + 2 * kTable;
     uint32_t *pre = ws0 + a.P;
+    uint32_t *minpos = pre + a.P + 1;         // with more than 32 workers: per slot
     __shared__ uint32_t tmp[kWaves];
 
     const uint32_t c = a.c_lo + blockIdx.x;
@@ -2409,9 +2412,11 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
     uint32_t bad = 0;
 
     if (E <= kCap) {
+        const bool masks = P <= 32u;          // uniform
         for (uint32_t t = threadIdx.x; t < kTable; t += kBlock) {
             keys[t] = 0xffffffffu;
-            vmask[t] = 0u;
+            vmask[t] = 0u;                    // (and vals[t] = +0.0)
+            if (!masks) minpos[t] = 0xffffffffu;
         }
         __syncthreads();
         constexpr int EPT = kCap / kBlock;
@@ -2438,7 +2443,6 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
                 v[q] = a.msg_val[at];
             }
         }
-        const bool masks = P <= 32u;          // uniform
 #pragma unroll
         for (int q = 0; q < EPT; ++q) {
             const uint32_t e = threadIdx.x + q * kBlock;
@@ -2488,12 +2492,32 @@ __global__ __launch_bounds__(kBlock, 8) void k_agg(AggArgs a)
                 }
             }
         } else {
-            for (uint32_t p = 0; p < P; ++p) {   // worker order, one worker at a time
-                if (pre[p + 1] == pre[p]) continue;
+            // more workers than mask bits: in each round every slot adds its
+            // pending entry of lowest chunk position (entry e's worker is
+            // nondecreasing in e, so this is worker order), found with an LDS
+            // minimum; one round per entry of the fullest slot, whatever P is.
+            // The winner clears the slot's minimum; a loser reading it then
+            // still sees a position other than its own.
+            uint32_t pend = 0, more = 0;
+#pragma unroll
+            for (int q = 0; q < EPT; ++q)
+                if (slot[q] >= 0) pend |= 1u << q;
+            more = pend;
+            while (__syncthreads_or((int)more)) {
 #pragma unroll
                 for (int q = 0; q < EPT; ++q)
-                    if (slot[q] >= 0 && wk[q] == p) vals[slot[q]] = vals[slot[q]] + v[q];
+                    if (pend & (1u << q)) atomicMin(&minpos[slot[q]], threadIdx.x + q * kBlock);
                 __syncthreads();
+#pragma unroll
+                for (int q = 0; q < EPT; ++q) {
+                    if (!(pend & (1u << q))) continue;
+                    if (minpos[slot[q]] == threadIdx.x + q * kBlock) {
+                        vals[slot[q]] = vals[slot[q]] + v[q];
+                        minpos[slot[q]] = 0xffffffffu;
+                        pend &= ~(1u << q);
+                    }
+                }
+                more = pend;
             }
         }
         // apply at every touched index: every weight load of the thread is
@@ -2702,7 +2726,10 @@ hipError_t launch_agg_starts(const AggArgs &a, hipStream_t s)
 
 hipError_t launch_agg(const AggArgs &a, uint32_t nchunks, uint32_t table_log2, bool dense, hipStream_t s)
 {
-    const size_t lds = ((2u << table_log2) + 2u * a.P + 1u) * sizeof(uint32_t);
+    // keys and sums (or masks), the workers' starts and offsets, and with
+    // more than 32 workers a per-slot minimum position
+    const size_t lds =
+        ((2u << table_log2) + (a.P > 32u ? (1u << table_log2) : 0u) + 2u * a.P + 1u) * sizeof(uint32_t);
     const dim3 g(nchunks), b(kBlock);
     if (table_log2 == kAggTableLog2 && dense)
         hipLaunchKernelGGL(HIP_KERNEL_NAME(k_agg<kAggTableLog2, true>), g, b, lds, s, a);

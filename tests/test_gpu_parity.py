@@ -517,13 +517,13 @@ def _aggregate_case(oracle, sizes, k, P, seed, collide=0.0):
     return off, moff, idx, val, w
 
 
-@pytest.mark.parametrize("P", [1, 3, 16, 20, 40])
+@pytest.mark.parametrize("P", [1, 3, 16, 20, 32, 33, 40, 130])
 def test_aggregate_dense_and_shared_indices(oracle, P):
     """Layers that send every entry (k = n: summed per index from fixed
     message positions) beside sparse layers whose indices are shared by many
     workers (worker-ordered sums through the LDS table: ranks of up to P - 1
-    for P <= 32, one phase per worker beyond), against the oracle bit for
-    bit."""
+    from the slots' worker masks for P <= 32, rounds of lowest-position
+    entries beyond), against the oracle bit for bit."""
     import torch
     sizes = [1, 63, 256, 257, 1000, 5000, 40_000, 9000, 70_001]
     k = np.array([1, 63, 256, 257, 1000, 5000, 400, 9000, 701], np.int64)
