@@ -92,6 +92,10 @@ LAYOUT_CASES = [
     # (name, layer sizes, ratio (num, den) or "rand", value kind, P, steps)
     ("one_small", [1000], (1, 100), "normal", 3, 2),
     ("small_boundary", [4095, 4096, 4097, 1, 2, 3, 5], (1, 10), "normal", 2, 2),
+    # layers of up to 37888 entries are done whole in one workgroup (acc in LDS)
+    ("local_boundary", [37887, 37888, 37889, 64, 37888], (1, 10), "normal", 2, 2),
+    ("local_ties", [37888, 30001, 2], (1, 3), "bf16", 3, 2),
+    ("local_equal", [37888, 1000], (1, 1000), "equal", 2, 2),
     ("full_sample_boundary", [16383, 16384, 16385, 16387], (1, 100), "normal", 4, 2),
     ("unaligned", [7, 50001, 3, 70001, 9, 65536], (1, 1000), "normal", 5, 3),
     ("dense_big", [20000, 5001, 40000], (1, 1), "normal", 3, 2),
