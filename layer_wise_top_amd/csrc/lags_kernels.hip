@@ -368,18 +368,18 @@ struct LdsRun {
 
 // ---------------------------------------------------------------------------
 // k_sample: one 1024-thread workgroup per sampled layer.  The whole sample is
-// requested at once (4 float4 of grad and residual per thread), its keys go
-// to LDS, and two 12-bit histogram passes locate the 24-bit key prefix that
-// holds the rank-th largest sample key.  The guess G is that prefix's lower
-// edge, so at least as many entries reach G as reach the exact sample
-// quantile.
+// requested at once (4 float4 of grad and residual per thread), each thread
+// keeps its 16 keys in registers, and two 12-bit histogram passes over them
+// locate the 24-bit key prefix that holds the rank-th largest sample key.
+// The guess G is that prefix's lower edge, so at least as many entries reach
+// G as reach the exact sample quantile.
 constexpr int kSampleThreads = 1024;
 constexpr uint32_t kSampleBins = 4096;
 
 __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 {
     constexpr int NT = kSampleThreads;
-    __shared__ uint32_t keys[kSampleMax];
+    constexpr int KPT = kSampleMax / NT;       // sample keys per thread
     __shared__ uint32_t hist[kSampleBins];     // first 12 key bits below the sign
     __shared__ uint32_t hist2[kSampleBins];    // the next 12, inside the chosen bin
     __shared__ uint32_t tmp[NT / 64];
@@ -408,12 +408,14 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
         return;
     }
     uint32_t cnt, rank, m = 0;
+    uint32_t kr[KPT];             // the thread's keys (0 past the layer's end: never counted)
     LdsRun run;
     if (S.full_sample) {
         cnt = S.n;
         rank = S.k;
         // the whole layer is requested at once (cnt <= kSampleMax entries)
         constexpr int EPT = kSampleMax / NT;
+        static_assert(EPT == KPT, "one key per entry");
         float gv[EPT], rv[EPT];
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
@@ -424,9 +426,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 #pragma unroll
         for (int u = 0; u < EPT; ++u) {
             const uint32_t i = threadIdx.x + u * NT;
+            kr[u] = 0u;
             if (i < cnt) {
                 const uint32_t key = key_of(gv[u] + rv[u]);
-                keys[i] = key;
+                kr[u] = key;
                 m = max(m, key);
                 run.add(hist, key >> 19);
             }
@@ -435,6 +438,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
         cnt = S.nchunk * kSampleChunk;
         rank = S.j;
         constexpr int QPT = kSampleMax / 4 / NT;            // float4 per thread
+        static_assert(QPT * 4 == KPT, "four keys per float4");
         constexpr uint32_t QPC = kSampleChunk / 4;          // float4 per chunk
         const uint64_t span = S.b4 - S.a4 - kSampleChunk;
         const v4f *g4 = reinterpret_cast<const v4f *>(a.grad);
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t key = key_of(acc[j]);
-                keys[qi * 4 + j] = key;
+                kr[u * 4 + j] = key;
                 m = max(m, key);
                 run.add(hist, key >> 19);
             }
@@ -485,9 +489,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(SparsifyArgs a)
     block_find_rank<NT>(hist, kSampleBins, rank, res, tmp);   // ends at a barrier
     const uint32_t b1 = res[0];
     const uint32_t rank2 = rank - res[1];
-    for (uint32_t e = threadIdx.x; e < cnt; e += NT) {
-        const uint32_t key = keys[e];
-        if ((key >> 19) == b1) run.add(hist2, (key >> 7) & (kSampleBins - 1));
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const bool in = !S.full_sample || threadIdx.x + (uint32_t)u * NT < cnt;
+        if (in && (kr[u] >> 19) == b1) run.add(hist2, (kr[u] >> 7) & (kSampleBins - 1));
     }
     run.flush(hist2);
     __syncthreads();             // also: every thread has read res
