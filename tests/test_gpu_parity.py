@@ -543,6 +543,30 @@ def test_aggregate_dense_and_shared_indices(oracle, P):
     assert_bits_equal(f"P={P} weights", to_np_f32(w_d), oracle.aggregate(idx, val, w, 0.05))
 
 
+def test_aggregate_max_workers(oracle):
+    """The most workers the boundary accepts (LAGS_MAX_WORKERS = 1024), half
+    of every worker's sparse entries drawn from one shared set (slots with
+    hundreds of entries, summed in worker order), beside a layer that every
+    worker sends whole; two calls in a row on the same workspace."""
+    import torch
+    P = 1024
+    sizes = [3000, 257, 70_001, 1]
+    k = np.array([30, 257, 70, 1], np.int64)
+    off, moff, idx, val, w = _aggregate_case(oracle, sizes, k, P, 1024, collide=0.5)
+    run = GpuRunner(off, k, P)
+    run.msg_idx.copy_(to_dev(idx))
+    run.msg_val.copy_(to_dev(val))
+    w_d = to_dev(w)
+    w_o = w
+    for call in range(2):
+        run.aggregate(w_d, 0.05)
+        torch.cuda.synchronize()
+        w_o = oracle.aggregate(idx, val, w_o, 0.05)
+        rep = run.report()
+        assert rep["bad_entries"] == 0, rep
+        assert_bits_equal(f"P={P} weights, call {call}", to_np_f32(w_d), w_o)
+
+
 def test_aggregate_dense_layer_with_entries_out_of_place(oracle):
     """A k = n layer whose message holds an index of another layer and a
     swapped pair: those chunks are summed by index instead, the foreign entry
