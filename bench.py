@@ -21,7 +21,10 @@ VGG-16, ResNet-50, LSTM), each timed the same way in the same run (at least
 --pipeline adds a second measurement of the same step issued layer range by
 layer range (lags_sparsify_range / lags_aggregate_range, last layers first),
 with the ranges of the merged-message schedule (lags_merge_schedule) under a
-synthetic cost model stated in pipeline_model().
+synthetic cost model stated in pipeline_model(), timed as issued from Python
+and as one captured HIP graph replayed (the GPU's own cost, without the
+host's per-call issue time; one replay is first checked bit for bit against
+an eager step from the same state).
 
 Every line also carries "exact_mode": the sparsify call with
 LAGS_SPARSIFY_EXACT (multi-workgroup radix select) from the state after the
@@ -462,6 +465,45 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True, p
         e1.record(stream)
         torch.cuda.synchronize()
         ms_piped = e0.elapsed_time(e1) / steps
+        # the same issue captured once into a HIP graph and replayed: the
+        # GPU's own cost per step, without the host's per-call issue time
+        # (one replay is first checked bit for bit against an eager step
+        # from the same state)
+        gs = torch.cuda.Stream()
+
+        def piped_on(s):
+            for l0, l1 in runs:
+                lags.lags_sparsify_range(lay, l0, l1, g_d, r_d, mi[0], mv[0], ws, 0, s)
+                lags.lags_aggregate_range(lay, l0, l1, w_d, mi, mv, P, wl.lr, ws, s)
+
+        torch.cuda.synchronize()
+        r0, w0 = r_d.clone(), w_d.clone()
+        torch.cuda.synchronize()              # the copies are done before gs starts
+        with torch.cuda.stream(gs):
+            piped_on(gs)
+        torch.cuda.synchronize()
+        want = (r_d.clone(), w_d.clone(), mi[0].clone(), mv[0].clone())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            piped_on(gs)
+        r_d.copy_(r0)
+        w_d.copy_(w0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_same = all(bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+                         for a, b in zip((r_d, w_d, mi[0], mv[0]), want))
+        del r0, w0, want
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / steps
+        del graph
         per_layer = [(l, l + 1) for l in range(wl.L - 1, -1, -1)]
         # the same, with per-layer sizes from each layer's overlap window
         k_ad = lags.lags_adaptive_k(off, backward, P, alpha, beta, (1, 1000))
@@ -493,6 +535,7 @@ def run_config(name, steps, warmup, do_cpu, flush, pipeline=False, exact=True, p
         del mi_ad, mv_ad, ws_ad
         out["pipeline"] = {
             "runs": len(runs), "ms_per_step": round(ms_piped, 5),
+            "ms_per_step_graph": round(ms_graph, 5), "graph_same_as_eager": graph_same,
             "model": "backward 66 ps/param, 50 us + all-gather bytes at 50 GB/s per message",
             "modelled_comm_finish_ms": {
                 "merged": round(finish * 1e3, 4),

@@ -152,6 +152,7 @@ def test_graph_capture_replays_match_eager():
         step()                                  # builds the device tables
     torch.cuda.synchronize()
     r_start, w_start = r.clone(), w.clone()
+    torch.cuda.synchronize()                    # the copies are done before s starts
     with torch.cuda.stream(s):
         step()
     torch.cuda.synchronize()
