@@ -8,7 +8,8 @@ block 0, a middle qkv matrix and the last fc2.  Messages, residuals and
 weights of those layers must match bit for bit.  Over all 193 layers the GPU
 output is checked for the invariants that fix the selection (sizes, order,
 range, residual bits, threshold order, tie prefix), and untouched weights
-must keep their bits over the whole buffer.
+must keep their bits over the whole buffer.  A 2.3B-entry layout checks the
+same beyond 2^31 entries (indices that only fit uint32).
 """
 import numpy as np
 import pytest
@@ -212,3 +213,101 @@ def test_slgs1p3b_full_size(oracle):
     _say("oracle aggregate over every index")
     w_o = oracle.aggregate(ai, av, w0, wl.lr)
     assert_bits_equal("weights of every index", to_np_f32(w_d), w_o)
+
+
+@pytest.mark.timeout(1200)
+def test_layout_beyond_2_31_entries(oracle):
+    """A 2.3B-entry layout (rho = 1/1000, P = 2): two 1.1B-entry layers, then
+    four layers whose every index lies above 2^31 (the uint32 index range the
+    boundary allows, beyond int32).  The four are recomputed by the oracle
+    (messages, residual and, restricted to each layer, weights, bit for
+    bit); every layer meets the selection's invariants; exact mode agrees bit
+    for bit.  Inputs: seeded normal draws on the device (gradient, weights)
+    and seeded stratified messages for the other worker."""
+    import torch
+    sizes = [1_100_000_003, 1_100_000_001, 20_000_001, 3, 30_000_000, 49_999_999]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n, L = int(off[-1]), len(sizes)
+    assert off[2] > 2 ** 31 and n < 2 ** 32 - 1
+    k = oracle.k_for_ratio(np.diff(off), 1, 1000)
+    moff = np.concatenate([[0], np.cumsum(k)])
+    K, P = int(k.sum()), 2
+    _say(f"[2^31] n={n:,} K={K:,}: inputs on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2311)
+    g_d = torch.randn(n, generator=gen, device="cuda")
+    w_d = torch.randn(n, generator=gen, device="cuda")
+    r_d = torch.zeros(n, dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(2312)
+    parts = []
+    for l in range(L):
+        n_l, k_l = int(sizes[l]), int(k[l])
+        lo = (np.arange(k_l, dtype=np.int64) * n_l) // k_l
+        hi = (np.arange(1, k_l + 1, dtype=np.int64) * n_l) // k_l
+        parts.append(off[l] + lo + (rng.random(k_l) * (hi - lo)).astype(np.int64))
+    oi = np.concatenate(parts).astype(np.uint32)[None]
+    ov = rng.standard_normal((1, K)).astype(np.float32)
+    a2 = int(off[2])
+    g_tail = to_np_f32(g_d[a2:])
+    w_tail = to_np_f32(w_d[a2:])
+    w0_d = w_d.clone()
+    run = GpuRunner(off, k, P)
+    run.set_others(oi, ov)
+    _say("[2^31] one step")
+    run.sparsify(g_d, r_d)
+    run.aggregate(w_d, 0.1)
+    torch.cuda.synchronize()
+    rep = run.report()
+    assert rep["layers_exact"] == 0 and rep["bad_entries"] == 0, rep
+
+    _say("[2^31] invariants over all layers")
+    # every masked check is per layer: torch's boolean indexing fails beyond
+    # 2^31 elements
+    mi = run.msg_idx[0, :K].long() & 0xFFFFFFFF
+    sent = torch.zeros(n, dtype=torch.bool, device="cuda")
+    sent[mi] = True
+    assert int(sent.sum()) == K
+    touched = sent.clone()
+    touched[torch.from_numpy(oi[0].astype(np.int64)).cuda()] = True
+    g_bits, r_bits, w_bits, w0_bits = (t.view(torch.int32) for t in (g_d, r_d, w_d, w0_d))
+    mv_bits = run.msg_val[0, :K].view(torch.int32)
+    for l in range(L):
+        a, b = int(off[l]), int(off[l + 1])
+        seg = mi[moff[l]:moff[l + 1]]
+        assert bool((seg >= a).all()) and bool((seg < b).all())
+        assert bool((seg[1:] > seg[:-1]).all())
+        assert bool((mv_bits[moff[l]:moff[l + 1]] == g_bits[seg]).all())
+        s_l, gb, rb = sent[a:b], g_bits[a:b], r_bits[a:b]
+        assert bool((rb[s_l] == 0).all())
+        assert bool((rb[~s_l] == gb[~s_l]).all())
+        ks = gb & 0x7FFFFFFF
+        T = int(ks[s_l].min())
+        if not bool(s_l.all()):
+            assert int(ks[~s_l].max()) <= T
+            tied_unsent = torch.nonzero(~s_l & (ks == T)).flatten()
+            if tied_unsent.numel():
+                assert int(torch.nonzero(s_l & (ks == T)).flatten().max()) < int(tied_unsent.min())
+        u_l = ~touched[a:b]
+        assert bool((w_bits[a:b][u_l] == w0_bits[a:b][u_l]).all())
+        del s_l, gb, rb, ks, u_l
+    del sent, touched, g_bits, r_bits, w_bits, w0_bits, w0_d
+
+    mi_h = to_np_u32(run.msg_idx[0, :K])
+    mv_h = to_np_f32(run.msg_val[0, :K])
+    for l in range(2, L):
+        a, b = int(off[l]), int(off[l + 1])
+        _say(f"[2^31] oracle layer {l} ([{a:,}, {b:,}))")
+        ga = g_tail[a - a2:b - a2]
+        mi_o, mv_o, r_o = oracle.sparsify([0, b - a], [int(k[l])], ga, np.zeros(b - a, np.float32))
+        assert_bits_equal(f"layer {l} msg_idx", mi_h[moff[l]:moff[l + 1]], mi_o.astype(np.uint32) + np.uint32(a))
+        assert_bits_equal(f"layer {l} msg_val", mv_h[moff[l]:moff[l + 1]], mv_o)
+        assert_bits_equal(f"layer {l} residual", to_np_f32(r_d[a:b]), r_o)
+        ai = np.full((P, K), 0xFFFFFFFF, np.uint32)
+        av = np.zeros((P, K), np.float32)
+        ai[0, moff[l]:moff[l + 1]] = mi_o.astype(np.uint32) + np.uint32(a)
+        av[0, moff[l]:moff[l + 1]] = mv_o
+        ai[1, moff[l]:moff[l + 1]] = oi[0, moff[l]:moff[l + 1]]
+        av[1, moff[l]:moff[l + 1]] = ov[0, moff[l]:moff[l + 1]]
+        w_o = oracle.aggregate(ai, av, w_tail[a - a2:b - a2], 0.1, lo=a, hi=b)
+        assert_bits_equal(f"layer {l} weights", to_np_f32(w_d[a:b]), w_o)
+    _exact_mode_agrees(run, g_d, r_d, rep["layers_sampled"], "2^31 layout")
