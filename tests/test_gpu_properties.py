@@ -80,6 +80,98 @@ def test_random_layouts(oracle, seed):
         r, w = r_o, w_o
 
 
+SPECIAL_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 4095, 4096, 4097, 16383, 16384, 16385, 37888, 65537]
+
+
+def _stratified_others(rng, off, k, P, collide):
+    """Messages of workers 1..P-1: one index drawn in each of k_l equal strata
+    of every layer (sorted and distinct); with `collide`, about half of the
+    workers share one draw, so many indices carry several workers."""
+    L, K = len(k), int(k.sum())
+    moff = np.concatenate([[0], np.cumsum(k)])
+    oi = np.empty((P - 1, K), np.uint32)
+    for l in range(L):
+        n_l, k_l = int(off[l + 1] - off[l]), int(k[l])
+        lo = (np.arange(k_l, dtype=np.int64) * n_l) // k_l
+        hi = (np.arange(1, k_l + 1, dtype=np.int64) * n_l) // k_l
+        shared = lo + (rng.random(k_l) * (hi - lo)).astype(np.int64)
+        for p in range(P - 1):
+            own = shared if (collide and rng.random() < 0.5) else lo + (rng.random(k_l) * (hi - lo)).astype(np.int64)
+            oi[p, moff[l]:moff[l + 1]] = own + off[l]
+    return oi, rng.standard_normal((P - 1, K)).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_random_layouts_with_ranges(oracle, seed):
+    """Random layouts (1 .. 30 layers, sizes log-uniform up to 1M entries or
+    boundary sizes, k random, within 2 of n, or from a ratio), P up to 40
+    with indices shared between workers, two steps, each issued as one call or
+    as a random cut into layer ranges in random order: messages, residuals
+    and weights bit-exact against the oracle, and exact mode from the same
+    residual too."""
+    import torch
+    from layer_wise_top_amd import lags
+    rng = np.random.default_rng(zlib.crc32(f"ranges layout {seed}".encode()))
+    L = int(rng.integers(1, 31))
+    sizes = np.array([int(rng.choice(SPECIAL_SIZES)) if rng.random() < 0.3
+                      else int(np.exp(rng.uniform(0, np.log(1_000_000)))) + 1 for _ in range(L)], np.int64)
+    off = np.zeros(L + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    n = int(off[-1])
+    mode = seed % 3
+    if mode == 0:
+        k = np.array([int(rng.integers(1, s + 1)) for s in sizes], np.int64)
+    elif mode == 1:
+        k = np.array([max(1, int(s) - int(rng.integers(0, 3))) for s in sizes], np.int64)
+    else:
+        k = oracle.k_for_ratio(sizes, 1, int(rng.choice([3, 100, 1000])))
+    P = int(rng.choice([1, 2, 3, 8, 16, 33, 40]))
+    collide = bool(seed % 2)
+    K = int(k.sum())
+    run = GpuRunner(off, k, P)
+    r = np.zeros(n, np.float32)
+    w = W.adversarial_values(3000 + seed, n, "normal")
+    for step in range(2):
+        kind = KINDS[int(rng.integers(0, len(KINDS)))]
+        ranged = (step + seed) % 2 == 1 and L > 1
+        _say(f"[ranges layout {seed}] L={L} n={n} K={K} P={P} step {step} {kind} ranges={ranged}")
+        g = W.adversarial_values(4000 + 10 * seed + step, n, kind)
+        g_d, r_d, w_d = to_dev(g), to_dev(r), to_dev(w)
+        if P > 1:
+            oi, ov = _stratified_others(rng, off, k, P, collide)
+            run.set_others(oi, ov)
+        if ranged:
+            cuts = sorted(set([0, L] + [int(c) for c in rng.integers(1, L, size=int(rng.integers(1, min(L, 6))))]))
+            parts = [(cuts[i], cuts[i + 1]) for i in range(len(cuts) - 1)]
+            for j in rng.permutation(len(parts)):
+                l0, l1 = parts[j]
+                lags.lags_sparsify_range(run.layout, l0, l1, g_d, r_d, run.msg_idx[0], run.msg_val[0], run.ws)
+                lags.lags_aggregate_range(run.layout, l0, l1, w_d, run.msg_idx, run.msg_val, P, 0.05, run.ws)
+        else:
+            run.sparsify(g_d, r_d)
+            run.aggregate(w_d, 0.05)
+        torch.cuda.synchronize()
+        assert run.report()["bad_entries"] == 0
+        mi_o, mv_o, r_o = oracle.sparsify(off, k, g, r)
+        mi_g, mv_g = run.message()
+        assert_bits_equal("msg_idx", mi_g, mi_o)
+        assert_bits_equal("msg_val", mv_g, mv_o)
+        assert_bits_equal("residual", to_np_f32(r_d), r_o)
+        ai = np.concatenate([mi_o[None], oi], 0) if P > 1 else mi_o[None]
+        av = np.concatenate([mv_o[None], ov], 0) if P > 1 else mv_o[None]
+        w_o = oracle.aggregate(ai, av, w, 0.05)
+        assert_bits_equal("weights", to_np_f32(w_d), w_o)
+        r2 = to_dev(r)
+        mi2 = torch.empty(K, dtype=torch.int32, device="cuda")
+        mv2 = torch.empty(K, dtype=torch.float32, device="cuda")
+        lags.lags_sparsify_layers(run.layout, g_d, r2, mi2, mv2, run.ws, lags.LAGS_SPARSIFY_EXACT)
+        torch.cuda.synchronize()
+        assert_bits_equal("exact-mode msg_idx", mi2.cpu().numpy().view(np.uint32), mi_o)
+        assert_bits_equal("exact-mode msg_val", to_np_f32(mv2), mv_o)
+        assert_bits_equal("exact-mode residual", to_np_f32(r2), r_o)
+        r, w = r_o, w_o
+
+
 def test_resume_equals_continuous_run():
     """ResNet-50: ten steps in one go equal five steps, a save of (weights,
     residual) to the host, a fresh layout and workspace, and five more steps
