@@ -27,16 +27,18 @@
 //                 gathers the threshold bin's candidates.
 //   k_fin_resolve one workgroup per sampled layer: resolves the exact
 //                 threshold key T and the tie cut (lowest indices first) and
-//                 scans segment counts into message offsets.  A layer whose
-//                 guess failed (fewer than k candidates above a nonzero G) is
-//                 done here by the exact multi-pass path.  One more workgroup per
-//                 small layer (<= 4096 entries) does that layer start to
-//                 finish (exact radix select in LDS).
+//                 scans segment counts into message offsets.  One more
+//                 workgroup per small layer (<= 4096 entries) does that layer
+//                 start to finish (exact radix select in LDS).
 //   k_fin_emit    writes the selected candidates of each segment, in index
 //                 order, to the message and zeroes their residual.  A layer
 //                 with fewer than k nonzero keys (G = 0, "zero mode") sends
 //                 every nonzero entry and its lowest-index zeros; segments
 //                 that send zeros are re-read from the residual buffer.
+//                 Then its first workgroups (all resident) select, by a
+//                 multi-workgroup radix select over the residual buffer, any
+//                 layer whose guess failed (fewer than k candidates above a
+//                 nonzero G, or a threshold bin larger than the layer's list).
 //   k_x_first, k_x_pass, k_x_pick, k_x_count, k_x_cut
 //                 exact mode (chosen by the caller): the threshold of every
 //                 sampled layer by a multi-workgroup radix select over all its
@@ -1256,8 +1258,8 @@ __device__ void resolve_tbin(const SparsifyArgs &a, const FinWork &f, uint32_t n
 // k_fin_resolve: one workgroup per sampled layer.  Resolves the exact
 // threshold key T and the tie cut inside the threshold bin and turns the
 // per-workgroup counts into message offsets.  A layer whose guess failed
-// (status not Ok, or a threshold bin above its list's capacity) is done here
-// by the exact multi-pass path over the accumulated values.
+// (status not Ok, or a threshold bin above its list's capacity) is left to
+// the fallback in k_fin_emit.
 __global__ __launch_bounds__(kBlock) void k_fin_resolve(SparsifyArgs a)
 {
     static_assert(kSmallMax <= 2 * kTbinCap, "a small layer's values fit the threshold-bin arrays");
