@@ -85,7 +85,6 @@ enum : uint32_t {
 enum : uint32_t {
     kStPending = 0,
     kStOk = 1,        // candidates hold the top k; threshold bin resolved
-    kStExact = 2,     // the exact multi-pass path handled the layer
     kStZero = 3,      // guess G = 0 and fewer than k nonzero keys: T = 0, all nonzero
                       // entries plus the lowest-index zeros are sent
     kStFix = 4,       // the guess failed (fewer than k candidates above a nonzero G, or a
