@@ -73,7 +73,7 @@ extern "C" {
                                   above the small-layer size finds its threshold
                                   by a multi-workgroup radix select over all its
                                   keys (three digit passes, then counting and
-                                  emission passes): the same results, about 28
+                                  emission passes): the same results, about 24
                                   bytes of memory traffic per entry instead of
                                   about 12 */
 
