@@ -244,15 +244,18 @@ __device__ uint32_t block_radix_select(const Val &val, const Match &match, uint3
         const uint32_t nbins = max(nb, (uint32_t)kBlock);
         for (uint32_t b = threadIdx.x; b < nbins; b += kBlock) hist[b] = 0;
         __syncthreads();
-        // four items per thread per round: their loads are in flight together
+        // four items per thread per round, requested together: the reads are
+        // unconditional, at indices clamped into [0, n), so that no branch
+        // separates them (val and match only read)
         for (uint32_t i0 = threadIdx.x; i0 < n; i0 += 4u * kBlock) {
             uint32_t v[4];
             bool ok[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t i = i0 + (uint32_t)u * kBlock;
-                ok[u] = i < n && match(i);
-                v[u] = ok[u] ? val(i) : 0u;
+                const uint32_t ic = min(i, n - 1u);
+                v[u] = val(ic);
+                ok[u] = match(ic) && i < n;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
